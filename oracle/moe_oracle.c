@@ -1,0 +1,312 @@
+/*
+ * ORACLE for the token-choice MoE FFN layer forward (one device's share, no
+ * expert parallelism).  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark may call it; the GPU library never does.
+ * It shares no code, header or constant with the GPU path.
+ *
+ * Plain, slow, obviously correct: every floating-point quantity is accumulated
+ * in binary64 in the order written below; there is no blocking and no fusion.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [EP]     "Expert-parallel MoE training" explainer (blog.vllbc.top,
+ *            visual-reading): the router / capacity / drop section, its capacity
+ *            calculator, and the walk through one MoE layer (dispatch, experts,
+ *            unpermute, gate-weighted sum, residual) plus its memory calculator
+ *            (gated FFN with gate / up / down matrices).
+ *   [DS7508] DeepSpeed discussion #7508 "The MoE spends too much time on the gate
+ *            network", first answer: capacity = ceil((tokens/experts)*cf*k) with
+ *            the worked value 10,923.
+ *   [SW]     Switch Transformers explainer ("AI 十大论文精讲（七）: Switch Routing"):
+ *            §1.1 routing (logits = router weight times x, softmax, argmax,
+ *            y = E_i(x) p_i(x)), §1.2 capacity and overflow through the residual,
+ *            §2.1 selective precision (router input, logits and softmax in fp32),
+ *            §2.3 expert FFN weights W_in / W_out.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - selection is on the fp32 logits, larger first, ties to the lower expert
+ *     index; the k choices are ordered that way (choice r = 0 is the best);
+ *   - capacity priority is choice-major: every token's first choice before any
+ *     second choice, token order inside each ("position" policy of [EP]);
+ *   - capacity is ceil(double(T*k) * cf / E), optionally raised to min_capacity;
+ *   - a dropped assignment contributes nothing and the remaining gates are not
+ *     renormalised; the residual carries a fully dropped token;
+ *   - GELU is the exact erf form; SwiGLU is silu(x W_gate) * (x W_up) then W_down;
+ *   - weights are stored [out_features, in_features] row-major:
+ *     W1, W3: [E][F][H]; W2: [E][H][F]; the router Wg is [H][E] (x . Wg).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_SOFTMAX_TOPK = 0, OR_SOFTMAX_TOPK_RENORM = 1, OR_TOPK_SOFTMAX = 2 };
+enum { OR_RELU = 0, OR_GELU = 1, OR_SWIGLU = 2 };
+
+/* A bf16 number is the upper half of an IEEE binary32; its value is exact in binary64. */
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double elem(const void *p, int dtype, int64_t i) {
+  if (dtype == OR_BF16) return bf16_to_double(((const uint16_t *)p)[i]);
+  return (double)((const float *)p)[i];
+}
+
+/* Capacity ([EP] router/capacity section: ceil((T*k/E)*cf); [DS7508]: 10,923 at
+ * T=32768, E=12, k=4, cf=1).  Returns -1 for dropless (no capacity limit). */
+int64_t oracle_capacity(int64_t T, int64_t k, int64_t E, double cf, int64_t min_capacity, int dropless) {
+  if (dropless) return -1;
+  double c = ceil((double)(T * k) * cf / (double)E);
+  int64_t C = (int64_t)c;
+  return C < min_capacity ? min_capacity : C;
+}
+
+/* Router logits ([EP] router: linear layer Wg in R^{HxE}; [SW] §1.1 h(x) = Wr x,
+ * §2.1 fp32 router): l[t,e] = fl32(sum_h x[t,h]*Wg[h,e]  +  bias[e]), the sum in
+ * binary64 over h ascending, rounded once to fp32.  bias may be NULL. */
+void oracle_logits(int64_t T, int64_t H, int64_t E, int x_dtype, const void *x, const float *Wg,
+                   const float *bias, float *logits) {
+#pragma omp parallel
+  {
+    double *acc = (double *)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int64_t e = 0; e < E; ++e) acc[e] = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        double xv = elem(x, x_dtype, t * H + h);
+        const float *w = Wg + h * E;
+        for (int64_t e = 0; e < E; ++e) acc[e] += xv * (double)w[e];
+      }
+      for (int64_t e = 0; e < E; ++e)
+        logits[t * E + e] = (float)(bias ? acc[e] + (double)bias[e] : acc[e]);
+    }
+    free(acc);
+  }
+}
+
+/* Top-k selection for one token ([EP] router: top-k after scoring; [SW] §1.1
+ * argmax for k=1): k rounds, each taking the largest remaining logit, the lower
+ * index on equal values. */
+static void select_topk(const float *l, int64_t E, int k, int32_t *idx) {
+  for (int r = 0; r < k; ++r) {
+    int32_t best = -1;
+    for (int64_t e = 0; e < E; ++e) {
+      int taken = 0;
+      for (int j = 0; j < r; ++j) taken |= (idx[j] == (int32_t)e);
+      if (taken) continue;
+      if (best < 0 || l[e] > l[best]) best = (int32_t)e;
+    }
+    idx[r] = best;
+  }
+}
+
+/* Gate values of the k choices ([EP] router: softmax then top-k, or top-k then
+ * normalise over the selected; [SW] §1.1 p_i = exp(h_i)/sum_j exp(h_j)), binary64
+ * from the fp32 logits, rounded once to fp32. */
+static void gates(const float *l, int64_t E, int k, int mode, const int32_t *idx, float *g) {
+  double m = l[idx[0]]; /* the largest logit */
+  if (mode == OR_TOPK_SOFTMAX) {
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) den += exp((double)l[idx[j]] - m);
+    for (int r = 0; r < k; ++r) g[r] = (float)(exp((double)l[idx[r]] - m) / den);
+    return;
+  }
+  double den = 0.0;
+  for (int64_t e = 0; e < E; ++e) den += exp((double)l[e] - m);
+  if (mode == OR_SOFTMAX_TOPK) {
+    for (int r = 0; r < k; ++r) g[r] = (float)(exp((double)l[idx[r]] - m) / den);
+    return;
+  }
+  /* OR_SOFTMAX_TOPK_RENORM: p over all E, then p of the chosen divided by their sum */
+  double p[16], s = 0.0;
+  for (int r = 0; r < k; ++r) {
+    p[r] = exp((double)l[idx[r]] - m) / den;
+    s += p[r];
+  }
+  for (int r = 0; r < k; ++r) g[r] = (float)(p[r] / s);
+}
+
+/*
+ * Routing plan from given fp32 logits: selection, gates, capacity, slot
+ * assignment, packing.  C < 0 means dropless.
+ *   - slot assignment ([EP] capacity / drop: "position" drops the assignments at
+ *     the end of the batch; over-capacity assignments skip the expert): walk
+ *     q = 0 .. T*k-1 with r = q / T, t = q % T; the assignment (t, r) to e = idx
+ *     takes slot n_e, then n_e += 1; it is kept iff slot < C.
+ *   - packing: offsets = exclusive prefix sum of kept; a kept assignment goes to
+ *     packed row offsets[e] + slot (-1 when dropped); row_token inverts it.
+ * Returns R = offsets[E], or -1 on bad arguments.
+ */
+int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int64_t C, const float *logits,
+                                 int32_t *topk_idx, float *topk_gate, int32_t *dst_row, int32_t *demand,
+                                 int32_t *kept, int32_t *offsets, int32_t *row_token, int32_t *n_dropped) {
+  if (k < 1 || k > 16 || k > E || T < 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    select_topk(logits + t * E, E, k, topk_idx + t * k);
+    gates(logits + t * E, E, k, gate_mode, topk_idx + t * k, topk_gate + t * k);
+  }
+  int64_t *n = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+  int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k > 0 ? T * k : 1));
+  for (int64_t q = 0; q < T * k; ++q) {
+    int64_t r = q / T, t = q % T;
+    int32_t e = topk_idx[t * k + r];
+    slot[t * k + r] = n[e];
+    n[e] += 1;
+  }
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    demand[e] = (int32_t)n[e];
+    kept[e] = (int32_t)((C < 0 || n[e] < C) ? n[e] : C);
+    offsets[e + 1] = offsets[e] + kept[e];
+  }
+  for (int64_t t = 0; t < T; ++t)
+    for (int r = 0; r < k; ++r) {
+      int64_t i = t * k + r;
+      int32_t e = topk_idx[i];
+      if (C < 0 || slot[i] < C) {
+        dst_row[i] = (int32_t)(offsets[e] + slot[i]);
+        row_token[dst_row[i]] = (int32_t)t;
+      } else {
+        dst_row[i] = -1;
+      }
+    }
+  *n_dropped = (int32_t)(T * k - offsets[E]);
+  free(n);
+  free(slot);
+  return offsets[E];
+}
+
+/* Dispatch ([EP] layer walk-through: tokens grouped by target expert):
+ * X[row] = x[row_token[row]], a copy of the row's bytes. */
+void oracle_dispatch(int64_t R, int64_t H, int dtype, const void *x, const int32_t *row_token, void *X) {
+  size_t rb = (size_t)H * (dtype == OR_BF16 ? 2 : 4);
+  for (int64_t row = 0; row < R; ++row)
+    memcpy((char *)X + (size_t)row * rb, (const char *)x + (size_t)row_token[row] * rb, rb);
+}
+
+static double act_relu(double u) { return u > 0.0 ? u : 0.0; }
+static double act_gelu(double u) { return 0.5 * u * (1.0 + erf(u / sqrt(2.0))); }
+static double act_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * Expert FFN on single rows ([SW] §2.3 W_in / W_out; [EP] memory calculator:
+ * gated FFN with gate / up / down): for a row x of expert e, in binary64 with no
+ * intermediate rounding,
+ *   2-matrix: u = x W_in (u_f = sum_h x_h W1[e][f][h]); h = ReLU(u) or GELU(u);
+ *   SwiGLU:   h = silu(x W_gate) * (x W_up)   (W_gate = W1, W_up = W3);
+ *   Y_n = sum_f h_f W2[e][n][f].
+ * xin: n_rows x H elements of dtype; Y: n_rows x H binary64.
+ */
+void oracle_expert_rows(int64_t n_rows, const int32_t *expert_of_row, int64_t H, int64_t F, int dtype, int act,
+                        const void *xin, const void *W1, const void *W3, const void *W2, double *Y) {
+#pragma omp parallel
+  {
+    double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+    double *hr = (double *)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      int64_t e = expert_of_row[i];
+      for (int64_t h = 0; h < H; ++h) xr[h] = elem(xin, dtype, i * H + h);
+      for (int64_t f = 0; f < F; ++f) {
+        int64_t base = (e * F + f) * H;
+        double u = 0.0;
+        for (int64_t h = 0; h < H; ++h) u += xr[h] * elem(W1, dtype, base + h);
+        if (act == OR_SWIGLU) {
+          double v = 0.0;
+          for (int64_t h = 0; h < H; ++h) v += xr[h] * elem(W3, dtype, base + h);
+          hr[f] = act_silu(u) * v;
+        } else {
+          hr[f] = act == OR_RELU ? act_relu(u) : act_gelu(u);
+        }
+      }
+      for (int64_t n = 0; n < H; ++n) {
+        int64_t base = (e * H + n) * F;
+        double y = 0.0;
+        for (int64_t f = 0; f < F; ++f) y += hr[f] * elem(W2, dtype, base + f);
+        Y[i * H + n] = y;
+      }
+    }
+    free(xr);
+    free(hr);
+  }
+}
+
+/* Expert FFN over the packed rows [0, offsets[E]): row of expert e = offsets[e] .. offsets[e+1]-1. */
+void oracle_expert_ffn(int64_t E, const int32_t *offsets, int64_t H, int64_t F, int dtype, int act, const void *X,
+                       const void *W1, const void *W3, const void *W2, double *Y) {
+  int64_t R = offsets[E];
+  int32_t *eo = (int32_t *)malloc(sizeof(int32_t) * (size_t)(R > 0 ? R : 1));
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t row = offsets[e]; row < offsets[e + 1]; ++row) eo[row] = (int32_t)e;
+  oracle_expert_rows(R, eo, H, F, dtype, act, X, W1, W3, W2, Y);
+  free(eo);
+}
+
+/*
+ * Combine ([EP] layer walk-through: unpermute, multiply by the gate, sum, add
+ * the residual; [SW] §1.1 y = E_i(x) p_i(x), §1.2 overflow passes through the
+ * residual): y[t] = res[t] + sum_{r ascending, dst_row[t,r] >= 0} g[t,r] Y[dst_row[t,r]],
+ * in binary64.  Y is binary64 [R][H]; residual (dtype) may be NULL.
+ * Only the tokens listed in `tokens` (n_tok of them) are computed when tokens != NULL;
+ * y then holds n_tok rows in that order.
+ */
+void oracle_combine(int64_t T, int64_t H, int k, int dtype, const double *Y, const float *topk_gate,
+                    const int32_t *dst_row, const void *residual, int64_t n_tok, const int64_t *tokens, double *y) {
+  int64_t n = tokens ? n_tok : T;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = tokens ? tokens[i] : i;
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = residual ? elem(residual, dtype, t * H + c) : 0.0;
+      for (int r = 0; r < k; ++r) {
+        int32_t d = dst_row[t * k + r];
+        if (d >= 0) acc += (double)topk_gate[t * k + r] * Y[(int64_t)d * H + c];
+      }
+      y[i * H + c] = acc;
+    }
+  }
+}
+
+/*
+ * Whole-layer output for selected tokens, from a routing plan this oracle made:
+ * y[t] = res[t] + sum over kept choices of g * FFN_e(x[t]).  Dispatch is a copy,
+ * so an expert's input row for (t, r) is x[t] itself.
+ */
+void oracle_token_outputs(int64_t n_tok, const int64_t *tokens, int64_t H, int64_t F, int k, int dtype, int act,
+                          const void *x, const int32_t *topk_idx, const float *topk_gate, const int32_t *dst_row,
+                          const void *W1, const void *W3, const void *W2, const void *residual, double *y) {
+  size_t eb = dtype == OR_BF16 ? 2 : 4;
+  int64_t nr = 0;
+  for (int64_t i = 0; i < n_tok; ++i)
+    for (int r = 0; r < k; ++r) nr += dst_row[tokens[i] * k + r] >= 0;
+  char *xs = (char *)calloc((size_t)(nr > 0 ? nr : 1) * (size_t)H, eb);
+  int32_t *es = (int32_t *)calloc((size_t)(nr > 0 ? nr : 1), sizeof(int32_t));
+  double *Ys = (double *)malloc(sizeof(double) * (size_t)(nr > 0 ? nr : 1) * (size_t)H);
+  int64_t j = 0;
+  for (int64_t i = 0; i < n_tok; ++i)
+    for (int r = 0; r < k; ++r)
+      if (dst_row[tokens[i] * k + r] >= 0) {
+        memcpy(xs + (size_t)j * H * eb, (const char *)x + (size_t)tokens[i] * H * eb, (size_t)H * eb);
+        es[j++] = topk_idx[tokens[i] * k + r];
+      }
+  oracle_expert_rows(nr, es, H, F, dtype, act, xs, W1, W3, W2, Ys);
+  j = 0;
+  for (int64_t i = 0; i < n_tok; ++i) {
+    int64_t t = tokens[i];
+    for (int64_t c = 0; c < H; ++c) y[i * H + c] = residual ? elem(residual, dtype, t * H + c) : 0.0;
+    for (int r = 0; r < k; ++r)
+      if (dst_row[t * k + r] >= 0) {
+        double g = (double)topk_gate[t * k + r];
+        for (int64_t c = 0; c < H; ++c) y[i * H + c] += g * Ys[j * H + c];
+        ++j;
+      }
+  }
+  free(xs);
+  free(es);
+  free(Ys);
+}
