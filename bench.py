@@ -1,0 +1,292 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+One step = one moe_forward (route -> slot assignment -> dispatch -> expert FFN ->
+combine) over one batch of seeded synthetic tokens already resident in HBM.
+Default workload: the Switch-style top-1 layer (T=16384, H=768, E=64, k=1,
+F=3072, GELU, cf=1.0 with drop, bf16 activations/weights, fp32 router).
+
+Prints one JSON line (see the design doc for the roofline and baseline definitions).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s + expert-GEMM % MFMA peak + route/dispatch % HBM BW"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # fp32 matrix
+PEAK_F64_TFLOPS = 78.6         # fp64 (vector and matrix)
+
+WORKLOADS = {
+    "1": "switch-tiny-fp32-T256-H64-E4-k1-F128-relu-cf1.25",
+    "2": "switch-top1-bf16-T16384-H768-E64-k1-F3072-gelu-cf1.0",
+    "3a": "ds7508-top4-bf16-T32768-H512-E12-k4-F2048-gelu-cf1.0",
+    "3b": "ds7508-top4-bf16-T32768-H512-E12-k4-F2048-gelu-cf0.5",
+    "3c": "ds7508-top4-bf16-T32768-H512-E12-k4-F2048-gelu-cf0.25",
+    "4": "mixtral-top2-bf16-T8192-H4096-E8-k2-F14336-swiglu-dropless",
+    "5": "deepseek-top8-bf16-T4096-H7168-E256-k8-F2048-swiglu-dropless",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "top_routing_expert_router_amd", "csrc", "ffn.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per expert-stage launch pair from the committed rocprofv3 PMC summary,
+    if it was taken on the current expert-FFN source; else None."""
+    path = os.path.join(ROOT, "profiles", f"expert_ffn_pmc_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("ffn_hip_sha256_16") != src_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_step_expert_stage"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the multi-GPU (expert-parallel) path is "
+                                   "a design in DESIGN.md, not code", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from top_routing_expert_router_amd import binding as B
+    from top_routing_expert_router_amd.synth import recipes
+
+    run = recipes.RUNS[args.config]
+    workload = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    B.lib()  # fail loudly if the library is not built
+    cfg = B.MoEConfig.from_run(run)
+    bf16 = run.dtype == recipes.BF16
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    eb = run.elem_bytes
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t0 = time.time()
+    x_h = recipes.gen_x(run)
+    wg_h, bias_h = recipes.gen_router(run)
+    keep_host = run.E * run.m * run.H * run.F * eb <= (4 << 30)  # host copies for the CPU baseline
+    host_w = {}
+
+    def upload(which):
+        out_f, in_f = (run.F, run.H) if which in ("w1", "w3") else (run.H, run.F)
+        w = torch.empty((run.E, out_f, in_f), dtype=tdt, device=dev)
+        per = max(1, (1 << 26) // (out_f * in_f))
+        parts = []
+        for e0 in range(0, run.E, per):
+            es = list(range(e0, min(run.E, e0 + per)))
+            p = recipes.gen_expert_weight(run, which, experts=es)
+            blk = np.stack([p[e] for e in es])
+            hb = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16) if blk.dtype == np.uint16 \
+                else torch.from_numpy(blk)
+            w[e0:e0 + len(es)].copy_(hb)
+            if keep_host:
+                parts.append(blk)
+        if keep_host:
+            host_w[which] = np.concatenate(parts)
+        return w
+
+    x = up(x_h)
+    wg, bias = up(wg_h), up(bias_h)
+    w1 = upload("w1")
+    w3 = upload("w3") if run.act == recipes.SWIGLU else None
+    w2 = upload("w2")
+    rmax = B.max_rows(cfg)
+    plan = B.alloc_plan(cfg, dev)
+    X = torch.empty((max(rmax, 1), run.H), dtype=tdt, device=dev)
+    Y = torch.empty_like(X)
+    y = torch.empty((run.T, run.H), dtype=tdt, device=dev)
+    ws = B.alloc_workspace(cfg, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s: {workload}, R_max={rmax}, ws={ws.numel() / 2**20:.1f} MiB")
+
+    def step():
+        B.forward(cfg, x, wg, bias, w1, w3, w2, x, y, plan, X, Y, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole-layer steps, back to back on one stream
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+
+    # ---- per-stage durations: the same kernels through the stage entry points,
+    # HIP events recorded on the stream the kernels run on (torch's current stream)
+    stages = ("route", "dispatch", "expert_ffn", "combine")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    acc = {s: 0.0 for s in stages}
+    for _ in range(args.steps):
+        ev[0].record()
+        B.route(cfg, x, wg, bias, plan, ws)
+        ev[1].record()
+        B.dispatch(cfg, x, plan, X)
+        ev[2].record()
+        B.expert_ffn(cfg, X, plan, w1, w3, w2, Y, ws)
+        ev[3].record()
+        B.combine(cfg, Y, plan, x, y)
+        ev[4].record()
+        torch.cuda.synchronize()
+        for i, s in enumerate(stages):
+            acc[s] += ev[i].elapsed_time(ev[i + 1])
+    stage_us = {s: acc[s] / args.steps * 1e3 for s in stages}
+    log("[bench] stages (us): " + ", ".join(f"{s}={v:.1f}" for s, v in stage_us.items()))
+
+    # ---- algorithmic work per step (from the plan of this batch)
+    kept = plan["kept"].cpu().numpy()
+    R = int(kept.sum())
+    nonempty = int((kept > 0).sum())
+    T, H, E, k, F, m = run.T, run.H, run.E, run.k, run.F, run.m
+    ffn_flops = 2.0 * R * H * F * m
+    ffn_bytes = nonempty * m * H * F * eb + 2.0 * R * H * eb
+    route_bytes = T * H * eb + H * E * 4 + E * 4 + T * k * 12
+    route_flops = 2.0 * T * H * E
+    disp_bytes = T * H * eb + R * H * eb
+    comb_bytes = R * H * eb + 2.0 * T * H * eb
+    mfma_peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+
+    def gbs(b, us):
+        return b / (us * 1e-6) / 1e9
+
+    t_ffn = stage_us["expert_ffn"]
+    ffn_tflops = ffn_flops / (t_ffn * 1e-6) / 1e12
+    ffn_gbs = gbs(ffn_bytes, t_ffn)
+    t_mfma = ffn_flops / (mfma_peak * 1e12) * 1e6
+    t_hbm = ffn_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ffn_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(ffn_tflops / mfma_peak, 4)}
+    roof["traffic"] = read_traffic(workload)
+    roof["kernel"] = "expert_ffn (grouped GEMM1 + GEMM2 launches)"
+    roof["algorithmic_per_launch"] = {"flops": ffn_flops, "bytes": ffn_bytes}
+
+    route_roof_us = max(route_bytes / (PEAK_HBM_GBS * 1e3), route_flops / (PEAK_F64_TFLOPS * 1e6))
+    stages_out = {
+        "route": {"us": round(stage_us["route"], 2), "GB_s": round(gbs(route_bytes, stage_us["route"]), 1),
+                  "hbm_frac": round(gbs(route_bytes, stage_us["route"]) / PEAK_HBM_GBS, 4),
+                  "roofline_frac": round(route_roof_us / stage_us["route"], 4),
+                  "note": "fp64-accumulated router: roofline = max(bytes/HBM, 2THE/fp64 peak)"},
+        "dispatch": {"us": round(stage_us["dispatch"], 2), "GB_s": round(gbs(disp_bytes, stage_us["dispatch"]), 1),
+                     "hbm_frac": round(gbs(disp_bytes, stage_us["dispatch"]) / PEAK_HBM_GBS, 4)},
+        "expert_ffn": {"us": round(t_ffn, 2), "TFLOP_s": round(ffn_tflops, 1),
+                       "mfma_frac": round(ffn_tflops / mfma_peak, 4), "GB_s": round(ffn_gbs, 1),
+                       "roofline_frac": round(max(t_mfma, t_hbm) / t_ffn, 4)},
+        "combine": {"us": round(stage_us["combine"], 2), "GB_s": round(gbs(comb_bytes, stage_us["combine"]), 1),
+                    "hbm_frac": round(gbs(comb_bytes, stage_us["combine"]) / PEAK_HBM_GBS, 4)},
+    }
+
+    # ---- CPU baseline: the oracle on the machine's host cores, bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(run, x_h, wg_h, bias_h, host_w, args.cpu_seconds) if keep_host else None
+
+    value = T / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs, random-init weights)",
+        "config": {"workload": workload, "T": T, "H": H, "E": E, "k": k, "F": F,
+                   "act": ["relu", "gelu", "swiglu"][run.act],
+                   "capacity": B.capacity(cfg), "R_kept": R, "dropped": T * k - R, "router": "fp32 logits (fp64 accumulation)"},
+        "expert_gemm_tflops": round(ffn_tflops, 1),
+        "expert_gemm_mfma_frac": round(ffn_tflops / mfma_peak, 4),
+        "route_dispatch_hbm_frac": {"route": stages_out["route"]["hbm_frac"],
+                                    "dispatch": stages_out["dispatch"]["hbm_frac"],
+                                    "combine": stages_out["combine"]["hbm_frac"]},
+        "stages": stages_out,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(run, x_h, wg_h, bias_h, host_w, target_s):
+    """Oracle tokens/s: routing over the whole batch (capacity needs every token),
+    the expert FFN + combine on a sample of tokens, scaled to the batch."""
+    import numpy as np
+
+    import oracle
+
+    C = None if run.dropless else oracle.capacity(run.T, run.k, run.E, run.cf, run.min_capacity)
+    t0 = time.perf_counter()
+    plan = oracle.route(x_h, run.dtype, wg_h, bias_h, run.k, run.gate_mode, C)
+    t_route = time.perf_counter() - t0
+    n = 64
+    rng = np.random.default_rng(0)
+    while True:
+        toks = np.sort(rng.choice(run.T, size=min(n, run.T), replace=False))
+        t1 = time.perf_counter()
+        oracle.token_outputs(toks, x_h, run.dtype, run.act, plan, host_w["w1"], host_w.get("w3"), host_w["w2"],
+                             residual=x_h)
+        t_s = time.perf_counter() - t1
+        if t_s >= 0.3 * target_s or n >= run.T:
+            break
+        n = min(run.T, int(n * max(2.0, 0.5 * target_s / max(t_s, 1e-3))))
+    per_tok = t_route / run.T + t_s / len(toks)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": round(1.0 / per_tok, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"routing of all {run.T} tokens ({t_route:.2f}s) + expert FFN and combine of {len(toks)} "
+                      f"sampled tokens ({t_s:.2f}s), fp64 C oracle with OpenMP"}
+
+
+if __name__ == "__main__":
+    main()

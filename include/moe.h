@@ -1,0 +1,180 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) token-choice MoE FFN layer forward.
+ *
+ * One device's share of a Mixture-of-Experts FFN layer (no expert parallelism):
+ *   route    logits = x . Wg (+ bias) in fp32, softmax, top-k, gates
+ *   assign   capacity-limited slot assignment (drop or dropless), packing
+ *   dispatch gather token rows into expert-contiguous buffers
+ *   experts  grouped-GEMM FFN (ReLU / GELU / SwiGLU)
+ *   combine  gate-weighted sum of expert outputs plus an optional residual
+ *
+ * Sources (web pages, by title and section):
+ *   [EP]     "Expert-parallel MoE training" explainer (blog.vllbc.top, visual
+ *            reading): router Wg in R^{HxE} with softmax then top-k, or top-k then
+ *            normalise over the selected; capacity = ceil((T*k/E)*cf); drop or
+ *            dropless; "position" drop policy; the walk through one MoE layer
+ *            (permute, experts, unpermute, gate-weighted sum, residual); gated
+ *            experts with gate / up / down matrices (memory calculator).
+ *   [DS7508] DeepSpeed discussion #7508 "The MoE spends too much time on the gate
+ *            network": capacity ceil((tokens/experts)*cf*k) (10,923 worked value);
+ *            the dense one-hot [T,E,C] dispatch mask that blows up; padding-free
+ *            execution on the actual tokens per expert.
+ *   [SW]     Switch Transformers explainer ("AI 十大论文精讲（七）: Switch
+ *            Routing"): §1.1 router logits, softmax, argmax, y = E_i(x) p_i(x);
+ *            §1.2 capacity factor, overflow passes through the residual; §2.1
+ *            selective precision (router input, logits and softmax in fp32).
+ *
+ * Conventions (all entry points):
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees, or synchronises; it only enqueues kernels on `stream`.
+ *   - Pointers marked "device" are device (HBM) addresses; moe_config is read on
+ *     the host during the call and may be freed afterwards.
+ *   - stream: a hipStream_t passed as void* (NULL = the default stream).  Results
+ *     are valid once the stream has been synchronised.  No device-to-host copy
+ *     happens inside any call: the number of kept rows R stays on the device.
+ *   - Errors: every argument check runs on the host before anything is enqueued;
+ *     on error nothing is enqueued.  MOE_ERR_HIP means a launch failed (the
+ *     message of the failure is available from moe_last_error()).  No exception
+ *     crosses the ABI.
+ *   - Alignment: 16-byte aligned pointers with H % 8 == 0 and F % 8 == 0 take the
+ *     vector paths; every other shape takes a correct scalar path.
+ *   - Preconditions: inputs are finite (NaN / Inf behaviour is unspecified).
+ *   - Thread safety: calls are independent given distinct plan, workspace and
+ *     output buffers.
+ *   - Determinism: no floating-point atomics; repeated calls give the same bits.
+ *
+ * Data layout (row-major, 0-based):
+ *   x, residual, y : [T][H]  of dtype
+ *   Wg             : [H][E]  fp32 (logits = x . Wg)
+ *   bias           : [E]     fp32, may be NULL
+ *   W1 (gate/W_in) : [E][F][H] of dtype   (each matrix stored [out][in])
+ *   W3 (up)        : [E][F][H] of dtype   (SwiGLU only, else NULL)
+ *   W2 (down/W_out): [E][H][F] of dtype
+ *   X, Y           : [R_max][H] of dtype, expert-contiguous packed rows;
+ *                    rows [offsets[e], offsets[e+1]) belong to expert e.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad shape / mode / NULL required pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* valid in principle but not provided by this build */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype; /* of x, W1/W3/W2, X, Y, residual, y */
+
+/* Gate values g[t][r] of the k chosen experts ([EP] router; [SW] §1.1):
+ *   SOFTMAX_TOPK        p = softmax over all E logits; g_r = p[e_r]          (Switch, DeepSpeed)
+ *   SOFTMAX_TOPK_RENORM g_r = p[e_r] / sum_j p[e_j]                         (DeepSeek-style)
+ *   TOPK_SOFTMAX        g = softmax over the k chosen logits                (Megatron default)
+ * The last two are equal in exact arithmetic (the full denominator cancels). */
+typedef enum { MOE_SOFTMAX_TOPK = 0, MOE_SOFTMAX_TOPK_RENORM = 1, MOE_TOPK_SOFTMAX = 2 } moe_gate_mode;
+
+/* Expert FFN: RELU / GELU (exact erf form): y = act(x W_in) W_out;
+ * SWIGLU: y = (silu(x W_gate) * (x W_up)) W_down. */
+typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
+
+typedef struct {
+  int32_t T;              /* tokens, >= 0 (T = 0 is a valid no-op)            */
+  int32_t H;              /* hidden size, >= 1                                 */
+  int32_t E;              /* experts, 1 .. 1024                                */
+  int32_t k;              /* choices per token, 1 .. min(E, 16)                */
+  int32_t F;              /* expert FFN width, >= 1                            */
+  int32_t dtype;          /* moe_dtype                                         */
+  int32_t gate_mode;      /* moe_gate_mode                                     */
+  int32_t act;            /* moe_act                                           */
+  int32_t dropless;       /* 1: no capacity limit; 0: capacity from cf         */
+  int32_t min_capacity;   /* capacity floor (DeepSpeed-style); 0 = none        */
+  double capacity_factor; /* cf > 0 unless dropless                            */
+} moe_config;
+
+/* Routing plan: device arrays, allocated by the caller, written by moe_route. */
+typedef struct {
+  int32_t *topk_idx;  /* [T][k]  chosen experts; r = 0 is the largest logit, ties to the lower index */
+  float *topk_gate;   /* [T][k]  fp32 gate values (moe_gate_mode)                                  */
+  int32_t *dst_row;   /* [T][k]  packed row of the assignment in X / Y, or -1 if dropped            */
+  int32_t *demand;    /* [E]     assignments per expert before the capacity limit                   */
+  int32_t *kept;      /* [E]     min(demand, C)                                                      */
+  int32_t *offsets;   /* [E+1]   exclusive prefix sum of kept; offsets[E] = R                        */
+  int32_t *row_token; /* [R_max] token of each packed row (rows >= R are not written)                */
+  int32_t *n_dropped; /* [1]     T*k - R                                                             */
+  float *logits;      /* [T][E]  optional: fp32 router logits are written here when not NULL        */
+} moe_plan;
+
+/* ---- host-only helpers (no HIP call; usable without a GPU) ------------------ */
+
+/* MOE_OK, or the reason the configuration is rejected. */
+moe_status moe_validate(const moe_config *cfg);
+
+/* Expert capacity C = max(min_capacity, ceil(double(T*k) * cf / E)) ([EP] capacity;
+ * [DS7508]); -1 when dropless; -2 when the configuration is invalid. */
+int64_t moe_capacity(const moe_config *cfg);
+
+/* R_max: T*k when dropless, else min(T*k, E*C); the row count X / Y / row_token
+ * must hold.  -1 when the configuration is invalid. */
+int64_t moe_max_rows(const moe_config *cfg);
+
+/* Device workspace bytes that moe_route / moe_expert_ffn / moe_forward need
+ * (0 when the configuration is invalid). */
+size_t moe_workspace_bytes(const moe_config *cfg);
+
+const char *moe_status_str(moe_status s);
+
+/* Text of the last MOE_ERR_HIP failure on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ---- stream-ordered entry points ----------------------------------------------- */
+
+/* Route: logits ([SW] §1.1, fp32 per §2.1; the dot product is accumulated in
+ * binary64 and rounded once to fp32), top-k selection (larger logit first, ties to
+ * the lower expert index), gates (moe_gate_mode), capacity ([EP]; [DS7508]), and
+ * slot assignment in choice-major priority — every token's first choice before
+ * any second choice, token order inside each ([EP] "position" policy) — then
+ * packing into expert-contiguous rows.
+ * x: device [T][H] dtype.  Wg: device [H][E] fp32.  bias: device [E] fp32 or NULL.
+ * plan: every pointer but logits required.  ws: device, >= moe_workspace_bytes. */
+moe_status moe_route(const moe_config *cfg, const void *x, const float *Wg, const float *bias,
+                     const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch ([EP] layer walk-through: group tokens by target expert):
+ * X[dst_row[t][r]] = x[t] for every kept assignment (a bit copy).
+ * Reads plan->dst_row; X: device [R_max][H] dtype. */
+moe_status moe_dispatch(const moe_config *cfg, const void *x, const moe_plan *plan, void *X, void *stream);
+
+/* Expert FFN on the packed rows ([EP] gated experts; [SW] W_in / W_out;
+ * [DS7508] padding-free execution on the actual rows per expert): for expert e,
+ * rows [offsets[e], offsets[e+1]) of X give the same rows of Y.  bf16 runs use
+ * bf16 MFMA with fp32 accumulation; the hidden activation is stored in the
+ * workspace in dtype.  Reads plan->offsets only.  W3 required iff SWIGLU. */
+moe_status moe_expert_ffn(const moe_config *cfg, const void *X, const moe_plan *plan, const void *W1,
+                          const void *W3, const void *W2, void *Y, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine ([EP] unpermute, multiply by the gate, sum, add the residual; [SW] §1.2
+ * overflow passes through the residual):
+ * y[t] = residual[t] + sum_{r ascending, dst_row >= 0} topk_gate[t][r] * Y[dst_row[t][r]],
+ * accumulated in fp32 and rounded once to dtype.  residual: device [T][H] or NULL (= 0).
+ * Gates are not renormalised after drops. */
+moe_status moe_combine(const moe_config *cfg, const void *Y, const moe_plan *plan, const void *residual,
+                       void *y, void *stream);
+
+/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine, in
+ * that order on `stream`.  X and Y: device [R_max][H] dtype. */
+moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, const float *bias, const void *W1,
+                       const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,
+                       void *X, void *Y, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

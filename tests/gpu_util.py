@@ -1,0 +1,106 @@
+"""Helpers for the GPU parity tests: host <-> device marshalling, tolerances."""
+import numpy as np
+
+from top_routing_expert_router_amd import binding as B
+from top_routing_expert_router_amd import synth
+from top_routing_expert_router_amd.synth import recipes
+
+# Output tolerances of the layer (residual-free output y):
+#   bf16 runs: max-abs <= 2e-2 and relative L2 <= 5e-3; fp32 runs: relative L2 <= 1e-5.
+BF16_MAXABS, BF16_RELL2, F32_RELL2 = 2e-2, 5e-3, 1e-5
+GATE_REL = 1e-5
+LOGIT_RELL2 = 1e-5
+
+PLAN_INT = ("topk_idx", "dst_row", "demand", "kept", "offsets", "n_dropped")
+
+
+def dev(a, device):
+    import torch
+
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def host(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f64(a):
+    if a.dtype == np.uint16:
+        return synth.bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+def err_stats(got, ref):
+    got, ref = as_f64(got) if got.dtype != np.float64 else got, ref
+    d = got - ref
+    maxabs = float(np.abs(d).max()) if d.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d)) / nref if nref > 0 else float(np.linalg.norm(d))
+    return maxabs, rel
+
+
+def assert_close(got, ref, bf16, what=""):
+    maxabs, rel = err_stats(got, ref)
+    print(f"[parity] {what}: max-abs {maxabs:.3e} rel-L2 {rel:.3e}", flush=True)
+    if bf16:
+        assert maxabs <= BF16_MAXABS and rel <= BF16_RELL2, (what, maxabs, rel)
+    else:
+        assert rel <= F32_RELL2, (what, maxabs, rel)
+
+
+def assert_plan_equal(gplan, oplan, what=""):
+    """Discrete plan: bit-exact.  Gates: relative 1e-5."""
+    R = oplan["R"]
+    for n in PLAN_INT:
+        g = host(gplan[n])
+        o = oplan[n]
+        assert np.array_equal(g.reshape(o.shape), o), f"{what}: {n} differs ({int((g.reshape(o.shape) != o).sum())})"
+    g_rt = host(gplan["row_token"])[:R]
+    assert np.array_equal(g_rt, oplan["row_token"]), f"{what}: row_token differs"
+    gg = host(gplan["topk_gate"]).astype(np.float64)
+    og = oplan["topk_gate"].astype(np.float64)
+    rel = np.abs(gg - og) / np.maximum(np.abs(og), 1e-30)
+    assert rel.max(initial=0.0) <= GATE_REL, f"{what}: gate rel err {rel.max()}"
+
+
+def plan_to_device(oplan, cfg, device):
+    """Upload an oracle-made plan (as the input of a single-stage GPU test)."""
+    import torch
+
+    p = B.alloc_plan(cfg, device)
+    for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets", "n_dropped"):
+        p[n].copy_(torch.from_numpy(np.ascontiguousarray(oplan[n]).reshape(tuple(p[n].shape))))
+    rt = np.full(p["row_token"].numel(), -1, np.int32)
+    rt[:oplan["R"]] = oplan["row_token"]
+    p["row_token"].copy_(torch.from_numpy(rt))
+    return p
+
+
+def upload_expert_weight(run, which, device, keep=()):
+    """Device tensor of a whole expert weight, generated expert by expert (bounded host memory).
+    Returns (tensor, {e: host copy} for the experts in `keep`)."""
+    import torch
+
+    out_f, in_f = (run.F, run.H) if which in ("w1", "w3") else (run.H, run.F)
+    tdt = torch.bfloat16 if run.dtype == recipes.BF16 else torch.float32
+    w = torch.empty((run.E, out_f, in_f), dtype=tdt, device=device)
+    kept = {}
+    per = max(1, (1 << 26) // (out_f * in_f))  # ~64M elements per host chunk
+    for e0 in range(0, run.E, per):
+        es = list(range(e0, min(run.E, e0 + per)))
+        part = recipes.gen_expert_weight(run, which, experts=es)
+        block = np.stack([part[e] for e in es])
+        w[e0:e0 + len(es)].copy_(dev(block, "cpu"))
+        for e in es:
+            if e in keep:
+                kept[e] = part[e]
+    return w, kept

@@ -1,0 +1,107 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32.  A bf16 value is the upper half of a binary32, so widening is
+// a shift; narrowing rounds to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Loads 8 consecutive elements [i, i+8) of a row of `n` elements as fp32,
+// zero-filling past the end.  `vec_ok` promises 16-byte alignment of every
+// vector access (the row base and i are multiples of the vector width).
+template <bool kBF16>
+__device__ __forceinline__ void load8_f32(const void* row, int64_t i, int64_t n, bool vec_ok, float (&v)[8]) {
+  if (kBF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(row);
+    if (vec_ok && i + 8 <= n) {
+      u32x4_t q = *reinterpret_cast<const u32x4_t*>(p + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(q[j] << 16);
+        v[2 * j + 1] = __uint_as_float(q[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (i + j < n) ? bf16_bits_to_f32(p[i + j]) : 0.0f;
+    }
+  } else {
+    const float* p = static_cast<const float*>(row);
+    if (vec_ok && i + 8 <= n) {
+      f32x4_t a = *reinterpret_cast<const f32x4_t*>(p + i);
+      f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + i + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = a[j];
+        v[4 + j] = b[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (i + j < n) ? p[i + j] : 0.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64,
+// at most 1024).  `tmp` must hold blockDim.x / 64 + 1 ints.  Returns the exclusive
+// prefix and writes the block total into *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      int c = tmp[i];
+      tmp[i] = run;
+      run += c;
+    }
+    tmp[nw] = run;
+  }
+  __syncthreads();
+  int ex = tmp[w] + inc - v;
+  *total = tmp[nw];
+  __syncthreads();
+  return ex;
+}
+
+}  // namespace moe

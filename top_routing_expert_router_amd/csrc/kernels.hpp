@@ -1,0 +1,25 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
+                                int H, int E, bool vec_ok, hipStream_t st);
+hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, int nb, int32_t* topk_idx,
+                                float* topk_gate, int32_t* dst_rank, int32_t* hist, hipStream_t st);
+hipError_t launch_slot_scan(int32_t* hist, int Q, int E, int C, int32_t* demand, int32_t* kept, hipStream_t st);
+hipError_t launch_slot_finalize(const int32_t* base, int Q, int nb, int T, int E, int k, int C,
+                                const int32_t* topk_idx, const int32_t* kept, int32_t* dst_row, int32_t* row_token,
+                                int32_t* offsets, int32_t* n_dropped, int rmax, hipStream_t st);
+hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T, int H, int k, int rmax, bool bf16,
+                           bool vec_ok, hipStream_t st);
+hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
+                             const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
+                             int64_t R_max, hipStream_t st);
+hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
+                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st);
+
+}  // namespace moe

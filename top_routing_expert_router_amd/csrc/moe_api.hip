@@ -1,0 +1,215 @@
+// C ABI of the MoE layer forward: argument validation, capacity, workspace
+// sizing and the stream-ordered launch sequence.  Declarations and the
+// contract of every entry point are in include/moe.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace {
+
+constexpr int kBlockTokens = 64;  // tokens per histogram block (one wave in the select kernel)
+constexpr size_t kAlign = 256;
+
+thread_local char g_last_error[256] = "";
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status hip_fail(hipError_t err, const char* where) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(err));
+  return MOE_ERR_HIP;
+}
+
+// Capacity in 64-bit; -1 = dropless.  Plain ceil((T*k/E)*cf), raised to
+// min_capacity ("Expert-parallel MoE training" explainer, capacity section;
+// DeepSpeed discussion #7508).  Evaluated as one multiply, one divide, ceil.
+int64_t capacity_of(const moe_config* c) {
+  if (c->dropless) return -1;
+  const double v = ceil((double)((int64_t)c->T * c->k) * c->capacity_factor / (double)c->E);
+  int64_t C = v > 9.0e18 ? INT64_MAX : (int64_t)v;
+  if (C < c->min_capacity) C = c->min_capacity;
+  return C;
+}
+
+int64_t max_rows_of(const moe_config* c) {
+  const int64_t tk = (int64_t)c->T * c->k;
+  const int64_t C = capacity_of(c);
+  if (C < 0) return tk;
+  const int64_t ec = C > tk ? tk : C * c->E;
+  return ec < tk ? ec : tk;
+}
+
+// Capacity as the kernels use it: an int32 bound that no slot reaches when
+// nothing can be dropped.
+int effective_capacity(const moe_config* c) {
+  const int64_t C = capacity_of(c);
+  const int64_t tk = (int64_t)c->T * c->k;
+  if (C < 0 || C >= tk) return INT32_MAX;
+  return (int)C;
+}
+
+struct Layout {
+  int nb, Q;
+  size_t hist, logits, route_end, h, ffn_end, total;
+};
+
+Layout layout_of(const moe_config* c) {
+  Layout L;
+  L.nb = (c->T + kBlockTokens - 1) / kBlockTokens;
+  L.Q = c->k * L.nb;
+  const size_t eb = c->dtype == MOE_BF16 ? 2 : 4;
+  L.hist = 0;
+  L.logits = align_up(sizeof(int32_t) * (size_t)c->E * (size_t)L.Q);
+  L.route_end = L.logits + align_up(sizeof(float) * (size_t)c->T * (size_t)c->E);
+  L.h = 0;
+  L.ffn_end = align_up(eb * (size_t)max_rows_of(c) * (size_t)c->F);
+  L.total = L.route_end > L.ffn_end ? L.route_end : L.ffn_end;
+  if (L.total == 0) L.total = kAlign;
+  return L;
+}
+
+// The per-assignment arrays may be NULL only when there are no tokens.
+moe_status check_plan(const moe_config* c, const moe_plan* p) {
+  if (!p || !p->demand || !p->kept || !p->offsets || !p->n_dropped) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && (!p->topk_idx || !p->topk_gate || !p->dst_row || !p->row_token)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->H < 1 || c->F < 1) return MOE_ERR_INVALID_ARG;
+  if (c->E < 1 || c->E > 1024) return MOE_ERR_INVALID_ARG;
+  if (c->k < 1 || c->k > 16 || c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)c->T * c->k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->gate_mode < MOE_SOFTMAX_TOPK || c->gate_mode > MOE_TOPK_SOFTMAX) return MOE_ERR_INVALID_ARG;
+  if (c->act < MOE_RELU || c->act > MOE_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (c->dropless != 0 && c->dropless != 1) return MOE_ERR_INVALID_ARG;
+  if (c->min_capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (!c->dropless && !(c->capacity_factor > 0.0 && isfinite(c->capacity_factor))) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int64_t moe_capacity(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return -2;
+  return capacity_of(c);
+}
+
+int64_t moe_max_rows(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return -1;
+  return max_rows_of(c);
+}
+
+size_t moe_workspace_bytes(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return 0;
+  return layout_of(c).total;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const float* bias, const moe_plan* plan,
+                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if ((s = check_plan(c, plan)) != MOE_OK) return s;
+  if ((c->T > 0 && !x) || !Wg) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(c);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(w + L.hist);
+  float* logits = plan->logits ? plan->logits : reinterpret_cast<float*>(w + L.logits);
+  const bool bf16 = c->dtype == MOE_BF16;
+  const int C = effective_capacity(c);
+  hipError_t e;
+  if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
+                                     st)) != hipSuccess)
+    return hip_fail(e, "router_logits");
+  if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, c->gate_mode, L.nb, plan->topk_idx, plan->topk_gate,
+                                     plan->dst_row, hist, st)) != hipSuccess)
+    return hip_fail(e, "router_select");
+  if ((e = moe::launch_slot_scan(hist, L.Q, c->E, C, plan->demand, plan->kept, st)) != hipSuccess)
+    return hip_fail(e, "slot_scan");
+  if ((e = moe::launch_slot_finalize(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->kept, plan->dst_row,
+                                     plan->row_token, plan->offsets, plan->n_dropped, (int)max_rows_of(c), st)) != hipSuccess)
+    return hip_fail(e, "slot_finalize");
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_config* c, const void* x, const moe_plan* plan, void* X, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (!plan || (c->T > 0 && (!plan->dst_row || !x || !X))) return MOE_ERR_INVALID_ARG;
+  const bool bf16 = c->dtype == MOE_BF16;
+  hipError_t e = moe::launch_dispatch(x, plan->dst_row, X, c->T, c->H, c->k, (int)max_rows_of(c), bf16,
+                                      aligned16(x) && aligned16(X), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "dispatch");
+}
+
+moe_status moe_expert_ffn(const moe_config* c, const void* X, const moe_plan* plan, const void* W1, const void* W3,
+                          const void* W2, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (!plan || !plan->offsets) return MOE_ERR_INVALID_ARG;
+  if (!W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  const int64_t R_max = max_rows_of(c);
+  if (R_max > 0 && (!X || !Y)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(c);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  void* h = static_cast<char*>(ws) + L.h;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(X) && aligned16(Y) && aligned16(W1) &&
+                   aligned16(W3) && aligned16(W2) && aligned16(h);
+  hipError_t e = moe::launch_expert_ffn(X, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec, R_max,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "expert_ffn");
+}
+
+moe_status moe_combine(const moe_config* c, const void* Y, const moe_plan* plan, const void* residual, void* y,
+                       void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (!plan || (c->T > 0 && (!plan->dst_row || !plan->topk_gate || !y))) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && !Y && max_rows_of(c) > 0) return MOE_ERR_INVALID_ARG;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && aligned16(Y) && aligned16(y) && aligned16(residual);
+  hipError_t e = moe::launch_combine(Y, plan->dst_row, plan->topk_gate, residual, y, c->T, c->H, c->k,
+                                     (int)max_rows_of(c), bf16, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "combine");
+}
+
+moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
+                       const void* W3, const void* W2, const void* residual, void* y, const moe_plan* plan, void* X,
+                       void* Y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if ((s = check_plan(c, plan)) != MOE_OK) return s;
+  if (!W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr) || !Wg) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && (!x || !y || !X || !Y)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
+  if ((s = moe_route(c, x, Wg, bias, plan, ws, ws_bytes, stream)) != MOE_OK) return s;
+  if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
+  if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
+  return moe_combine(c, Y, plan, residual, y, stream);
+}
+
+}  // extern "C"
