@@ -280,3 +280,26 @@ def test_capacity_calculator_scenario_on_gpu(gpu):
     _check_route(r, gplan, oplan)
     assert U.host(gplan["n_dropped"])[0] == 472
     assert U.host(gplan["offsets"])[-1] == 2048 - 472
+
+
+@pytest.mark.parametrize("act,F,H", [(recipes.GELU, 3328, 128), (recipes.SWIGLU, 1664, 128), (recipes.RELU, 1280, 256)])
+def test_expert_ffn_large_tiles(gpu, act, F, H):
+    """Expert FFN on shapes that take the 256-row pipelined tiles (many rows per expert),
+    every output element compared."""
+    import torch
+
+    r = recipes.SMALL["4"].scaled(name=f"tiles-{act}", T=4096, H=H, F=F, E=4, k=1, act=act, dropless=1,
+                                  gate_mode=recipes.SOFTMAX_TOPK, bias="n1")
+    d = recipes.gen_all(r)
+    oplan = _oracle_route(r, d["x"], d["wg"], d["bias"])
+    X = oracle.dispatch(d["x"], r.dtype, oplan)
+    Yref = oracle.expert_ffn(X, oplan["offsets"], r.dtype, r.act, d["w1"], d["w3"], d["w2"])
+    cfg = B.MoEConfig.from_run(r)
+    gp = U.plan_to_device(oplan, cfg, gpu)
+    Xd = torch.zeros((B.max_rows(cfg), r.H), dtype=torch.bfloat16, device=gpu)
+    Xd[:oplan["R"]].copy_(U.dev(X, "cpu"))
+    Yd = torch.zeros_like(Xd)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.expert_ffn(cfg, Xd, gp, U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), Yd, ws)
+    torch.cuda.synchronize()
+    U.assert_close(U.host(Yd)[:oplan["R"]], Yref, True, f"expert FFN large tiles act={act}")

@@ -20,11 +20,26 @@ namespace moe {
 
 enum { EPI_NONE = 0, EPI_RELU = 1, EPI_GELU = 2, EPI_SWIGLU = 3 };
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (|error| <= 1.5e-7 for all x), with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, ax, 1.0f));
+  float p = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+  p = __builtin_fmaf(t, p, 1.421413741f);
+  p = __builtin_fmaf(t, p, -0.284496736f);
+  p = __builtin_fmaf(t, p, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(__builtin_fmaf(-p, e, 1.0f), x);
+}
+
 template <int EPI>
 __device__ __forceinline__ float epilogue(float a, float b) {
   if (EPI == EPI_RELU) return a > 0.0f ? a : 0.0f;
-  if (EPI == EPI_GELU) return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
-  if (EPI == EPI_SWIGLU) return (a / (1.0f + expf(-a))) * b;
+  if (EPI == EPI_GELU) return 0.5f * a * (1.0f + erf_as7126(a * 0.70710678118654752f));
+  if (EPI == EPI_SWIGLU)  // silu(a) * b = a / (1 + e^-a) * b
+    return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f)) * b;
   return a;
 }
 
@@ -243,6 +258,314 @@ __global__ void __launch_bounds__(64) grouped_gemm_scalar_kernel(const void* __r
   else static_cast<float*>(C)[(size_t)row * N + n] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined persistent grouped GEMM (the bf16 path when K % 32 == 0).
+//
+// Roles: the MFMA's first operand is a weight fragment (rows n), the second a
+// token fragment (rows m), so each lane ends with four consecutive output
+// columns of one token row and writes them as one 8-byte store.
+//
+// Workgroup tile: BM token rows x 256 weight rows (= 256 output columns, or
+// for SwiGLU 128 gate + 128 up rows = 128 output columns), 8 waves as 2 x 4
+// (two per SIMD), each wave (BM/2) token rows x 64 weight rows, i.e.
+// (BM/64) x 2 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.
+//
+// Data movement: global_load_lds_dwordx4 moves 16-byte chunks straight into
+// LDS (no VGPR staging).  A stage holds BM + 256 rows of 32 k (64 B per row);
+// chunk c of row r sits at slot c ^ ((r >> 2) & 3) of its row.  The LDS has 64
+// four-byte banks and serves a 16-byte-per-lane read 16 lanes at a time, so the
+// 16 rows such a phase touches land in 16 distinct 16-byte bank groups.  S
+// stages form a ring: the loads of stage j + S - 1 are issued right after the
+// barrier of step j and waited for S - 1 steps later with an explicit vmcnt
+// (vector memory operations complete in issue order; stores issued in between
+// only make a wait stricter).
+//
+// Persistent: at most one workgroup per CU; workgroup b takes every G-th tile
+// of the device-side tile list (expert-major, then n-tile, then m-tile).  The
+// stage ring runs on across tile boundaries, so the next tile's first loads
+// are in flight while the current tile's epilogue runs.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier ordering LDS accesses for the compiler, without the
+// vmcnt(0) that a memory fence would add (direct-to-LDS loads are waited on
+// explicitly before it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most `after` stages of L loads are outstanding.
+template <int L>
+__device__ __forceinline__ void wait_stages(int after) {
+  switch (after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    case 2: wait_vmcnt<2 * L>(); break;
+    case 3: wait_vmcnt<3 * L>(); break;
+    default: wait_vmcnt<4 * L>(); break;
+  }
+}
+
+struct PipeTile {
+  int e, row0, rows, n0;
+};
+
+constexpr int PG_WAVES = 8;
+
+// BM token rows x WR weight rows per tile, BK k per stage, S stages, waves as
+// WGM (token direction) x 8 / WGM (weight direction).
+template <int BM, int WR, int BK, int S, int WGM, int EPI>
+__global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
+                                                                   const uint16_t* __restrict__ W,
+                                                                   const uint16_t* __restrict__ W2,
+                                                                   uint16_t* __restrict__ C,
+                                                                   const int32_t* __restrict__ offsets, int E,
+                                                                   int N, int K, int rmax) {
+  constexpr bool kGated = EPI == EPI_SWIGLU;
+  constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
+  constexpr int ROWS = BM + WR;                           // rows per stage
+  constexpr int CPR = BK / 8;                             // 16-byte chunks per row
+  constexpr int RSH = CPR == 8 ? 1 : (CPR == 4 ? 2 : 3);  // rows per 256-byte LDS phase = 1 << RSH
+  constexpr int STAGE = ROWS * BK;                        // bf16 elements per stage
+  constexpr int L = ROWS * CPR / (64 * PG_WAVES);         // 16-byte loads per wave per stage
+  constexpr int WGN = PG_WAVES / WGM;
+  constexpr int MF = BM / WGM / 32;                       // token fragments per wave
+  constexpr int NF = WR / WGN / 32;                       // weight fragments per wave
+  constexpr int HF = kGated ? NF / 2 : NF;                // output column fragments per wave
+  constexpr int KS = BK / 16;                             // MFMA k-steps per stage
+  static_assert(ROWS * CPR % (64 * PG_WAVES) == 0 && BM % 64 == 0 && (CPR == 4 || CPR == 8 || CPR == 2), "tile");
+  static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
+  static_assert(S >= 2 && S - 2 <= 4 && (S - 1) * L < 64 && KS % 2 == 0, "stages");
+  extern __shared__ __align__(16) uint16_t smem[];
+  int* s_ts = reinterpret_cast<int*>(smem + S * STAGE);  // [E+1] first tile of each expert
+  int* s_off = s_ts + (E + 1);                             // [E+1] offsets
+  __shared__ int s_scan[PG_WAVES + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int ntn = (N + BN - 1) / BN;
+
+  {  // tile list: ceil(kept_e / BM) * ntn tiles per expert
+    const int per = (E + 511) / 512;
+    const int e0 = tid * per;
+    int cnt = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) cnt += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+    }
+    int total;
+    int run = block_exclusive_scan(cnt, s_scan, &total);
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        s_ts[e] = run;
+        s_off[e] = offsets[e];
+        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+      }
+    }
+    if (tid == 0) {
+      s_ts[E] = total;
+      s_off[E] = offsets[E];
+    }
+    __syncthreads();
+  }
+  const int G = gridDim.x;
+  const int total_tiles = s_ts[E];
+  // Workgroups are dealt to the 8 XCDs round-robin (b % 8).  Round i gives XCD
+  // x the contiguous tile range [i*G + x*G/8, i*G + (x+1)*G/8), so tiles that
+  // share a weight tile or a block of token rows meet in the same L2.
+  const int slot = (G % 8 == 0) ? ((int)blockIdx.x % 8) * (G / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int my_tiles = total_tiles > slot ? (total_tiles - 1 - slot) / G + 1 : 0;
+  const int nk = K / BK;
+  const int total_steps = my_tiles * nk;
+  if (total_steps == 0) return;
+
+  auto decode = [&](int i) {  // i-th tile of this workgroup
+    const int g = slot + i * G;
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_ts[mid] <= g) lo = mid;
+      else hi = mid;
+    }
+    const int mt_e = (s_off[lo + 1] - s_off[lo] + BM - 1) / BM;
+    const int local = g - s_ts[lo];
+    const int nt = local / mt_e;
+    PipeTile t;
+    t.e = lo;
+    t.row0 = s_off[lo] + (local - nt * mt_e) * BM;
+    t.rows = min(min(BM, s_off[lo + 1] - t.row0), rmax - t.row0);
+    if (t.rows <= 0) {  // only for offsets inconsistent with the row buffers
+      t.rows = 0;
+      t.row0 = 0;
+    }
+    t.n0 = nt * BN;
+    return t;
+  };
+
+  // chunk c of stage row r -> LDS element offset.  A 16-byte-per-lane read is
+  // served 16 lanes (256 B, all 64 banks) at a time; rows that share a phase
+  // get different chunk slots.
+  auto lds_pos = [](int r, int c) { return (r * CPR + (c ^ ((r >> RSH) & (CPR - 1)))) * 8; };
+
+  auto issue = [&](int buf, const PipeTile& t, int kstep) {
+    uint16_t* st = smem + buf * STAGE;
+    const int k0 = kstep * BK;
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+      const int blk = q * PG_WAVES + w;  // 64 lanes = 64 / CPR rows; never straddles the two regions
+      const int p = blk * 64 + lane;
+      const int r = p / CPR;
+      const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
+      const uint16_t* g;
+      if (r < BM) {
+        const int rr = r < t.rows ? r : 0;
+        g = A + (size_t)(t.row0 + rr) * K + k0 + c * 8;
+      } else {
+        const int wr = r - BM;
+        const uint16_t* base = (kGated && wr >= WR / 2) ? W2 : W;
+        int n = t.n0 + (kGated ? (wr & (WR / 2 - 1)) : wr);
+        n = n < N ? n : N - 1;
+        g = base + ((size_t)t.e * N + n) * K + k0 + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds(g, st + blk * 512, 16, 0, 0);
+    }
+  };
+
+  f32x16_t acc[NF][MF];
+  auto zero = [&]() {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[f][i][v] = 0.0f;
+  };
+
+  struct Frags {
+    bf16x8_t w[NF], x[MF];
+  };
+  auto read_frags = [&](int buf, int kk, Frags& fr) {
+    const uint16_t* st = smem + buf * STAGE;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int r = BM + (kGated ? (f / HF) * (WR / 2) + wn * (HF * 32) + (f % HF) * 32 : wn * (NF * 32) + f * 32) +
+                    (lane & 31);
+      fr.w[f] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int r = wm * (MF * 32) + i * 32 + (lane & 31);
+      fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+    }
+  };
+  auto mfma = [&](const Frags& fr) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+        acc[f][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.w[f], fr.x[i], acc[f][i], 0, 0, 0);
+  };
+
+  // accumulator element 4g + jj of lane l: weight row 8g + 4(l / 32) + jj, token row l % 32
+  auto store = [&](const PipeTile& t) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int m = wm * (MF * 32) + i * 32 + (lane & 31);
+      if (m < t.rows) {
+        uint16_t* crow = C + (size_t)(t.row0 + m) * N;
+#pragma unroll
+        for (int f = 0; f < HF; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
+            if (n < N) {
+              float v[4];
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
+                               : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
+              uint2 pk;
+              pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+              pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              *reinterpret_cast<uint2*>(crow + n) = pk;
+            }
+          }
+      }
+    }
+  };
+
+  PipeTile lt = decode(0);  // tile of the next stage to load
+  int lt_i = 0, lt_k = 0, issued = 0;
+  auto issue_next = [&]() {
+    issue(issued % S, lt, lt_k);
+    ++issued;
+    if (++lt_k == nk) {
+      lt_k = 0;
+      if (++lt_i < my_tiles) lt = decode(lt_i);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (issued < total_steps) issue_next();
+
+  // Step j: (loads of stage j + S - 1 into the buffer stage j - 1 used) ->
+  // MFMAs of stage j, reading k-step kk + 1 while k-step kk multiplies ->
+  // wait for stage j + 1, barrier, read its first k-step while the last MFMAs
+  // of stage j drain.  A buffer is overwritten only after the barrier that
+  // follows every wave's last read of it.
+  PipeTile ct = decode(0);  // tile being computed
+  zero();
+  Frags fr[2];
+  wait_stages<L>(issued - 1);
+  lds_barrier();
+  read_frags(0, 0, fr[0]);
+  for (int j = 0; j < total_steps; ++j) {
+    if (issued < total_steps) issue_next();
+    const int buf = j % S;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) read_frags(buf, kk + 1, fr[(kk + 1) & 1]);
+      mfma(fr[kk & 1]);
+    }
+    if (j + 1 < total_steps) {
+      wait_stages<L>(issued - j - 2);  // stage j + 1 complete
+      lds_barrier();
+      read_frags((j + 1) % S, 0, fr[0]);
+    }
+    if ((j + 1) % nk == 0) {
+      store(ct);
+      zero();
+      if (j + 1 < total_steps) ct = decode((j + 1) / nk);
+    }
+  }
+}
+
+template <int BM, int WR, int BK, int S, int WGM, int EPI>
+static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
+                              int N, int K, int64_t R_max, int cus, hipStream_t st) {
+  constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
+  const int ntn = (N + BN - 1) / BN;
+  const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
+  if (tiles <= 0) return hipSuccess;
+  const int grid = (int)(tiles < cus ? tiles : cus);
+  const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
+  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (err != hipSuccess) return err;
+  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI><<<dim3(grid), dim3(64 * PG_WAVES), shm, st>>>(
+      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch_bf16(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, hipStream_t st) {
@@ -274,6 +597,19 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
 template <int EPI>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
                              const int32_t* offsets, int E, int N, int K, int64_t R_max, hipStream_t st) {
+  if (vec && bf16 && K % 64 == 0) {
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+    // 256 x 256 tiles (two 64 KB stages) unless the experts are small or such
+    // tiles would leave CUs idle; else 128 x 256 tiles (three 48 KB stages)
+    constexpr int BN = EPI == EPI_SWIGLU ? 128 : 256;
+    const int64_t tiles256 = (R_max / 256) * ((N + BN - 1) / BN);
+    if (R_max / E > 128 && tiles256 >= 2 * (int64_t)cus)
+      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+  }
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
