@@ -65,6 +65,76 @@ def read_traffic(workload):
         return None
 
 
+EXPERT_KERNEL = "grouped_gemm"
+COPY_BYTES = 256 << 20
+
+
+def _kernel_rows(db_path):
+    import sqlite3
+
+    db = sqlite3.connect(db_path)
+    return db.execute("select name, duration from kernels order by start").fetchall()
+
+
+def summarize_trace(db_path, cmd):
+    """Per-kernel duration summary of a rocprofv3 --kernel-trace database (text)."""
+    import collections
+
+    agg = collections.OrderedDict()
+    for name, dur in _kernel_rows(db_path):
+        a = agg.setdefault(name, [0, 0.0, float("inf"), 0.0])
+        a[0] += 1
+        a[1] += dur
+        a[2] = min(a[2], dur)
+        a[3] = max(a[3], dur)
+    total = sum(v[1] for v in agg.values())
+    print(f"# rocprofv3 kernel-trace summary\n# command: {cmd}\n# durations in microseconds")
+    print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share':>7}  kernel")
+    for name, (c, t, mn, mx) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"{c:6d} {t / c / 1e3:10.2f} {mn / 1e3:10.2f} {mx / 1e3:10.2f} {100 * t / total:6.1f}%  {name[:110]}")
+
+
+def summarize_pmc(fetch_db, write_db, workload, cmd):
+    """HBM bytes of the expert-FFN kernels from FETCH_SIZE / WRITE_SIZE runs, each scaled by
+    what the same counter reads for the plain device copy of COPY_BYTES run in that process."""
+    import sqlite3
+
+    def per_kernel(db_path, counter):
+        db = sqlite3.connect(db_path)
+        rows = db.execute("select name, counter_value from pmc_events where counter_name = ?", (counter,)).fetchall()
+        out = {}
+        for n, v in rows:
+            out.setdefault(n, []).append(v)
+        return out
+
+    f = per_kernel(fetch_db, "FETCH_SIZE")
+    w = per_kernel(write_db, "WRITE_SIZE")
+
+    def copy_kib(d):
+        vals = [v for n, vs in d.items() if "copy" in n.lower() or "elementwise" in n.lower() for v in vs
+                if v * 1024 > COPY_BYTES / 8]
+        return sorted(vals)[len(vals) // 2] if vals else None
+
+    cf, cw = copy_kib(f), copy_kib(w)
+    sf = COPY_BYTES / (cf * 1024) if cf else 1.0
+    sw = COPY_BYTES / (cw * 1024) if cw else 1.0
+    print(f"# rocprofv3 PMC summary: HBM bytes of the expert FFN launches\n# command: {cmd}")
+    print(f"workload: {workload}")
+    print(f"ffn_hip_sha256_16: {src_hash()}")
+    print(f"copy_kernel_bytes: {COPY_BYTES}")
+    print(f"fetch_scale_from_copy: {sf:.4f}   # copy reads {COPY_BYTES} B; FETCH_SIZE read {cf} KiB")
+    print(f"write_scale_from_copy: {sw:.4f}   # copy writes {COPY_BYTES} B; WRITE_SIZE read {cw} KiB")
+    tot = 0.0
+    for n in sorted(set(f) | set(w)):
+        if EXPERT_KERNEL not in n:
+            continue
+        fb = sum(f.get(n, [0])) / max(len(f.get(n, [1])), 1) * 1024 * sf
+        wb = sum(w.get(n, [0])) / max(len(w.get(n, [1])), 1) * 1024 * sw
+        tot += fb + wb
+        print(f"kernel: {n[:90]}  read_bytes_per_launch: {fb:.4g}  write_bytes_per_launch: {wb:.4g}")
+    print(f"hbm_bytes_per_step_expert_stage: {tot:.6g}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,7 +143,19 @@ def main():
     ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of 256 MiB (the PMC byte-counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DB", help="print the kernel summary of a rocprofv3 database")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print expert-FFN HBM bytes from FETCH_SIZE / WRITE_SIZE rocprofv3 databases")
+    ap.add_argument("--cmd", default="", help="command line to record in a summary")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, WORKLOADS[args.config], args.cmd)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; the multi-GPU (expert-parallel) path is "
                                    "a design in DESIGN.md, not code", "n_gpus": args.gpus}))
@@ -146,6 +228,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- timed region: K whole-layer steps, back to back on one stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
