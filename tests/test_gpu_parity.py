@@ -303,3 +303,74 @@ def test_expert_ffn_large_tiles(gpu, act, F, H):
     B.expert_ffn(cfg, Xd, gp, U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), Yd, ws)
     torch.cuda.synchronize()
     U.assert_close(U.host(Yd)[:oplan["R"]], Yref, True, f"expert FFN large tiles act={act}")
+
+
+# --------------------------------------------------------------------------- split-bf16 router
+
+
+def _radius(x, wg, bias, v):
+    """Certified radius of an approximate logit (bf16 x, H % 64 == 0): c1 ||x|| ||w_e|| + c2 |v| + c3 |b_e|,
+    with c1 = 1.01 (65 (1 + 2^-7) + 129 2^-7) 2^-23 + 4 H 2^-53 (per 64-wide h chunk, an fp32 chain of the
+    64 exact products with the leading bf16 piece and one of the 128 with the two trailing pieces),
+    c2 = 2^-24 + 2^-44 and c3 = H 2^-52."""
+    H = x.shape[1]
+    xf = U.as_f64(x)
+    xn = np.sqrt((xf * xf).sum(1))
+    wn = np.sqrt((wg.astype(np.float64) ** 2).sum(0))
+    c1 = 1.01 * (65 * (1 + 2.0 ** -7) + 129 * 2.0 ** -7) * 2.0 ** -23 + 4 * H * 2.0 ** -53
+    b = np.zeros(wg.shape[1]) if bias is None else np.abs(bias.astype(np.float64))
+    return c1 * xn[:, None] * wn[None, :] + (2.0 ** -24 + 2.0 ** -44) * np.abs(v) + H * 2.0 ** -52 * b[None, :]
+
+
+@pytest.mark.parametrize("name", ["2", "3a", "4", "5"])
+def test_split_router_error_within_radius(gpu, name):
+    """Every logit the split router leaves approximate lies inside its certified radius of the
+    binary64-defined logit, by a wide margin; routing stays bit-exact."""
+    r = recipes.SMALL[name] if name in recipes.SMALL else recipes.SMALL["3x"]
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    _, gplan = _gpu_route(r, gpu, x, wg, bias)
+    oplan = _oracle_route(r, x, wg, bias)
+    gl = U.host(gplan["logits"]).astype(np.float64)
+    ol = oplan["logits"].astype(np.float64)
+    rho = _radius(x, wg, bias, ol)
+    ratio = float((np.abs(gl - ol) / rho).max())
+    print(f"[split] run {r.name}: max |approx - exact| / radius = {ratio:.3e}", flush=True)
+    assert ratio < 0.25
+    U.assert_plan_equal(gplan, oplan, f"split router {r.name}")
+
+
+def test_split_router_pieces_exact(gpu):
+    """One-hot rows of x make logit (t, e) equal to Wg[t][e]: the three bf16 pieces of every fp32
+    weight, with exponents spread over 2^-60 .. 2^20, must add back to it exactly."""
+    H, E = 256, 64
+    rng = np.random.default_rng(7)
+    mant = rng.integers(1 << 23, 1 << 24, size=(H, E)).astype(np.float64)
+    ex = rng.integers(-60, 20, size=(H, E))
+    sign = np.where(rng.random((H, E)) < 0.5, -1.0, 1.0)
+    wg = (sign * mant * np.exp2(ex - 23)).astype(np.float32)
+    x = np.zeros((H, H), np.uint16)
+    x[np.arange(H), np.arange(H)] = 0x3F80  # bf16 1.0
+    r = recipes.SMALL["2"].scaled(name="pieces", T=H, H=H, E=E, k=2, gate_mode=recipes.TOPK_SOFTMAX, bias="none")
+    _, gplan = _gpu_route(r, gpu, x, wg, None)
+    assert np.array_equal(U.host(gplan["logits"]), wg)
+    U.assert_plan_equal(gplan, _oracle_route(r, x, wg, None), "pieces")
+
+
+def test_split_router_exact_and_near_ties(gpu):
+    """Duplicated router columns tie exactly for every token; a copy perturbed in one weight by one
+    ulp ties within rounding.  The recomputed logits decide both, lower index first on exact ties."""
+    r = recipes.SMALL["5"].scaled(name="coltie", T=777, H=256, E=16, k=4, bias="none")
+    x = recipes.gen_x(r)
+    wg, _ = recipes.gen_router(r)
+    wg[:, 2] *= 3.0
+    wg[:, 5] = wg[:, 2]
+    wg[:, 9] = wg[:, 2]
+    wg[17, 9] = np.nextafter(wg[17, 9], np.float32(np.inf))
+    wg[:, 12] = wg[:, 2]
+    wg[200, 12] = np.nextafter(wg[200, 12], np.float32(-np.inf))
+    oplan = _oracle_route(r, x, wg, None)
+    sel = oplan["topk_idx"].reshape(r.T, r.k)
+    assert (sel == 2).any() and ((sel == 5).any(1) & (sel == 2).any(1)).any()
+    _, gplan = _gpu_route(r, gpu, x, wg, None)
+    _check_route(r, gplan, oplan)

@@ -104,4 +104,33 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return ex;
 }
 
+// Explicit waits for direct-to-LDS loads (vector memory operations complete in
+// issue order, so `vmcnt <= N` means all but the last N issued have landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier ordering LDS accesses for the compiler, without the
+// vmcnt(0) that a memory fence would add (direct-to-LDS loads are waited on
+// explicitly before it).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most `after` stages of L loads are outstanding.
+template <int L>
+__device__ __forceinline__ void wait_stages(int after) {
+  switch (after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    case 2: wait_vmcnt<2 * L>(); break;
+    case 3: wait_vmcnt<3 * L>(); break;
+    default: wait_vmcnt<4 * L>(); break;
+  }
+}
+
 }  // namespace moe

@@ -8,6 +8,25 @@ namespace moe {
 
 hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
                                 int H, int E, bool vec_ok, hipStream_t st);
+// Split-bf16 router (bf16 x, H % 64 == 0, 16-byte aligned x): logits with a
+// certified radius, choices and gates per token, exact recomputation of the
+// undecided tokens.  Ranks come from launch_router_rank afterwards.
+struct SplitScratch {
+  void* wp;       // [3][Ep][H] bf16 weight pieces
+  double* wsq;    // [H/64][Ep] partial sums of w^2
+  double* wn;     // [Ep] ||w_e||
+  float* xsq;     // [T] sum_h x^2
+  int2* pairs;    // [T*E] candidate (token, expert)
+  int4* utok;     // [T] queued tokens (token, first pair, pair count)
+  int* count;     // [2] pairs, queued tokens
+};
+int split_router_ep(int E);
+int split_router_hs(int H);
+hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
+                               int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
+                               hipStream_t st);
+hipError_t launch_router_rank(const int32_t* topk_idx, int T, int E, int k, int nb, int32_t* dst_rank, int32_t* hist,
+                              hipStream_t st);
 hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, int nb, int32_t* topk_idx,
                                 float* topk_gate, int32_t* dst_rank, int32_t* hist, hipStream_t st);
 hipError_t launch_slot_scan(int32_t* hist, int Q, int E, int C, int32_t* demand, int32_t* kept, hipStream_t st);

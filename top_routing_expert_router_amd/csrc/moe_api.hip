@@ -54,8 +54,13 @@ int effective_capacity(const moe_config* c) {
 
 struct Layout {
   int nb, Q;
-  size_t hist, logits, route_end, h, ffn_end, total;
+  bool split;  // split-bf16 router buffers present
+  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, route_end, h, ffn_end, total;
 };
+
+// The split-bf16 router runs for bf16 activations with H a multiple of 64 and a
+// 16-byte aligned x; otherwise the binary64 router does.
+bool split_router_shape(const moe_config* c) { return c->dtype == MOE_BF16 && c->H % 64 == 0; }
 
 Layout layout_of(const moe_config* c) {
   Layout L;
@@ -64,7 +69,21 @@ Layout layout_of(const moe_config* c) {
   const size_t eb = c->dtype == MOE_BF16 ? 2 : 4;
   L.hist = 0;
   L.logits = align_up(sizeof(int32_t) * (size_t)c->E * (size_t)L.Q);
-  L.route_end = L.logits + align_up(sizeof(float) * (size_t)c->T * (size_t)c->E);
+  size_t end = L.logits + align_up(sizeof(float) * (size_t)c->T * (size_t)c->E);
+  L.split = split_router_shape(c);
+  L.wp = L.wsq = L.wn = L.xsq = L.pairs = L.utok = L.count = end;
+  if (L.split) {
+    const size_t Ep = (size_t)moe::split_router_ep(c->E), HS = (size_t)moe::split_router_hs(c->H);
+    L.wp = end;
+    L.wsq = L.wp + align_up(sizeof(uint16_t) * 3 * Ep * (size_t)c->H);
+    L.wn = L.wsq + align_up(sizeof(double) * HS * Ep);
+    L.xsq = L.wn + align_up(sizeof(double) * Ep);
+    L.pairs = L.xsq + align_up(sizeof(float) * (size_t)c->T);
+    L.utok = L.pairs + align_up(sizeof(int2) * (size_t)c->T * (size_t)c->E);
+    L.count = L.utok + align_up(sizeof(int4) * (size_t)c->T);
+    end = L.count + kAlign;
+  }
+  L.route_end = end;
   L.h = 0;
   L.ffn_end = align_up(eb * (size_t)max_rows_of(c) * (size_t)c->F);
   L.total = L.route_end > L.ffn_end ? L.route_end : L.ffn_end;
@@ -141,12 +160,28 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   const bool bf16 = c->dtype == MOE_BF16;
   const int C = effective_capacity(c);
   hipError_t e;
-  if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
-                                     st)) != hipSuccess)
-    return hip_fail(e, "router_logits");
-  if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, c->gate_mode, L.nb, plan->topk_idx, plan->topk_gate,
-                                     plan->dst_row, hist, st)) != hipSuccess)
-    return hip_fail(e, "router_select");
+  if (L.split && aligned16(x)) {
+    moe::SplitScratch sc;
+    sc.wp = w + L.wp;
+    sc.wsq = reinterpret_cast<double*>(w + L.wsq);
+    sc.wn = reinterpret_cast<double*>(w + L.wn);
+    sc.xsq = reinterpret_cast<float*>(w + L.xsq);
+    sc.pairs = reinterpret_cast<int2*>(w + L.pairs);
+    sc.utok = reinterpret_cast<int4*>(w + L.utok);
+    sc.count = reinterpret_cast<int*>(w + L.count);
+    if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, c->gate_mode, plan->topk_idx,
+                                      plan->topk_gate, sc, st)) != hipSuccess)
+      return hip_fail(e, "router_split");
+    if ((e = moe::launch_router_rank(plan->topk_idx, c->T, c->E, c->k, L.nb, plan->dst_row, hist, st)) != hipSuccess)
+      return hip_fail(e, "router_rank");
+  } else {
+    if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
+                                       st)) != hipSuccess)
+      return hip_fail(e, "router_logits");
+    if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, c->gate_mode, L.nb, plan->topk_idx,
+                                       plan->topk_gate, plan->dst_row, hist, st)) != hipSuccess)
+      return hip_fail(e, "router_select");
+  }
   if ((e = moe::launch_slot_scan(hist, L.Q, c->E, C, plan->demand, plan->kept, st)) != hipSuccess)
     return hip_fail(e, "slot_scan");
   if ((e = moe::launch_slot_finalize(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->kept, plan->dst_row,

@@ -1,0 +1,639 @@
+// Router logits on the bf16 matrix cores with a certified error radius, and an
+// exact recomputation of the logits whose ordering the radius cannot settle.
+//
+// The routing decision (the k experts of a token and their order; Switch
+// Transformers explainer §1.1, "Expert-parallel MoE training" explainer, router
+// part) is defined on fp32 logits l = fl32(bias + sum_h x*Wg), the sum taken in
+// binary64 (§2.1 of the Switch explainer keeps the router in fp32).  Here:
+//
+//  1. prep:    Wg [H][E] fp32 is split per element into three bf16 values,
+//              w = hi + mid + lo exactly (each residual of an RNE rounding to 8
+//              significant bits has at most 16, then 8 bits left), stored
+//              expert-major [3][Ep][H]; partial sums of w^2 per 64 h.
+//  2. approx:  v = fl32(bias + sum over 64-wide h chunks of two fp32 MFMA
+//              chains, one over the 64 exact products x*hi and one over the
+//              128 products x*mid, x*lo; chain sums added in binary64).  A sum
+//              of n terms whose every addition errs by at most 2^-23 of the
+//              running magnitude (round-to-nearest or truncation alike) is off
+//              by at most ~n 2^-23 sum|terms|; |hi| <= (1 + 2^-8)|w| and
+//              |mid| + |lo| <= 2^-7 |w|; Cauchy-Schwarz gives sum|x*w| <=
+//              ||x|| ||w_e||.  Hence
+//                |v - l_exact| <= rho = c1 ||x|| ||w_e|| + c2 |v| + c3 |bias|.
+//  3. certify: per token (one wave), the top k by (v desc, index asc) and its
+//              gates.  The decision is certain when fl32(v - rho) of each
+//              selected expert exceeds fl32(v + rho) of the next one and of
+//              every unselected expert (fp32 rounding is monotone, so the exact
+//              fp32 logits keep that order strictly).  Otherwise every expert
+//              whose interval reaches the lowest selected lower bound is a
+//              candidate and the token is queued.
+//  4. refine:  per queued token, each candidate's logit is recomputed exactly
+//              (binary64 sum of x * (hi + mid + lo), rounded once to fp32) in
+//              place, then the token's top k and gates are taken again.
+//
+// Non-candidates keep their approximate logit, which is strictly below every
+// selected exact logit, so the selection over the patched row equals the one
+// over the exact logits; their gates differ from exact ones by about 1e-7
+// (relative).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 64;  // h per pipeline stage and per fp32 accumulation chain
+
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_bits(w);
+  const float r1 = w - bf16_bits_to_f32(hi);  // exact
+  mid = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mid);  // exact, at most 8 significant bits
+  lo = f32_to_bf16_bits(r2);                    // exact
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Prep: one block per 64 experts x 64 h.  wp[p][e][h] (zero rows past E) and
+// wsq[h / 64][e] = sum over the block's 64 h of w^2 (binary64, fixed order).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) router_split_prep_kernel(const float* __restrict__ Wg, int H, int E, int Ep,
+                                                                uint16_t* __restrict__ wp, double* __restrict__ wsq,
+                                                                int* __restrict__ count) {
+  __shared__ float tile[64][65];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * 64;
+  const int h0 = blockIdx.y * kChunk;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 2) count[tid] = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = (tid >> 6) + 4 * j;
+    const int e = e0 + (tid & 63);
+    tile[r][tid & 63] = e < E ? Wg[(size_t)(h0 + r) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  const int el = tid >> 2, hq = tid & 3;  // expert e0 + el, h sub-range 16*hq
+  const int e = e0 + el;
+  double sq = 0.0;
+  uint32_t pk[3][8];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    uint32_t h0b, m0, l0, h1b, m1, l1;
+    const float a = tile[16 * hq + j][el], b = tile[16 * hq + j + 1][el];
+    sq = __builtin_fma((double)a, (double)a, sq);
+    sq = __builtin_fma((double)b, (double)b, sq);
+    split3(a, h0b, m0, l0);
+    split3(b, h1b, m1, l1);
+    pk[0][j / 2] = h0b | (h1b << 16);
+    pk[1][j / 2] = m0 | (m1 << 16);
+    pk[2][j / 2] = l0 | (l1 << 16);
+  }
+  if (e < Ep) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      uint16_t* dst = wp + ((size_t)p * Ep + e) * H + h0 + 16 * hq;
+      *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
+      *reinterpret_cast<u32x4_t*>(dst + 8) = u32x4_t{pk[p][4], pk[p][5], pk[p][6], pk[p][7]};
+    }
+  }
+  sq += __shfl_xor(sq, 1, 64);
+  sq += __shfl_xor(sq, 2, 64);
+  if (hq == 0 && e < Ep) wsq[(size_t)blockIdx.y * Ep + e] = sq;
+}
+
+// ---------------------------------------------------------------------------
+// Approximate logits: v_mfma_f32_16x16x32_bf16 on x (bf16, exact) times the
+// weight pieces.  8 waves as TG token groups x EG expert groups x KS h slices;
+// a wave owns 16*MF tokens x 16*WN experts of its slice.  A stage holds, per
+// slice, BM x-rows and 3*BN piece rows of 64 h (128 B per row, chunk c of row r
+// at slot c ^ ((r >> 1) & 7), so the 16 rows a 16-lane LDS read phase touches
+// hit distinct banks), filled by direct-to-LDS loads; S stages in a ring.
+// After every stage both fp32 chains are added into binary64 accumulators and
+// cleared.  Slices are combined through LDS in slice order.  Also writes
+// sum_h x^2 per token (fp32), and the blocks of the first token tile write the
+// norms ||w_e|| of their experts.
+// ---------------------------------------------------------------------------
+template <int TG, int EG, int KS, int MF, int WN, int S>
+__global__ void __launch_bounds__(512) router_split_logits_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wp,
+                                                                  const float* __restrict__ bias,
+                                                                  const double* __restrict__ wsq,
+                                                                  float* __restrict__ logits,
+                                                                  float* __restrict__ xsq, double* __restrict__ wn,
+                                                                  int T, int H, int E, int Ep) {
+  static_assert(TG * EG * KS == 8, "8 waves");
+  constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
+  constexpr int SR = BM + 3 * BN;  // rows per slice per stage
+  constexpr int ROWS = KS * SR;
+  constexpr int NI = ROWS / 8;  // 64-lane load instructions per stage (8 rows each)
+  constexpr int L = (NI + 7) / 8;
+  constexpr int STAGE = ROWS * kChunk;  // bf16 elements
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tg = w % TG, eg = (w / TG) % EG, ks = w / (TG * EG);
+  const int t0 = blockIdx.x * BM, e0 = blockIdx.y * BN;
+  const int nk = H / kChunk;
+  const int nks = nk / KS;  // stages (chunks per slice)
+
+  auto lds_pos = [](int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; };
+
+  auto issue = [&](int buf, int j) {
+    uint16_t* st = smem + buf * STAGE;
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+      int g = q * 8 + w;
+      if (g >= NI) g = NI - 1;  // waves without a group of their own repeat the last one
+      const int p = g * 64 + lane;
+      const int r = p >> 3;
+      const int c = (p & 7) ^ ((r >> 1) & 7);
+      const int sl = r / SR, rr = r % SR;
+      const int h = (sl * nks + j) * kChunk + c * 8;
+      const uint16_t* src;
+      if (rr < BM) {
+        const int t = t0 + rr < T ? t0 + rr : T - 1;
+        src = x + (size_t)t * H + h;
+      } else {
+        const int q2 = rr - BM;
+        src = wp + ((size_t)(q2 / BN) * Ep + e0 + q2 % BN) * H + h;
+      }
+      __builtin_amdgcn_global_load_lds(src, st + g * 512, 16, 0, 0);
+    }
+  };
+
+  f32x4_t acc_hi[MF][WN], acc_ml[MF][WN];
+  double acc64[MF][WN][4];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      acc_hi[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc_ml[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc64[i][n][j] = 0.0;
+    }
+  float sq[MF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i) sq[i] = 0.0f;
+
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (issued < nks) issue(issued % S, issued), ++issued;
+
+  const int rbase = ks * SR;
+  for (int j = 0; j < nks; ++j) {
+    wait_stages<L>(issued - j - 1);
+    lds_barrier();
+    if (issued < nks) issue(issued % S, issued), ++issued;
+    const uint16_t* st = smem + (j % S) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 4);
+      bf16x8_t a[MF];
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(rbase + (tg * MF + i) * 16 + (lane & 15), c));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+              st + lds_pos(rbase + BM + p * BN + (eg * WN + n) * 16 + (lane & 15), c));
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+            if (p == 0) acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_hi[i][n], 0, 0, 0);
+            else acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_ml[i][n], 0, 0, 0);
+          }
+        }
+      if (eg == 0) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          const u32x4_t u = __builtin_bit_cast(u32x4_t, a[i]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float lo = __uint_as_float(u[q] << 16), hi = __uint_as_float(u[q] & 0xFFFF0000u);
+            sq[i] = __builtin_fmaf(lo, lo, sq[i]);
+            sq[i] = __builtin_fmaf(hi, hi, sq[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          acc64[i][n][jj] += (double)acc_hi[i][n][jj];
+          acc64[i][n][jj] += (double)acc_ml[i][n][jj];
+        }
+        acc_hi[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc_ml[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+
+  // row sums of x^2: lanes l, l^16, l^32, l^48 hold the four k groups of row l%16
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    sq[i] += __shfl_xor(sq[i], 16, 64);
+    sq[i] += __shfl_xor(sq[i], 32, 64);
+  }
+
+  // slices > 0 hand their partial sums to slice 0 through LDS
+  if (KS > 1) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    double* red = reinterpret_cast<double*>(smem);
+    float* rsq = reinterpret_cast<float*>(red + (size_t)(KS - 1) * TG * EG * MF * WN * 4 * 64);
+    const int wi = tg + TG * eg;
+    if (ks > 0) {
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int n = 0; n < WN; ++n)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            red[((((size_t)(ks - 1) * TG * EG + wi) * MF + i) * WN * 4 + n * 4 + jj) * 64 + lane] = acc64[i][n][jj];
+      if (eg == 0)
+#pragma unroll
+        for (int i = 0; i < MF; ++i) rsq[(((ks - 1) * TG + tg) * MF + i) * 64 + lane] = sq[i];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int k2 = 1; k2 < KS; ++k2) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int n = 0; n < WN; ++n)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              acc64[i][n][jj] +=
+                  red[((((size_t)(k2 - 1) * TG * EG + wi) * MF + i) * WN * 4 + n * 4 + jj) * 64 + lane];
+        if (eg == 0)
+#pragma unroll
+          for (int i = 0; i < MF; ++i) sq[i] += rsq[(((k2 - 1) * TG + tg) * MF + i) * 64 + lane];
+      }
+    }
+  }
+
+  if (blockIdx.x == 0 && tid < BN && e0 + tid < E) {
+    double s = 0.0;
+    for (int hb = 0; hb < nk; ++hb) s += wsq[(size_t)hb * Ep + e0 + tid];
+    wn[e0 + tid] = sqrt(s * (1.0 + 0x1p-40));
+  }
+  if (ks != 0) return;
+
+  // accumulator lane l: tokens 4*(l/16) + jj, expert l%16 of the fragment
+#pragma unroll
+  for (int n = 0; n < WN; ++n) {
+    const int e = e0 + (eg * WN + n) * 16 + (lane & 15);
+    if (e >= E) continue;
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = t0 + (tg * MF + i) * 16 + 4 * (lane >> 4) + jj;
+        if (t < T) logits[(size_t)t * E + e] = (float)(acc64[i][n][jj] + b);
+      }
+  }
+  if (eg == 0 && lane < 16) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int t = t0 + (tg * MF + i) * 16 + lane;
+      if (t < T) xsq[t] = sq[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top k of one token's logit row with one wave (lane l holds experts l + 64j):
+// k rounds of a wave-wide maximum of (value desc, index asc).  All lanes end
+// with the chosen experts, their values and (if kIv) the interval bounds
+// carried along; `taken` marks the chosen entries in their owner lanes.
+// ---------------------------------------------------------------------------
+template <int JE, int KMAX, bool kIv>
+__device__ __forceinline__ void wave_topk(const float (&v)[JE], const float (&lo)[JE], const float (&hi)[JE],
+                                          bool (&taken)[JE], int k, int (&se)[KMAX], float (&sv)[KMAX],
+                                          float (&slo)[KMAX], float (&shi)[KMAX]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r >= k) break;
+    float bv = -__builtin_inff(), blo = 0.f, bhi = 0.f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (!taken[j] && (v[j] > bv || (v[j] == bv && lane + 64 * j < be))) {
+        bv = v[j];
+        be = lane + 64 * j;
+        if (kIv) {
+          blo = lo[j];
+          bhi = hi[j];
+        }
+      }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 64);
+      const int oe = __shfl_xor(be, d, 64);
+      float olo = 0.f, ohi = 0.f;
+      if (kIv) {
+        olo = __shfl_xor(blo, d, 64);
+        ohi = __shfl_xor(bhi, d, 64);
+      }
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+        if (kIv) {
+          blo = olo;
+          bhi = ohi;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (lane + 64 * j == be) taken[j] = true;
+    se[r] = be;
+    sv[r] = bv;
+    slo[r] = blo;
+    shi[r] = bhi;
+  }
+}
+
+// Gates of the chosen experts (gate_mode 0: softmax over all E; otherwise the
+// softmax over the k chosen), written by lanes 0..k-1.
+template <int JE, int KMAX>
+__device__ __forceinline__ void wave_gates(const float (&v)[JE], int E, int k, int gate_mode, const int (&se)[KMAX],
+                                           const float (&sv)[KMAX], int t, int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_gate) {
+  const int lane = threadIdx.x & 63;
+  const float m = sv[0];
+  float den = 0.0f;
+  if (gate_mode == 0) {
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (lane + 64 * j < E) den += expf(v[j] - m);
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
+  } else {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+      if (r < k) den += expf(sv[r] - m);
+  }
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r)
+    if (r < k && lane == r) {
+      topk_idx[(size_t)t * k + r] = se[r];
+      topk_gate[(size_t)t * k + r] = expf(sv[r] - m) / den;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Certify + select: one wave per token.  Writes the token's choices and gates
+// from the approximate logits; when the radius leaves the decision open, also
+// queues the token (utok: token, first pair, pair count) and its candidates.
+// ---------------------------------------------------------------------------
+template <int JE, int KMAX>
+__global__ void __launch_bounds__(256) router_certify_kernel(const float* __restrict__ logits,
+                                                             const float* __restrict__ xsq,
+                                                             const double* __restrict__ wn,
+                                                             const float* __restrict__ bias, int T, int H, int E,
+                                                             int k, int gate_mode, double c1,
+                                                             int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_gate, int2* __restrict__ pairs,
+                                                             int4* __restrict__ utok, int* __restrict__ count) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  const double xn = sqrt((double)xsq[t] * (1.0 + (double)H * 0x1p-22 + 0x1p-20));  // bound on ||x||
+  const double c2 = 0x1p-24 + 0x1p-44;
+  const double c3 = (double)H * 0x1p-52;
+  float v[JE], lo[JE], hi[JE];
+  bool taken[JE];
+  bool bad = !(xn <= 1e300);
+#pragma unroll
+  for (int j = 0; j < JE; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      v[j] = row[e];
+      const double vd = v[j];
+      const double bd = bias ? (double)bias[e] : 0.0;
+      const double rho = c1 * xn * wn[e] + c2 * fabs(vd) + c3 * fabs(bd) + 1e-30;
+      lo[j] = (float)(vd - rho);
+      hi[j] = (float)(vd + rho);
+      bad |= !(fabsf(v[j]) <= 3.0e38f) || !(rho <= 1e300);
+      taken[j] = false;
+    } else {
+      v[j] = lo[j] = hi[j] = -__builtin_inff();
+      taken[j] = true;
+    }
+  }
+  int se[KMAX];
+  float sv[KMAX], slo[KMAX], shi[KMAX];
+  wave_topk<JE, KMAX, true>(v, lo, hi, taken, k, se, sv, slo, shi);
+  wave_gates<JE, KMAX>(v, E, k, gate_mode, se, sv, t, topk_idx, topk_gate);
+
+  float tau = slo[0];
+  bool ordered = true;
+#pragma unroll
+  for (int r = 1; r < KMAX; ++r)
+    if (r < k) {
+      ordered &= slo[r - 1] > shi[r];
+      tau = fminf(tau, slo[r]);
+    }
+  float rest = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < JE; ++j)
+    if (!taken[j]) rest = fmaxf(rest, hi[j]);
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) rest = fmaxf(rest, __shfl_xor(rest, d, 64));
+  bad = __ballot(bad) != 0;
+  if (!bad && ordered && tau > rest) return;  // decision certified
+
+  int mine = 0;
+  bool cand[JE];
+#pragma unroll
+  for (int j = 0; j < JE; ++j) {
+    cand[j] = lane + 64 * j < E && (bad || taken[j] || hi[j] >= tau);
+    mine += cand[j];
+  }
+  const int incl = wave_inclusive_scan(mine);
+  const int total = __shfl(incl, 63, 64);
+  int base = 0, slot = 0;
+  if (lane == 0) {
+    base = atomicAdd(&count[0], total);
+    slot = atomicAdd(&count[1], 1);
+    utok[slot] = int4{t, base, total, 0};
+  }
+  base = __shfl(base, 0, 64);
+  int pos = base + incl - mine;
+#pragma unroll
+  for (int j = 0; j < JE; ++j)
+    if (cand[j]) pairs[pos++] = int2{t, lane + 64 * j};
+}
+
+// ---------------------------------------------------------------------------
+// Refine: one block (4 waves) per queued token.  Each wave recomputes whole
+// candidates: binary64 sum of x[t][h] * (hi+mid+lo), lane-strided over h in
+// 8-element groups, a fixed butterfly across the wave, plus the bias, rounded
+// once to fp32.  Then wave 0 takes the token's top k and gates again.
+// ---------------------------------------------------------------------------
+template <int JE, int KMAX>
+__global__ void __launch_bounds__(256) router_refine_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wp,
+                                                            const float* __restrict__ bias,
+                                                            const int2* __restrict__ pairs,
+                                                            const int4* __restrict__ utok,
+                                                            const int* __restrict__ count, float* __restrict__ logits,
+                                                            int H, int E, int Ep, int k, int gate_mode,
+                                                            int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_gate) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ntok = count[1];
+  for (int u = blockIdx.x; u < ntok; u += gridDim.x) {
+    const int4 rec = utok[u];
+    const int t = rec.x;
+    const uint16_t* xr = x + (size_t)t * H;
+    for (int c = w; c < rec.z; c += 4) {
+      const int e = pairs[rec.y + c].y;
+      const uint16_t* w0 = wp + (size_t)e * H;
+      const uint16_t* w1 = wp + ((size_t)Ep + e) * H;
+      const uint16_t* w2 = wp + ((size_t)2 * Ep + e) * H;
+      double s = 0.0;
+      for (int h = 8 * lane; h < H; h += 512) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + h);
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(w0 + h);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(w1 + h);
+        const u32x4_t cc = *reinterpret_cast<const u32x4_t*>(w2 + h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int sh = half ? 0 : 16;
+            const uint32_t m = half ? 0xFFFF0000u : 0xFFFFFFFFu;
+            const double xd = (double)__uint_as_float((xv[q] << sh) & m);
+            const double wd = (double)__uint_as_float((a[q] << sh) & m) +
+                              (double)__uint_as_float((b[q] << sh) & m) +
+                              (double)__uint_as_float((cc[q] << sh) & m);
+            s = __builtin_fma(xd, wd, s);
+          }
+        }
+      }
+#pragma unroll
+      for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+      if (lane == 0) logits[(size_t)t * E + e] = (float)(s + (bias ? (double)bias[e] : 0.0));
+    }
+    __syncthreads();
+    if (w == 0) {
+      const float* row = logits + (size_t)t * E;
+      float v[JE], dummy[JE];
+      bool taken[JE];
+#pragma unroll
+      for (int j = 0; j < JE; ++j) {
+        const int e = lane + 64 * j;
+        v[j] = e < E ? row[e] : -__builtin_inff();
+        dummy[j] = 0.f;
+        taken[j] = e >= E;
+      }
+      int se[KMAX];
+      float sv[KMAX], s1[KMAX], s2[KMAX];
+      wave_topk<JE, KMAX, false>(v, dummy, dummy, taken, k, se, sv, s1, s2);
+      wave_gates<JE, KMAX>(v, E, k, gate_mode, se, sv, t, topk_idx, topk_gate);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+int split_router_bn(int E) { return E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : 128; }
+
+int split_router_ep(int E) {
+  const int bn = split_router_bn(E);
+  return (E + bn - 1) / bn * bn;
+}
+
+int split_router_hs(int H) { return H / kChunk; }
+
+template <int TG, int EG, int KS, int MF, int WN, int S>
+static hipError_t launch_split_logits(const uint16_t* x, const uint16_t* wp, const float* bias, const double* wsq,
+                                      float* logits, float* xsq, double* wn, int T, int H, int E, int Ep,
+                                      hipStream_t st) {
+  constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
+  constexpr int ROWS = KS * (BM + 3 * BN);
+  size_t shm = sizeof(uint16_t) * (size_t)S * ROWS * kChunk;
+  const size_t red = (KS > 1) ? (sizeof(double) * (size_t)(KS - 1) * TG * EG * MF * WN * 4 * 64 +
+                                 sizeof(float) * (size_t)(KS - 1) * TG * MF * 64)
+                              : 0;
+  if (red > shm) shm = red;
+  hipError_t err = hipFuncSetAttribute((const void*)router_split_logits_kernel<TG, EG, KS, MF, WN, S>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (err != hipSuccess) return err;
+  dim3 grid((T + BM - 1) / BM, Ep / BN);
+  router_split_logits_kernel<TG, EG, KS, MF, WN, S><<<grid, dim3(512), shm, st>>>(x, wp, bias, wsq, logits, xsq, wn,
+                                                                                  T, H, E, Ep);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
+                               int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
+                               hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int Ep = split_router_ep(E), nk = H / kChunk;
+  uint16_t* wp = static_cast<uint16_t*>(sc.wp);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  router_split_prep_kernel<<<dim3((Ep + 63) / 64, nk), dim3(256), 0, st>>>(Wg, H, E, Ep, wp, sc.wsq, sc.count);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+#define MOE_SL(TG, EG, KS, MF, WN, S) \
+  launch_split_logits<TG, EG, KS, MF, WN, S>(xb, wp, bias, sc.wsq, logits, sc.xsq, sc.wn, T, H, E, Ep, st)
+  if (E <= 16) {
+    // 16 experts per wave; split h across waves when there are few tokens
+    if ((int64_t)T >= 128 * 256 || nk % 2) err = MOE_SL(8, 1, 1, 1, 1, 4);
+    else if ((int64_t)T >= 64 * 256 || nk % 4) err = MOE_SL(4, 1, 2, 1, 1, 3);
+    else err = MOE_SL(2, 1, 4, 1, 1, 3);
+  } else if (E <= 32) {
+    err = MOE_SL(8, 1, 1, 1, 2, 4);
+  } else if (E <= 64) {
+    err = MOE_SL(4, 2, 1, 1, 2, 4);
+  } else {
+    err = MOE_SL(2, 4, 1, 2, 2, 2);
+  }
+#undef MOE_SL
+  if (err != hipSuccess) return err;
+
+  // hi chain: 64 products (+ the running sum), |hi| <= (1 + 2^-7)|w|; mid/lo
+  // chain: 128 products, |mid| + |lo| <= 2^-7 |w|; 2^-23 per addition, 1%
+  // slack; binary64 sums (here and in the exact definition) add at most
+  // 4 H 2^-53 relative to sum|x*w|.
+  const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
+  const int je = (E + 63) / 64;
+  const dim3 cgrid((T + 3) / 4), rgrid(T < 1024 ? T : 1024);
+#define MOE_CR(J, K)                                                                                             \
+  do {                                                                                                           \
+    router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(logits, sc.xsq, sc.wn, bias, T, H, E, k, gate_mode, \
+                                                             c1, topk_idx, topk_gate, sc.pairs, sc.utok,        \
+                                                             sc.count);                                          \
+    if ((err = hipGetLastError()) != hipSuccess) return err;                                                     \
+    router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,  \
+                                                            H, E, Ep, k, gate_mode, topk_idx, topk_gate);        \
+  } while (0)
+#define MOE_CR_K(J)            \
+  if (k <= 1) MOE_CR(J, 1);    \
+  else if (k <= 2) MOE_CR(J, 2); \
+  else if (k <= 4) MOE_CR(J, 4); \
+  else if (k <= 8) MOE_CR(J, 8); \
+  else MOE_CR(J, 16)
+  if (je <= 1) { MOE_CR_K(1); }
+  else if (je <= 2) { MOE_CR_K(2); }
+  else if (je <= 4) { MOE_CR_K(4); }
+  else if (je <= 8) { MOE_CR_K(8); }
+  else { MOE_CR_K(16); }
+#undef MOE_CR_K
+#undef MOE_CR
+  return hipGetLastError();
+}
+
+}  // namespace moe
