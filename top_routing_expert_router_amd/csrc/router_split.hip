@@ -102,6 +102,192 @@ __global__ void __launch_bounds__(256) router_split_prep_kernel(const float* __r
 }
 
 // ---------------------------------------------------------------------------
+// Selection on one token's logit row by a group of G lanes (G = 16, 32 or 64;
+// lane g of the group holds experts g + G*j): k rounds of a group-wide maximum
+// of (value desc, index asc).  All lanes of the group end with the chosen
+// experts, their values and (if kIv) their interval bounds; `taken` marks the
+// chosen entries in their owner lanes.
+// ---------------------------------------------------------------------------
+template <int G, int JE, int KMAX, bool kIv>
+__device__ __forceinline__ void group_topk(const float (&v)[JE], const float (&lo)[JE], const float (&hi)[JE],
+                                           bool (&taken)[JE], int k, int (&se)[KMAX], float (&sv)[KMAX],
+                                           float (&slo)[KMAX], float (&shi)[KMAX]) {
+  const int lg = threadIdx.x & (G - 1);
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r >= k) break;
+    float bv = -__builtin_inff(), blo = 0.f, bhi = 0.f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (!taken[j] && (v[j] > bv || (v[j] == bv && lg + G * j < be))) {
+        bv = v[j];
+        be = lg + G * j;
+        if (kIv) {
+          blo = lo[j];
+          bhi = hi[j];
+        }
+      }
+#pragma unroll
+    for (int d = G / 2; d > 0; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 64);
+      const int oe = __shfl_xor(be, d, 64);
+      float olo = 0.f, ohi = 0.f;
+      if (kIv) {
+        olo = __shfl_xor(blo, d, 64);
+        ohi = __shfl_xor(bhi, d, 64);
+      }
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+        if (kIv) {
+          blo = olo;
+          bhi = ohi;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (lg + G * j == be) taken[j] = true;
+    se[r] = be;
+    sv[r] = bv;
+    slo[r] = blo;
+    shi[r] = bhi;
+  }
+}
+
+// Gates of the chosen experts (gate_mode 0: softmax over all E; otherwise the
+// softmax over the k chosen); choice r is written by lane r % G of the group.
+template <int G, int JE, int KMAX>
+__device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, int gate_mode, const int (&se)[KMAX],
+                                            const float (&sv)[KMAX], int t, bool active,
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+  const int lg = threadIdx.x & (G - 1);
+  const float m = sv[0];
+  float den = 0.0f;
+  if (gate_mode == 0) {
+#pragma unroll
+    for (int j = 0; j < JE; ++j)
+      if (lg + G * j < E) den += expf(v[j] - m);
+#pragma unroll
+    for (int d = G / 2; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
+  } else {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+      if (r < k) den += expf(sv[r] - m);
+  }
+  if (!active) return;
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r)
+    if (r < k && (r & (G - 1)) == lg) {  // every choice r < k has a writer, also when G < k
+      topk_idx[(size_t)t * k + r] = se[r];
+      topk_gate[(size_t)t * k + r] = expf(sv[r] - m) / den;
+    }
+}
+
+// Choices, gates and certification of one token held by a group of G lanes
+// (v: approximate logits; wne: ||w_e|| rounded up; be: bias; xn: bound on
+// ||x||; all radius arithmetic in fp32 rounded up by a 2^-20 margin).  An
+// undecided token is queued with the experts whose exact logit is needed: the
+// chosen ones whose interval meets another chosen one's or an unchosen one's,
+// and the unchosen ones whose interval reaches the lowest chosen lower bound.
+// Every other expert's interval is disjoint from all intervals that matter, so
+// its approximate logit sorts where its exact one would.
+template <int G, int JE, int KMAX>
+__device__ __forceinline__ void certify_token(const float (&v)[JE], const float (&wne)[JE], const float (&be)[JE],
+                                              int E, int H, int k, int gate_mode, float c1, bool active, int t,
+                                              float xn, int32_t* __restrict__ topk_idx,
+                                              float* __restrict__ topk_gate, int2* __restrict__ pairs,
+                                              int4* __restrict__ utok, int* __restrict__ count) {
+  const int lane = threadIdx.x & 63, lg = lane & (G - 1);
+  constexpr float up = 1.0f + 0x1p-20f;
+  const float c2 = 0x1p-24f + 0x1p-44f;
+  const float c3 = (float)H * 0x1p-52f;
+  float lo[JE], hi[JE];
+  bool taken[JE];
+  bool bad = !(xn <= 1e30f);
+#pragma unroll
+  for (int j = 0; j < JE; ++j) {
+    if (lg + G * j < E) {
+      const float rho = (c1 * xn * wne[j] + c2 * fabsf(v[j]) + c3 * fabsf(be[j])) * up + 1e-30f;
+      lo[j] = v[j] - rho;
+      hi[j] = v[j] + rho;
+      bad |= !(fabsf(v[j]) <= 3.0e38f) || !(rho <= 1e30f);
+      taken[j] = false;
+    } else {
+      lo[j] = hi[j] = -__builtin_inff();
+      taken[j] = true;
+    }
+  }
+  int se[KMAX];
+  float sv[KMAX], slo[KMAX], shi[KMAX];
+  group_topk<G, JE, KMAX, true>(v, lo, hi, taken, k, se, sv, slo, shi);
+  group_gates<G, JE, KMAX>(v, E, k, gate_mode, se, sv, t, active, topk_idx, topk_gate);
+
+  float tau = slo[0];
+  bool ordered = true;
+#pragma unroll
+  for (int r = 1; r < KMAX; ++r)
+    if (r < k) {
+      ordered &= slo[r - 1] > shi[r];
+      tau = fminf(tau, slo[r]);
+    }
+  float rest = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < JE; ++j)
+    if (!taken[j] && lg + G * j < E) rest = fmaxf(rest, hi[j]);
+#pragma unroll
+  for (int d = G / 2; d > 0; d >>= 1) rest = fmaxf(rest, __shfl_xor(rest, d, 64));
+  const uint64_t gmask = (G == 64 ? ~0ull : ((1ull << (G & 63)) - 1)) << (lane & ~(G - 1));
+  bad = (__ballot(bad) & gmask) != 0;
+  const bool queue = active && (bad || !ordered || !(tau > rest));
+
+  bool cand[JE];
+  uint64_t bj[JE];
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < JE; ++j) {
+    const int e = lg + G * j;
+    bool need = false;
+    if (queue && e < E) {
+      if (bad) {
+        need = true;
+      } else if (taken[j]) {
+        need = lo[j] <= rest;
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r)
+          if (r < k && se[r] != e && slo[r] <= hi[j] && shi[r] >= lo[j]) need = true;
+      } else {
+        need = hi[j] >= tau;
+      }
+    }
+    cand[j] = need;
+    bj[j] = __ballot(need) & gmask;
+    total += __popcll(bj[j]);
+  }
+  int base = 0;
+  if (queue && lg == 0) {
+    base = atomicAdd(&count[0], total);
+    const int slot = atomicAdd(&count[1], 1);
+    utok[slot] = int4{t, base, total, 0};
+  }
+  base = __shfl(base, lane & ~(G - 1), 64);
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int off = 0;
+#pragma unroll
+  for (int j = 0; j < JE; ++j) {
+    if (cand[j]) pairs[base + off + __popcll(bj[j] & lt)] = int2{t, lg + G * j};
+    off += __popcll(bj[j]);
+  }
+}
+
+// Bound on ||x|| from the fp32 sum of squares (each of the <= H additions errs
+// by at most 2^-24 relative) and on the rounding of the square root.
+__device__ __forceinline__ float xnorm_bound(float sq, int H) {
+  return sqrtf(sq * (1.0f + (float)H * 0x1p-22f + 0x1p-20f)) * (1.0f + 0x1p-20f);
+}
+
+// ---------------------------------------------------------------------------
 // Approximate logits: v_mfma_f32_16x16x32_bf16 on x (bf16, exact) times the
 // weight pieces.  8 waves as TG token groups x EG expert groups x KS h slices;
 // a wave owns 16*MF tokens x 16*WN experts of its slice.  A stage holds, per
@@ -113,14 +299,12 @@ __global__ void __launch_bounds__(256) router_split_prep_kernel(const float* __r
 // sum_h x^2 per token (fp32), and the blocks of the first token tile write the
 // norms ||w_e|| of their experts.
 // ---------------------------------------------------------------------------
-template <int TG, int EG, int KS, int MF, int WN, int S>
-__global__ void __launch_bounds__(512) router_split_logits_kernel(const uint16_t* __restrict__ x,
-                                                                  const uint16_t* __restrict__ wp,
-                                                                  const float* __restrict__ bias,
-                                                                  const double* __restrict__ wsq,
-                                                                  float* __restrict__ logits,
-                                                                  float* __restrict__ xsq, double* __restrict__ wn,
-                                                                  int T, int H, int E, int Ep) {
+template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX>
+__global__ void __launch_bounds__(512) router_split_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wp, const float* __restrict__ bias,
+    const double* __restrict__ wsq, float* __restrict__ logits, float* __restrict__ xsq, double* __restrict__ wn,
+    int T, int H, int E, int Ep, int k, int gate_mode, double c1, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, int2* __restrict__ pairs, int4* __restrict__ utok, int* __restrict__ count) {
   static_assert(TG * EG * KS == 8, "8 waves");
   constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
   constexpr int SR = BM + 3 * BN;  // rows per slice per stage
@@ -277,122 +461,88 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(const uint16_t
     }
   }
 
-  if (blockIdx.x == 0 && tid < BN && e0 + tid < E) {
-    double s = 0.0;
-    for (int hb = 0; hb < nk; ++hb) s += wsq[(size_t)hb * Ep + e0 + tid];
-    wn[e0 + tid] = sqrt(s * (1.0 + 0x1p-40));
+  if (!FUSE) {
+    if (blockIdx.x == 0 && tid < BN && e0 + tid < E) {
+      double s = 0.0;
+      for (int hb = 0; hb < nk; ++hb) s += wsq[(size_t)hb * Ep + e0 + tid];
+      wn[e0 + tid] = sqrt(s * (1.0 + 0x1p-40));
+    }
+    if (ks != 0) return;
   }
-  if (ks != 0) return;
 
   // accumulator lane l: tokens 4*(l/16) + jj, expert l%16 of the fragment
-#pragma unroll
-  for (int n = 0; n < WN; ++n) {
-    const int e = e0 + (eg * WN + n) * 16 + (lane & 15);
-    if (e >= E) continue;
-    const double b = bias ? (double)bias[e] : 0.0;
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int t = t0 + (tg * MF + i) * 16 + 4 * (lane >> 4) + jj;
-        if (t < T) logits[(size_t)t * E + e] = (float)(acc64[i][n][jj] + b);
-      }
+  constexpr int SV = BN + 1;  // row stride of the staged logits
+  float* s_v = reinterpret_cast<float*>(smem);
+  float* s_x = s_v + BM * SV;
+  if (FUSE) {
+    if (KS == 1) wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the stage buffers (and slice partials)
   }
-  if (eg == 0 && lane < 16) {
+  if (ks == 0) {
 #pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int t = t0 + (tg * MF + i) * 16 + lane;
-      if (t < T) xsq[t] = sq[i];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Top k of one token's logit row with one wave (lane l holds experts l + 64j):
-// k rounds of a wave-wide maximum of (value desc, index asc).  All lanes end
-// with the chosen experts, their values and (if kIv) the interval bounds
-// carried along; `taken` marks the chosen entries in their owner lanes.
-// ---------------------------------------------------------------------------
-template <int JE, int KMAX, bool kIv>
-__device__ __forceinline__ void wave_topk(const float (&v)[JE], const float (&lo)[JE], const float (&hi)[JE],
-                                          bool (&taken)[JE], int k, int (&se)[KMAX], float (&sv)[KMAX],
-                                          float (&slo)[KMAX], float (&shi)[KMAX]) {
-  const int lane = threadIdx.x & 63;
+    for (int n = 0; n < WN; ++n) {
+      const int el = (eg * WN + n) * 16 + (lane & 15);
+      const int e = e0 + el;
+      if (e >= E) continue;
+      const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    if (r >= k) break;
-    float bv = -__builtin_inff(), blo = 0.f, bhi = 0.f;
-    int be = 0x7fffffff;
+      for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int j = 0; j < JE; ++j)
-      if (!taken[j] && (v[j] > bv || (v[j] == bv && lane + 64 * j < be))) {
-        bv = v[j];
-        be = lane + 64 * j;
-        if (kIv) {
-          blo = lo[j];
-          bhi = hi[j];
+        for (int jj = 0; jj < 4; ++jj) {
+          const int tl = (tg * MF + i) * 16 + 4 * (lane >> 4) + jj;
+          const float v = (float)(acc64[i][n][jj] + b);
+          if (t0 + tl < T) logits[(size_t)(t0 + tl) * E + e] = v;
+          if (FUSE) s_v[tl * SV + el] = v;
         }
-      }
+    }
+    if (eg == 0 && lane < 16) {
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, 64);
-      const int oe = __shfl_xor(be, d, 64);
-      float olo = 0.f, ohi = 0.f;
-      if (kIv) {
-        olo = __shfl_xor(blo, d, 64);
-        ohi = __shfl_xor(bhi, d, 64);
-      }
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-        if (kIv) {
-          blo = olo;
-          bhi = ohi;
-        }
+      for (int i = 0; i < MF; ++i) {
+        const int tl = (tg * MF + i) * 16 + lane;
+        if (!FUSE && t0 + tl < T) xsq[t0 + tl] = sq[i];
+        if (FUSE) s_x[tl] = sq[i];
       }
     }
-#pragma unroll
-    for (int j = 0; j < JE; ++j)
-      if (lane + 64 * j == be) taken[j] = true;
-    se[r] = be;
-    sv[r] = bv;
-    slo[r] = blo;
-    shi[r] = bhi;
   }
-}
-
-// Gates of the chosen experts (gate_mode 0: softmax over all E; otherwise the
-// softmax over the k chosen), written by lanes 0..k-1.
-template <int JE, int KMAX>
-__device__ __forceinline__ void wave_gates(const float (&v)[JE], int E, int k, int gate_mode, const int (&se)[KMAX],
-                                           const float (&sv)[KMAX], int t, int32_t* __restrict__ topk_idx,
-                                           float* __restrict__ topk_gate) {
-  const int lane = threadIdx.x & 63;
-  const float m = sv[0];
-  float den = 0.0f;
-  if (gate_mode == 0) {
-#pragma unroll
-    for (int j = 0; j < JE; ++j)
-      if (lane + 64 * j < E) den += expf(v[j] - m);
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
-  } else {
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r)
-      if (r < k) den += expf(sv[r] - m);
-  }
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r)
-    if (r < k && lane == r) {
-      topk_idx[(size_t)t * k + r] = se[r];
-      topk_gate[(size_t)t * k + r] = expf(sv[r] - m) / den;
+  if constexpr (FUSE) {
+    // the workgroup holds all E logits of its BM tokens: choices, gates and
+    // certification here in one pass, G lanes per token, JE experts per lane
+    static_assert(BN <= 64, "all experts in one tile");
+    constexpr int G0 = 512 / BM < BN ? 512 / BM : BN;
+    constexpr int G = G0 >= 64 ? 64 : G0;
+    constexpr int JE = BN / G;
+    const int lg = lane & (G - 1);
+    const int tl = tid / G;  // token of this group
+    __shared__ float s_wn[BN];  // ||w_e||, rounded up
+    if (tid < BN) {
+      double sw = 0.0;
+      if (tid < E)
+        for (int hb = 0; hb < nk; ++hb) sw += wsq[(size_t)hb * Ep + tid];
+      s_wn[tid] = (float)sqrt(sw * (1.0 + 0x1p-40)) * (1.0f + 0x1p-20f);
     }
+    __syncthreads();
+    float wne[JE], be[JE], v[JE];
+#pragma unroll
+    for (int j = 0; j < JE; ++j) {
+      const int e = lg + G * j;
+      wne[j] = e < E ? s_wn[e] : 0.0f;
+      be[j] = (bias && e < E) ? bias[e] : 0.0f;
+    }
+    const int t = t0 + tl;
+    const bool active = tl < BM && t < T;
+#pragma unroll
+    for (int j = 0; j < JE; ++j) {
+      const int e = lg + G * j;
+      v[j] = (active && e < E) ? s_v[tl * SV + e] : -__builtin_inff();
+    }
+    const float xn = active ? xnorm_bound(s_x[tl], H) : 0.0f;
+    certify_token<G, JE, KMAX>(v, wne, be, E, H, k, gate_mode, (float)c1 * (1.0f + 0x1p-20f), active,
+                               active ? t : 0, xn, topk_idx, topk_gate, pairs, utok, count);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Certify + select: one wave per token.  Writes the token's choices and gates
-// from the approximate logits; when the radius leaves the decision open, also
-// queues the token (utok: token, first pair, pair count) and its candidates.
+// Certify + select (experts beyond one workgroup's tile): one wave per token.
 // ---------------------------------------------------------------------------
 template <int JE, int KMAX>
 __global__ void __launch_bounds__(256) router_certify_kernel(const float* __restrict__ logits,
@@ -407,71 +557,18 @@ __global__ void __launch_bounds__(256) router_certify_kernel(const float* __rest
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  const double xn = sqrt((double)xsq[t] * (1.0 + (double)H * 0x1p-22 + 0x1p-20));  // bound on ||x||
-  const double c2 = 0x1p-24 + 0x1p-44;
-  const double c3 = (double)H * 0x1p-52;
-  float v[JE], lo[JE], hi[JE];
-  bool taken[JE];
-  bool bad = !(xn <= 1e300);
+  const float xn = xnorm_bound(xsq[t], H);
+  float v[JE], be[JE], wne[JE];
 #pragma unroll
   for (int j = 0; j < JE; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      v[j] = row[e];
-      const double vd = v[j];
-      const double bd = bias ? (double)bias[e] : 0.0;
-      const double rho = c1 * xn * wn[e] + c2 * fabs(vd) + c3 * fabs(bd) + 1e-30;
-      lo[j] = (float)(vd - rho);
-      hi[j] = (float)(vd + rho);
-      bad |= !(fabsf(v[j]) <= 3.0e38f) || !(rho <= 1e300);
-      taken[j] = false;
-    } else {
-      v[j] = lo[j] = hi[j] = -__builtin_inff();
-      taken[j] = true;
-    }
+    v[j] = e < E ? row[e] : -__builtin_inff();
+    wne[j] = e < E ? (float)wn[e] * (1.0f + 0x1p-20f) : 0.0f;
+    be[j] = (bias && e < E) ? bias[e] : 0.0f;
   }
-  int se[KMAX];
-  float sv[KMAX], slo[KMAX], shi[KMAX];
-  wave_topk<JE, KMAX, true>(v, lo, hi, taken, k, se, sv, slo, shi);
-  wave_gates<JE, KMAX>(v, E, k, gate_mode, se, sv, t, topk_idx, topk_gate);
-
-  float tau = slo[0];
-  bool ordered = true;
-#pragma unroll
-  for (int r = 1; r < KMAX; ++r)
-    if (r < k) {
-      ordered &= slo[r - 1] > shi[r];
-      tau = fminf(tau, slo[r]);
-    }
-  float rest = -__builtin_inff();
-#pragma unroll
-  for (int j = 0; j < JE; ++j)
-    if (!taken[j]) rest = fmaxf(rest, hi[j]);
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) rest = fmaxf(rest, __shfl_xor(rest, d, 64));
-  bad = __ballot(bad) != 0;
-  if (!bad && ordered && tau > rest) return;  // decision certified
-
-  int mine = 0;
-  bool cand[JE];
-#pragma unroll
-  for (int j = 0; j < JE; ++j) {
-    cand[j] = lane + 64 * j < E && (bad || taken[j] || hi[j] >= tau);
-    mine += cand[j];
-  }
-  const int incl = wave_inclusive_scan(mine);
-  const int total = __shfl(incl, 63, 64);
-  int base = 0, slot = 0;
-  if (lane == 0) {
-    base = atomicAdd(&count[0], total);
-    slot = atomicAdd(&count[1], 1);
-    utok[slot] = int4{t, base, total, 0};
-  }
-  base = __shfl(base, 0, 64);
-  int pos = base + incl - mine;
-#pragma unroll
-  for (int j = 0; j < JE; ++j)
-    if (cand[j]) pairs[pos++] = int2{t, lane + 64 * j};
+  certify_token<64, JE, KMAX>(v, wne, be, E, H, k, gate_mode, (float)c1 * (1.0f + 0x1p-20f), true, t, xn, topk_idx,
+                              topk_gate, pairs, utok,
+                              count);
 }
 
 // ---------------------------------------------------------------------------
@@ -539,8 +636,8 @@ __global__ void __launch_bounds__(256) router_refine_kernel(const uint16_t* __re
       }
       int se[KMAX];
       float sv[KMAX], s1[KMAX], s2[KMAX];
-      wave_topk<JE, KMAX, false>(v, dummy, dummy, taken, k, se, sv, s1, s2);
-      wave_gates<JE, KMAX>(v, E, k, gate_mode, se, sv, t, topk_idx, topk_gate);
+      group_topk<64, JE, KMAX, false>(v, dummy, dummy, taken, k, se, sv, s1, s2);
+      group_gates<64, JE, KMAX>(v, E, k, gate_mode, se, sv, t, true, topk_idx, topk_gate);
     }
     __syncthreads();
   }
@@ -556,24 +653,47 @@ int split_router_ep(int E) {
 
 int split_router_hs(int H) { return H / kChunk; }
 
-template <int TG, int EG, int KS, int MF, int WN, int S>
-static hipError_t launch_split_logits(const uint16_t* x, const uint16_t* wp, const float* bias, const double* wsq,
-                                      float* logits, float* xsq, double* wn, int T, int H, int E, int Ep,
-                                      hipStream_t st) {
+struct SplitArgs {
+  const uint16_t* x;
+  const uint16_t* wp;
+  const float* bias;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_gate;
+  const SplitScratch* sc;
+  int T, H, E, Ep, k, gate_mode;
+  double c1;
+};
+
+template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX>
+static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
   constexpr int ROWS = KS * (BM + 3 * BN);
   size_t shm = sizeof(uint16_t) * (size_t)S * ROWS * kChunk;
   const size_t red = (KS > 1) ? (sizeof(double) * (size_t)(KS - 1) * TG * EG * MF * WN * 4 * 64 +
                                  sizeof(float) * (size_t)(KS - 1) * TG * MF * 64)
                               : 0;
+  const size_t fz = FUSE ? sizeof(float) * (size_t)BM * (BN + 2) : 0;
   if (red > shm) shm = red;
-  hipError_t err = hipFuncSetAttribute((const void*)router_split_logits_kernel<TG, EG, KS, MF, WN, S>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (fz > shm) shm = fz;
+  auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (err != hipSuccess) return err;
-  dim3 grid((T + BM - 1) / BM, Ep / BN);
-  router_split_logits_kernel<TG, EG, KS, MF, WN, S><<<grid, dim3(512), shm, st>>>(x, wp, bias, wsq, logits, xsq, wn,
-                                                                                  T, H, E, Ep);
+  dim3 grid((a.T + BM - 1) / BM, a.Ep / BN);
+  kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
+                                     a.k, a.gate_mode, a.c1, a.topk_idx, a.topk_gate, a.sc->pairs, a.sc->utok,
+                                     a.sc->count);
   return hipGetLastError();
+}
+
+// fused selection: one instantiation per bound on k
+template <int TG, int EG, int KS, int MF, int WN, int S>
+static hipError_t launch_split_fused(const SplitArgs& a, hipStream_t st) {
+  if (a.k <= 1) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 1>(a, st);
+  if (a.k <= 2) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 2>(a, st);
+  if (a.k <= 4) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 4>(a, st);
+  if (a.k <= 8) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 8>(a, st);
+  return launch_split_logits<TG, EG, KS, MF, WN, S, true, 16>(a, st);
 }
 
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
@@ -587,41 +707,44 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-#define MOE_SL(TG, EG, KS, MF, WN, S) \
-  launch_split_logits<TG, EG, KS, MF, WN, S>(xb, wp, bias, sc.wsq, logits, sc.xsq, sc.wn, T, H, E, Ep, st)
-  if (E <= 16) {
-    // 16 experts per wave; split h across waves when there are few tokens
-    if ((int64_t)T >= 128 * 256 || nk % 2) err = MOE_SL(8, 1, 1, 1, 1, 4);
-    else if ((int64_t)T >= 64 * 256 || nk % 4) err = MOE_SL(4, 1, 2, 1, 1, 3);
-    else err = MOE_SL(2, 1, 4, 1, 1, 3);
-  } else if (E <= 32) {
-    err = MOE_SL(8, 1, 1, 1, 2, 4);
-  } else if (E <= 64) {
-    err = MOE_SL(4, 2, 1, 1, 2, 4);
-  } else {
-    err = MOE_SL(2, 4, 1, 2, 2, 2);
-  }
-#undef MOE_SL
-  if (err != hipSuccess) return err;
-
   // hi chain: 64 products (+ the running sum), |hi| <= (1 + 2^-7)|w|; mid/lo
   // chain: 128 products, |mid| + |lo| <= 2^-7 |w|; 2^-23 per addition, 1%
   // slack; binary64 sums (here and in the exact definition) add at most
   // 4 H 2^-53 relative to sum|x*w|.
   const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
+  SplitArgs a{xb, wp, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1};
+
+  if (E <= 16) {
+    // 16 experts per wave; split h across waves when there are few tokens
+    if ((int64_t)T >= 128 * 256 || nk % 2) err = launch_split_fused<8, 1, 1, 1, 1, 4>(a, st);
+    else if ((int64_t)T >= 64 * 256 || nk % 4) err = launch_split_fused<4, 1, 2, 1, 1, 3>(a, st);
+    else err = launch_split_fused<2, 1, 4, 1, 1, 3>(a, st);
+  } else if (E <= 32) {
+    err = launch_split_fused<8, 1, 1, 1, 2, 4>(a, st);
+  } else if (E <= 64) {
+    err = launch_split_fused<2, 4, 1, 2, 1, 4>(a, st);
+  } else {
+    err = (nk % 2) ? launch_split_logits<2, 4, 1, 2, 2, 2, false, 1>(a, st)
+                   : launch_split_logits<2, 2, 2, 2, 2, 2, false, 1>(a, st);
+  }
+  if (err != hipSuccess) return err;
+
   const int je = (E + 63) / 64;
-  const dim3 cgrid((T + 3) / 4), rgrid(T < 1024 ? T : 1024);
-#define MOE_CR(J, K)                                                                                             \
-  do {                                                                                                           \
-    router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(logits, sc.xsq, sc.wn, bias, T, H, E, k, gate_mode, \
-                                                             c1, topk_idx, topk_gate, sc.pairs, sc.utok,        \
-                                                             sc.count);                                          \
-    if ((err = hipGetLastError()) != hipSuccess) return err;                                                     \
-    router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,  \
-                                                            H, E, Ep, k, gate_mode, topk_idx, topk_gate);        \
+  const dim3 cgrid((T + 3) / 4), rgrid(T < 256 ? T : 256);
+  const bool fused = E <= 64;
+#define MOE_CR(J, K)                                                                                               \
+  do {                                                                                                             \
+    if (!fused) {                                                                                                  \
+      router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(logits, sc.xsq, sc.wn, bias, T, H, E, k, gate_mode, \
+                                                               c1, topk_idx, topk_gate, sc.pairs, sc.utok,        \
+                                                               sc.count);                                          \
+      if ((err = hipGetLastError()) != hipSuccess) return err;                                                     \
+    }                                                                                                              \
+    router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,    \
+                                                            H, E, Ep, k, gate_mode, topk_idx, topk_gate);          \
   } while (0)
-#define MOE_CR_K(J)            \
-  if (k <= 1) MOE_CR(J, 1);    \
+#define MOE_CR_K(J)              \
+  if (k <= 1) MOE_CR(J, 1);      \
   else if (k <= 2) MOE_CR(J, 2); \
   else if (k <= 4) MOE_CR(J, 4); \
   else if (k <= 8) MOE_CR(J, 8); \
