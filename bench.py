@@ -299,12 +299,20 @@ def main():
     roof["kernel"] = "expert_ffn (grouped GEMM1 + GEMM2 launches)"
     roof["algorithmic_per_launch"] = {"flops": ffn_flops, "bytes": ffn_bytes}
 
-    route_roof_us = max(route_bytes / (PEAK_HBM_GBS * 1e3), route_flops / (PEAK_F64_TFLOPS * 1e6))
+    split_router = bf16 and H % 64 == 0
+    if split_router:  # three bf16 pieces per router weight on the bf16 matrix cores
+        route_roof_us = max(route_bytes / (PEAK_HBM_GBS * 1e3), 3 * route_flops / (PEAK_BF16_TFLOPS * 1e6))
+        route_note = "split-bf16 router: roofline = max(bytes/HBM, 3 x 2THE / bf16 peak)"
+    else:
+        route_roof_us = max(route_bytes / (PEAK_HBM_GBS * 1e3), route_flops / (PEAK_F64_TFLOPS * 1e6))
+        route_note = "binary64 router: roofline = max(bytes/HBM, 2THE / fp64 peak)"
+    router_desc = ("fp32 logits: split-bf16 MFMA with a certified radius, binary64 recomputation of undecided "
+                   "tokens" if split_router else "fp32 logits (binary64 accumulation)")
     stages_out = {
         "route": {"us": round(stage_us["route"], 2), "GB_s": round(gbs(route_bytes, stage_us["route"]), 1),
                   "hbm_frac": round(gbs(route_bytes, stage_us["route"]) / PEAK_HBM_GBS, 4),
                   "roofline_frac": round(route_roof_us / stage_us["route"], 4),
-                  "note": "fp64-accumulated router: roofline = max(bytes/HBM, 2THE/fp64 peak)"},
+                  "note": route_note},
         "dispatch": {"us": round(stage_us["dispatch"], 2), "GB_s": round(gbs(disp_bytes, stage_us["dispatch"]), 1),
                      "hbm_frac": round(gbs(disp_bytes, stage_us["dispatch"]) / PEAK_HBM_GBS, 4)},
         "expert_ffn": {"us": round(t_ffn, 2), "TFLOP_s": round(ffn_tflops, 1),
@@ -335,7 +343,7 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs, random-init weights)",
         "config": {"workload": workload, "T": T, "H": H, "E": E, "k": k, "F": F,
                    "act": ["relu", "gelu", "swiglu"][run.act],
-                   "capacity": B.capacity(cfg), "R_kept": R, "dropped": T * k - R, "router": "fp32 logits (fp64 accumulation)"},
+                   "capacity": B.capacity(cfg), "R_kept": R, "dropped": T * k - R, "router": router_desc},
         "expert_gemm_tflops": round(ffn_tflops, 1),
         "expert_gemm_mfma_frac": round(ffn_tflops / mfma_peak, 4),
         "route_dispatch_hbm_frac": {"route": stages_out["route"]["hbm_frac"],

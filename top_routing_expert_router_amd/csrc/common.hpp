@@ -121,15 +121,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Waits until at most `after` stages of L loads are outstanding.
+// Waits until at most `after` stages of L loads are outstanding (a count past
+// the counter's range of 63 waits for more, never less).
 template <int L>
 __device__ __forceinline__ void wait_stages(int after) {
+  constexpr int c1 = L < 63 ? L : 63, c2 = 2 * L < 63 ? 2 * L : 63, c3 = 3 * L < 63 ? 3 * L : 63,
+                c4 = 4 * L < 63 ? 4 * L : 63;
   switch (after) {
     case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<L>(); break;
-    case 2: wait_vmcnt<2 * L>(); break;
-    case 3: wait_vmcnt<3 * L>(); break;
-    default: wait_vmcnt<4 * L>(); break;
+    case 1: wait_vmcnt<c1>(); break;
+    case 2: wait_vmcnt<c2>(); break;
+    case 3: wait_vmcnt<c3>(); break;
+    default: wait_vmcnt<c4>(); break;
   }
 }
 

@@ -265,20 +265,23 @@ __global__ void __launch_bounds__(64) grouped_gemm_scalar_kernel(const void* __r
 // token fragment (rows m), so each lane ends with four consecutive output
 // columns of one token row and writes them as one 8-byte store.
 //
-// Workgroup tile: BM token rows x 256 weight rows (= 256 output columns, or
-// for SwiGLU 128 gate + 128 up rows = 128 output columns), 8 waves as 2 x 4
-// (two per SIMD), each wave (BM/2) token rows x 64 weight rows, i.e.
-// (BM/64) x 2 v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.
+// Workgroup tile: BM token rows x WR weight rows (WR output columns, or for
+// SwiGLU WR/2 gate + WR/2 up rows = WR/2 output columns), NW waves as WGM
+// (token direction) x NW/WGM (weight direction); a wave owns MF x NF
+// v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulators.  Shapes in use:
+// 256 x 256 (2 x 4 waves), 256 x 192 (4 x 2 waves, for N where it fills the
+// CUs in whole waves of tiles) and 128 x 256 (2 x 4 waves, small experts).
 //
 // Data movement: global_load_lds_dwordx4 moves 16-byte chunks straight into
-// LDS (no VGPR staging).  A stage holds BM + 256 rows of 32 k (64 B per row);
-// chunk c of row r sits at slot c ^ ((r >> 2) & 3) of its row.  The LDS has 64
-// four-byte banks and serves a 16-byte-per-lane read 16 lanes at a time, so the
-// 16 rows such a phase touches land in 16 distinct 16-byte bank groups.  S
+// LDS (no VGPR staging).  A stage holds BM + WR rows of BK = 64 k (128 B per
+// row); chunk c of row r sits at slot c ^ ((r >> 1) & 7) of its row.  The LDS
+// has 64 four-byte banks and serves a 16-byte-per-lane read 16 lanes at a
+// time, so the 16 rows such a phase touches land in distinct bank groups.  S
 // stages form a ring: the loads of stage j + S - 1 are issued right after the
 // barrier of step j and waited for S - 1 steps later with an explicit vmcnt
 // (vector memory operations complete in issue order; stores issued in between
-// only make a wait stricter).
+// only make a wait stricter).  Within a stage, the fragment reads of k-step
+// kk + 1 are interleaved one by one with the MFMAs of k-step kk.
 //
 // Persistent: at most one workgroup per CU; workgroup b takes every G-th tile
 // of the device-side tile list (expert-major, then n-tile, then m-tile).  The
@@ -289,12 +292,11 @@ struct PipeTile {
   int e, row0, rows, n0;
 };
 
-constexpr int PG_WAVES = 8;
 
-// BM token rows x WR weight rows per tile, BK k per stage, S stages, waves as
-// WGM (token direction) x 8 / WGM (weight direction).
-template <int BM, int WR, int BK, int S, int WGM, int EPI>
-__global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
+// BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
+// as WGM (token direction) x NW / WGM (weight direction).
+template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
                                                                    uint16_t* __restrict__ C,
@@ -306,26 +308,27 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_
   constexpr int CPR = BK / 8;                             // 16-byte chunks per row
   constexpr int RSH = CPR == 8 ? 1 : (CPR == 4 ? 2 : 3);  // rows per 256-byte LDS phase = 1 << RSH
   constexpr int STAGE = ROWS * BK;                        // bf16 elements per stage
-  constexpr int L = ROWS * CPR / (64 * PG_WAVES);         // 16-byte loads per wave per stage
-  constexpr int WGN = PG_WAVES / WGM;
+  constexpr int L = ROWS * CPR / (64 * NW);         // 16-byte loads per wave per stage
+  constexpr int WGN = NW / WGM;
   constexpr int MF = BM / WGM / 32;                       // token fragments per wave
   constexpr int NF = WR / WGN / 32;                       // weight fragments per wave
   constexpr int HF = kGated ? NF / 2 : NF;                // output column fragments per wave
   constexpr int KS = BK / 16;                             // MFMA k-steps per stage
-  static_assert(ROWS * CPR % (64 * PG_WAVES) == 0 && BM % 64 == 0 && (CPR == 4 || CPR == 8 || CPR == 2), "tile");
+  static_assert(ROWS * CPR % (64 * NW) == 0 && BM % 64 == 0 && (CPR == 4 || CPR == 8 || CPR == 2), "tile");
   static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
+  static_assert(MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
   static_assert(S >= 2 && S - 2 <= 4 && (S - 1) * L < 64 && KS % 2 == 0, "stages");
   extern __shared__ __align__(16) uint16_t smem[];
   int* s_ts = reinterpret_cast<int*>(smem + S * STAGE);  // [E+1] first tile of each expert
   int* s_off = s_ts + (E + 1);                             // [E+1] offsets
-  __shared__ int s_scan[PG_WAVES + 1];
+  __shared__ int s_scan[NW + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
   const int ntn = (N + BN - 1) / BN;
 
   {  // tile list: ceil(kept_e / BM) * ntn tiles per expert
-    const int per = (E + 511) / 512;
+    const int per = (E + 64 * NW - 1) / (64 * NW);
     const int e0 = tid * per;
     int cnt = 0;
     for (int j = 0; j < per; ++j) {
@@ -392,7 +395,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_
     const int k0 = kstep * BK;
 #pragma unroll
     for (int q = 0; q < L; ++q) {
-      const int blk = q * PG_WAVES + w;  // 64 lanes = 64 / CPR rows; never straddles the two regions
+      const int blk = q * NW + w;  // 64 lanes = 64 / CPR rows; never straddles the two regions
       const int p = blk * 64 + lane;
       const int r = p / CPR;
       const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
@@ -507,6 +510,16 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_
     for (int kk = 0; kk < KS; ++kk) {
       if (kk + 1 < KS) read_frags(buf, kk + 1, fr[(kk + 1) & 1]);
       mfma(fr[kk & 1]);
+      if (kk + 1 < KS) {
+        // one fragment read of the next k-step between consecutive MFMAs, so
+        // the LDS latency hides behind the matrix pipe instead of a full drain
+#pragma unroll
+        for (int q = 0; q < MF + NF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - (MF + NF), 0);
+      }
     }
     if (j + 1 < total_steps) {
       wait_stages<L>(issued - j - 2);  // stage j + 1 complete
@@ -521,7 +534,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_pipe_kernel(const uint16_
   }
 }
 
-template <int BM, int WR, int BK, int S, int WGM, int EPI>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
@@ -530,10 +543,10 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   if (tiles <= 0) return hipSuccess;
   const int grid = (int)(tiles < cus ? tiles : cus);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI>,
+  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (err != hipSuccess) return err;
-  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI><<<dim3(grid), dim3(64 * PG_WAVES), shm, st>>>(
+  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
       static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max);
   return hipGetLastError();
@@ -575,12 +588,22 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    // 256 x 256 tiles (two 64 KB stages) unless the experts are small or such
-    // tiles would leave CUs idle; else 128 x 256 tiles (three 48 KB stages)
-    constexpr int BN = EPI == EPI_SWIGLU ? 128 : 256;
-    const int64_t tiles256 = (R_max / 256) * ((N + BN - 1) / BN);
-    if (R_max / E > 128 && tiles256 >= 2 * (int64_t)cus)
+    // 256-row tiles (two stages of 256 + WR rows) for experts with more than
+    // 128 rows on average, with 256 or 192 weight rows per tile, whichever
+    // fills the CUs more evenly in whole waves of tiles; else 128 x 256 tiles
+    // (three 48 KB stages).
+    constexpr bool kGated = EPI == EPI_SWIGLU;
+    if (R_max / E > 128) {
+      auto fill = [&](int bn) {
+        const int64_t tiles = (R_max / 256) * ((N + bn - 1) / bn);
+        const int64_t waves = (tiles + cus - 1) / cus;
+        return waves > 0 ? (double)tiles / (double)(waves * cus) : 0.0;
+      };
+      if constexpr (!kGated)
+        if (fill(192) > fill(256) + 0.05)
+          return launch_pipe<256, 192, 64, 2, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
       return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+    }
     return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
   }
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
