@@ -44,6 +44,8 @@ def lib():
         L.oracle_route_from_logits.restype = i64
         L.oracle_route_from_logits.argtypes = [i64, i64, i32, i32, i64, vp] + [vp] * 8
         L.oracle_dispatch.restype = None
+        L.oracle_router_losses.restype = None
+        L.oracle_router_losses.argtypes = [i64, i64, i32, vp, vp, vp, i32, dbl, dbl, vp]
         L.oracle_dispatch.argtypes = [i64, i64, i32, vp, vp, vp]
         L.oracle_expert_rows.restype = None
         L.oracle_expert_rows.argtypes = [i64, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]
@@ -112,6 +114,18 @@ def route_from_logits(lg, k, gate_mode, C):
     plan["R"] = int(R)
     plan["row_token"] = plan["row_token"][:R].copy()
     return plan
+
+
+def router_losses(logits, topk_idx, demand, k, aux_mode=0, aux_coeff=1.0, z_coeff=1.0):
+    """(load-balancing loss, z-loss) of a routing: see oracle_router_losses."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    idx = _c(np.asarray(topk_idx).reshape(T, k), np.int32)
+    dem = _c(demand, np.int32)
+    out = np.zeros(2, np.float64)
+    lib().oracle_router_losses(T, E, k, _p(lg), _p(idx), _p(dem), int(aux_mode), float(aux_coeff),
+                               float(z_coeff), _p(out))
+    return float(out[0]), float(out[1])
 
 
 def route(x, dtype, wg, bias, k, gate_mode, C):

@@ -181,6 +181,53 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
   return offsets[E];
 }
 
+/*
+ * Router training terms ([EP] router section, the auxiliary-loss and z-loss
+ * paragraphs; [SW] "Load balance & capacity"), binary64 from the fp32 logits.
+ *   P_e   = (1/T) sum_t softmax(l_t)_e          mean routing probability
+ *   f_e   = demand_e / (T*k)   (aux_mode 0: every choice counts, k in the
+ *           denominator -- Switch, Megatron-Core, DeepSpeed top-1 / top-k)
+ *         = first_e / T        (aux_mode 1: only each token's first choice,
+ *           no division by k -- DeepSpeed's top-2 path)
+ *   out[0] = aux_coeff * E * sum_e f_e P_e      (uniform routing gives aux_coeff)
+ *   out[1] = z_coeff * (1/T) sum_t logsumexp(l_t)^2
+ * demand is the number of choices per expert before any capacity limit.
+ * T = 0 gives zeros.
+ */
+void oracle_router_losses(int64_t T, int64_t E, int k, const float *logits, const int32_t *topk_idx,
+                          const int32_t *demand, int aux_mode, double aux_coeff, double z_coeff, double *out) {
+  out[0] = out[1] = 0.0;
+  if (T <= 0) return;
+  double *P = (double *)calloc((size_t)E, sizeof(double));
+  double zsum = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const float *l = logits + t * E;
+    double m = l[0];
+    for (int64_t e = 1; e < E; ++e)
+      if (l[e] > m) m = l[e];
+    double den = 0.0;
+    for (int64_t j = 0; j < E; ++j) den += exp((double)l[j] - m);
+    for (int64_t j = 0; j < E; ++j) P[j] += exp((double)l[j] - m) / den;
+    const double lse = m + log(den);
+    zsum += lse * lse;
+  }
+  double dot = 0.0;
+  for (int64_t e = 0; e < E; ++e) {
+    double f;
+    if (aux_mode == 0) {
+      f = (double)demand[e] / ((double)T * (double)k);
+    } else {
+      int64_t first = 0;
+      for (int64_t t = 0; t < T; ++t) first += (topk_idx[t * k] == (int32_t)e);
+      f = (double)first / (double)T;
+    }
+    dot += f * (P[e] / (double)T);
+  }
+  out[0] = aux_coeff * (double)E * dot;
+  out[1] = z_coeff * zsum / (double)T;
+  free(P);
+}
+
 /* Dispatch ([EP] layer walk-through: tokens grouped by target expert):
  * X[row] = x[row_token[row]], a copy of the row's bytes. */
 void oracle_dispatch(int64_t R, int64_t H, int dtype, const void *x, const int32_t *row_token, void *X) {

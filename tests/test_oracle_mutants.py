@@ -26,6 +26,10 @@ MUTANTS = {
     "down_proj_transposed": ("int64_t base = (e * H + n) * F;\n        double y = 0.0;\n        for (int64_t f = 0; f < F; ++f) y += hr[f] * elem(W2, dtype, base + f);",
                              "double y = 0.0;\n        for (int64_t f = 0; f < F; ++f) y += hr[f] * elem(W2, dtype, (e * F + f) * H + n);"),
     "combine_drops_residual": ("double acc = residual ? elem(residual, dtype, t * H + c) : 0.0;", "double acc = 0.0;"),
+    "aux_without_k": ("f = (double)demand[e] / ((double)T * (double)k);", "f = (double)demand[e] / (double)T;"),
+    "aux_without_E": ("out[0] = aux_coeff * (double)E * dot;", "out[0] = aux_coeff * dot;"),
+    "zloss_not_squared": ("zsum += lse * lse;", "zsum += lse;"),
+    "zloss_without_max": ("const double lse = m + log(den);", "const double lse = log(den);"),
     "renorm_missing": ("for (int r = 0; r < k; ++r) g[r] = (float)(p[r] / s);", "for (int r = 0; r < k; ++r) g[r] = (float)(p[r]);"),
 }
 
@@ -44,6 +48,9 @@ PINS = [
     lambda: P.test_single_expert_is_dense_ffn(oracle.SWIGLU, oracle.BF16),
     lambda: P.test_switch_top1_output_is_gate_times_expert(),
     lambda: P.test_dropped_tokens_pass_residual_bit_exactly(),
+    lambda: P.test_aux_loss_is_coefficient_for_uniform_probabilities(2, 0),
+    lambda: P.test_aux_loss_hand_examples(),
+    lambda: P.test_z_loss_closed_forms(),
 ]
 
 
@@ -65,7 +72,8 @@ def test_pins_catch_mutant(tmp_path, name):
     good = oracle.lib()
     mutant = ctypes.CDLL(so)
     for fn in ("oracle_capacity", "oracle_logits", "oracle_route_from_logits", "oracle_dispatch",
-               "oracle_expert_rows", "oracle_expert_ffn", "oracle_combine", "oracle_token_outputs"):
+               "oracle_expert_rows", "oracle_expert_ffn", "oracle_combine", "oracle_token_outputs",
+               "oracle_router_losses"):
         g, m = getattr(good, fn), getattr(mutant, fn)
         m.restype, m.argtypes = g.restype, g.argtypes
     caught = []

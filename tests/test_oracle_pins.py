@@ -458,3 +458,82 @@ def test_combine_matches_explicit_sum():
             if plan["dst_row"][t, j] >= 0:
                 want[t] += float(plan["topk_gate"][t, j]) * Y[plan["dst_row"][t, j]]
     assert np.allclose(y, want, rtol=1e-15, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- router training terms
+
+
+def _random_routing(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    demand = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    return idx, demand
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_aux_loss_is_coefficient_for_uniform_probabilities(k, mode):
+    """[EP]: with uniform routing probabilities P_i = 1/E the loss is the coefficient itself,
+    whatever the token fractions (they sum to one)."""
+    T, E = 97, 8
+    idx, demand = _random_routing(T, E, k, 3)
+    lg = np.repeat(np.linspace(-3, 5, T, dtype=np.float32)[:, None], E, axis=1)  # equal within a token
+    aux, _ = oracle.router_losses(lg, idx, demand, k, mode, aux_coeff=0.01)
+    assert abs(aux - 0.01) <= 1e-15
+
+
+def test_aux_loss_is_coefficient_for_uniform_load():
+    """[EP]: with uniform token fractions f_i = 1/E the loss is the coefficient itself,
+    whatever the probabilities (they sum to one per token)."""
+    T, E, k = 64, 8, 2
+    idx = np.array([[t % E, (t + 3) % E] for t in range(T)], np.int32)
+    demand = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    assert (demand == T * k // E).all()
+    lg = np.random.default_rng(5).normal(size=(T, E)).astype(np.float32)
+    aux, _ = oracle.router_losses(lg, idx, demand, k, 0, aux_coeff=0.01)
+    assert abs(aux - 0.01) <= 1e-14
+
+
+def test_aux_loss_hand_examples():
+    """Two tokens, logits (ln 2, 0, 0): P = (1/2, 1/4, 1/4).  Choices (0, 1) and (0, 2):
+    every choice counted / k (f = 1/2, 1/4, 1/4) gives E * (1/4 + 1/16 + 1/16) = 9/8;
+    DeepSpeed's top-2 path (first choices only, f = 1, 0, 0) gives E * 1/2 = 3/2."""
+    lg = np.array([[math.log(2), 0, 0]] * 2, np.float32)
+    idx = np.array([[0, 1], [0, 2]], np.int32)
+    demand = np.array([2, 1, 1], np.int32)
+    a0, z = oracle.router_losses(lg, idx, demand, 2, 0)
+    a1, _ = oracle.router_losses(lg, idx, demand, 2, 1)
+    assert abs(a0 - 9 / 8) <= 1e-7 and abs(a1 - 3 / 2) <= 1e-7
+    assert abs(z - math.log(4) ** 2) <= 1e-6  # logsumexp = ln(2 + 1 + 1)
+
+
+def test_z_loss_closed_forms():
+    """z-loss = mean over tokens of logsumexp(logits)^2: all-zero logits give (ln E)^2; one
+    logit a_t far above the rest gives mean(a_t^2)."""
+    E = 12
+    _, z = oracle.router_losses(np.zeros((5, E), np.float32), np.zeros((5, 1), np.int32),
+                                np.array([5] + [0] * (E - 1), np.int32), 1, 0, z_coeff=1e-3)
+    assert abs(z - 1e-3 * math.log(E) ** 2) <= 1e-15
+    a = np.array([1.5, -2.0, 3.25, 0.5], np.float32)
+    lg = np.full((4, E), -150.0, np.float32)
+    lg[np.arange(4), [3, 0, 7, 11]] = a
+    _, z = oracle.router_losses(lg, np.array([[3], [0], [7], [11]], np.int32),
+                                np.bincount([3, 0, 7, 11], minlength=E).astype(np.int32), 1, 0)
+    assert abs(z - float(np.mean(a.astype(np.float64) ** 2))) <= 1e-12
+
+
+def test_router_losses_relabelling_invariance():
+    T, E, k = 50, 6, 2
+    rng = np.random.default_rng(9)
+    lg = rng.normal(size=(T, E)).astype(np.float32)
+    idx, demand = _random_routing(T, E, k, 11)
+    perm = rng.permutation(E)  # new label of expert e is perm[e]
+    lg2 = np.empty_like(lg)
+    lg2[:, perm] = lg
+    idx2 = perm[idx].astype(np.int32)
+    dem2 = np.empty_like(demand)
+    dem2[perm] = demand
+    for mode in (0, 1):
+        a, z = oracle.router_losses(lg, idx, demand, k, mode)
+        b, w = oracle.router_losses(lg2, idx2, dem2, k, mode)
+        assert abs(a - b) <= 1e-12 and abs(z - w) <= 1e-12
