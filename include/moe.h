@@ -84,6 +84,15 @@ typedef enum { MOE_SOFTMAX_TOPK = 0, MOE_SOFTMAX_TOPK_RENORM = 1, MOE_TOPK_SOFTM
  * SWIGLU: y = (silu(x W_gate) * (x W_up)) W_down. */
 typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
 
+/* Token fraction f_e of the load-balancing loss alpha * E * sum_e f_e P_e ([EP]
+ * router section, auxiliary-loss paragraph; [SW] "Load balance & capacity"):
+ *   MOE_AUX_ALL_CHOICES  f_e = demand_e / (T*k): every choice counts, k in the
+ *                        denominator (Switch, Megatron-Core, DeepSpeed top-1/top-k)
+ *   MOE_AUX_FIRST_CHOICE f_e = (tokens whose first choice is e) / T, no division
+ *                        by k (DeepSpeed's top-2 path)
+ * P_e is the mean over tokens of softmax(logits)_e in both. */
+typedef enum { MOE_AUX_ALL_CHOICES = 0, MOE_AUX_FIRST_CHOICE = 1 } moe_aux_mode;
+
 typedef struct {
   int32_t T;              /* tokens, >= 0 (T = 0 is a valid no-op)            */
   int32_t H;              /* hidden size, >= 1                                 */
@@ -96,6 +105,9 @@ typedef struct {
   int32_t dropless;       /* 1: no capacity limit; 0: capacity from cf         */
   int32_t min_capacity;   /* capacity floor (DeepSpeed-style); 0 = none        */
   double capacity_factor; /* cf > 0 unless dropless                            */
+  int32_t aux_mode;       /* moe_aux_mode (used when plan->losses != NULL)      */
+  double aux_coeff;       /* alpha of the load-balancing loss, finite          */
+  double z_coeff;         /* coefficient of the z-loss, finite                 */
 } moe_config;
 
 /* Routing plan: device arrays, allocated by the caller, written by moe_route. */
@@ -109,6 +121,10 @@ typedef struct {
   int32_t *row_token; /* [R_max] token of each packed row (rows >= R are not written)                */
   int32_t *n_dropped; /* [1]     T*k - R                                                             */
   float *logits;      /* [T][E]  optional: fp32 router logits are written here when not NULL        */
+  double *losses;     /* [2]     optional: when not NULL, moe_route writes the router training terms
+                       *         [0] = aux_coeff * E * sum_e f_e P_e   (load balancing, moe_aux_mode)
+                       *         [1] = z_coeff * mean_t logsumexp(logits_t)^2   (z-loss)
+                       *         ([EP] router section: auxiliary-loss and z-loss paragraphs)        */
 } moe_plan;
 
 /* ---- host-only helpers (no HIP call; usable without a GPU) ------------------ */
@@ -135,14 +151,17 @@ const char *moe_last_error(void);
 
 /* ---- stream-ordered entry points ----------------------------------------------- */
 
-/* Route: logits ([SW] §1.1, fp32 per §2.1; the dot product is accumulated in
- * binary64 and rounded once to fp32), top-k selection (larger logit first, ties to
+/* Route: logits ([SW] §1.1, fp32 per §2.1, defined as the binary64 dot product
+ * plus bias rounded once to fp32), top-k selection (larger logit first, ties to
  * the lower expert index), gates (moe_gate_mode), capacity ([EP]; [DS7508]), and
  * slot assignment in choice-major priority — every token's first choice before
  * any second choice, token order inside each ([EP] "position" policy) — then
- * packing into expert-contiguous rows.
+ * packing into expert-contiguous rows.  Every choice is the one the defined
+ * logits make; logits written to plan->logits are the defined values for the
+ * experts that decide a choice and within ~1e-7 relative of them otherwise.
+ * With plan->losses set, also the router training terms (see moe_plan).
  * x: device [T][H] dtype.  Wg: device [H][E] fp32.  bias: device [E] fp32 or NULL.
- * plan: every pointer but logits required.  ws: device, >= moe_workspace_bytes. */
+ * plan: every pointer but logits and losses required.  ws: device, >= moe_workspace_bytes. */
 moe_status moe_route(const moe_config *cfg, const void *x, const float *Wg, const float *bias,
                      const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
 

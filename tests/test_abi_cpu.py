@@ -44,7 +44,8 @@ def _cfg(**kw):
     dict(k=0), dict(k=17, E=32), dict(k=5, E=4), dict(E=0), dict(E=1025), dict(T=-1), dict(H=0), dict(F=0),
     dict(T=2**30, k=2), dict(dtype=2), dict(gate_mode=3), dict(act=3), dict(dropless=2), dict(min_capacity=-1),
     dict(capacity_factor=0.0), dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")),
-    dict(capacity_factor=float("inf")),
+    dict(capacity_factor=float("inf")), dict(aux_mode=2), dict(aux_mode=-1), dict(aux_coeff=float("nan")),
+    dict(z_coeff=float("inf")),
 ])
 def test_validate_rejects(kw):
     c = _cfg(**kw)

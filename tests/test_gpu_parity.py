@@ -326,7 +326,7 @@ def _radius(x, wg, bias, v):
 def test_split_router_error_within_radius(gpu, name):
     """Every logit the split router leaves approximate lies inside its certified radius of the
     binary64-defined logit, by a wide margin; routing stays bit-exact."""
-    r = recipes.SMALL[name] if name in recipes.SMALL else recipes.SMALL["3x"]
+    r = recipes.SMALL[name] if name in recipes.SMALL else recipes.SMALL["3a"]
     x = recipes.gen_x(r)
     wg, bias = recipes.gen_router(r)
     _, gplan = _gpu_route(r, gpu, x, wg, bias)
@@ -374,3 +374,57 @@ def test_split_router_exact_and_near_ties(gpu):
     assert (sel == 2).any() and ((sel == 5).any(1) & (sel == 2).any(1)).any()
     _, gplan = _gpu_route(r, gpu, x, wg, None)
     _check_route(r, gplan, oplan)
+
+
+# --------------------------------------------------------------------------- router training terms
+
+
+def _gpu_route_losses(r, gpu, x, wg, bias, aux_mode, aux_coeff, z_coeff):
+    import torch
+
+    cfg = B.MoEConfig.from_run(r)
+    cfg.aux_mode, cfg.aux_coeff, cfg.z_coeff = aux_mode, aux_coeff, z_coeff
+    plan = B.alloc_plan(cfg, gpu, logits=True, losses=True)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.route(cfg, U.dev(x, gpu), U.dev(wg, gpu), U.dev(bias, gpu), plan, ws)
+    torch.cuda.synchronize()
+    return plan
+
+
+@pytest.mark.parametrize("name", SMALL + ["full-2", "full-5"])
+@pytest.mark.parametrize("aux_mode", [0, 1])
+def test_router_losses(gpu, name, aux_mode):
+    """Load-balancing loss and z-loss against the oracle: on the oracle's own routing (1e-5
+    relative), and on the GPU's logits and choices (1e-6 relative: only the fp32 exp/log differ)."""
+    r = recipes.RUNS[name[5:]] if name.startswith("full-") else recipes.SMALL[name]
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    gplan = _gpu_route_losses(r, gpu, x, wg, bias, aux_mode, 0.01, 0.001)
+    got = U.host(gplan["losses"])
+    oplan = _oracle_route(r, x, wg, bias)
+    U.assert_plan_equal(gplan, oplan, f"losses routing {r.name}")
+    ref = oracle.router_losses(oplan["logits"], oplan["topk_idx"], oplan["demand"], r.k, aux_mode, 0.01, 0.001)
+    own = oracle.router_losses(U.host(gplan["logits"]), U.host(gplan["topk_idx"]), U.host(gplan["demand"]), r.k,
+                               aux_mode, 0.01, 0.001)
+    print(f"[losses] run {r.name} mode {aux_mode}: gpu {got[0]:.9g} {got[1]:.9g}  oracle {ref[0]:.9g} {ref[1]:.9g}",
+          flush=True)
+    for i in range(2):
+        assert abs(got[i] - ref[i]) <= 1e-5 * abs(ref[i]), (i, got[i], ref[i])
+        assert abs(got[i] - own[i]) <= 1e-6 * abs(own[i]), (i, got[i], own[i])
+
+
+def test_router_losses_uniform_and_empty(gpu):
+    """x = 0 and no bias: every probability is 1/E, so the load-balancing loss is the
+    coefficient itself, and the z-loss is coeff * (ln E)^2; T = 0 gives zeros."""
+    import math
+
+    r = recipes.SMALL["3a"].scaled(name="lossuni", T=300, bias="none")
+    x = np.zeros_like(recipes.gen_x(r))
+    wg, _ = recipes.gen_router(r)
+    for mode in (0, 1):
+        got = U.host(_gpu_route_losses(r, gpu, x, wg, None, mode, 0.01, 0.001)["losses"])
+        zref = 0.001 * math.log(r.E) ** 2
+        assert abs(got[0] - 0.01) <= 1e-8 and abs(got[1] - zref) <= 1e-6 * zref, (got, zref)
+    r0 = r.scaled(name="loss-T0", T=0)
+    got = U.host(_gpu_route_losses(r0, gpu, x[:0], wg, None, 0, 0.01, 0.001)["losses"])
+    assert (got == 0).all()

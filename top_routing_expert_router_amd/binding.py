@@ -30,12 +30,13 @@ class _Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dropless", ctypes.c_int32), ("min_capacity", ctypes.c_int32),
-                ("capacity_factor", ctypes.c_double)]
+                ("capacity_factor", ctypes.c_double), ("aux_mode", ctypes.c_int32), ("aux_coeff", ctypes.c_double),
+                ("z_coeff", ctypes.c_double)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets",
-                                               "row_token", "n_dropped", "logits")]
+                                               "row_token", "n_dropped", "logits", "losses")]
 
 
 @dataclass
@@ -51,10 +52,14 @@ class MoEConfig:
     dropless: int = 0
     capacity_factor: float = 1.0
     min_capacity: int = 0
+    aux_mode: int = 0  # 0: every choice / (T*k); 1: first choice / T
+    aux_coeff: float = 1e-2
+    z_coeff: float = 1e-3
 
     def c(self):
         return _Config(self.T, self.H, self.E, self.k, self.F, self.dtype, self.gate_mode, self.act, self.dropless,
-                       self.min_capacity, float(self.capacity_factor))
+                       self.min_capacity, float(self.capacity_factor), self.aux_mode, float(self.aux_coeff),
+                       float(self.z_coeff))
 
     @classmethod
     def from_run(cls, run):
@@ -141,11 +146,12 @@ def workspace_bytes(cfg: MoEConfig):
 
 def _plan_struct(plan):
     return _Plan(*[_ptr(plan.get(n)) for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets",
-                                               "row_token", "n_dropped", "logits")])
+                                               "row_token", "n_dropped", "logits", "losses")])
 
 
-def alloc_plan(cfg: MoEConfig, device, logits=False):
-    """Device tensors of a routing plan for cfg (caller-owned memory)."""
+def alloc_plan(cfg: MoEConfig, device, logits=False, losses=False):
+    """Device tensors of a routing plan for cfg (caller-owned memory); `losses` adds the
+    two router training terms (load-balancing loss, z-loss) as a float64 tensor of 2."""
     import torch
 
     T, E, k = cfg.T, cfg.E, cfg.k
@@ -162,6 +168,8 @@ def alloc_plan(cfg: MoEConfig, device, logits=False):
     )
     if logits:
         plan["logits"] = torch.empty((T, E), dtype=torch.float32, device=device)
+    if losses:
+        plan["losses"] = torch.empty(2, dtype=torch.float64, device=device)
     return plan
 
 

@@ -55,7 +55,7 @@ int effective_capacity(const moe_config* c) {
 struct Layout {
   int nb, Q;
   bool split;  // split-bf16 router buffers present
-  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, route_end, h, ffn_end, total;
+  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, lp, lz, lc, route_end, h, ffn_end, total;
 };
 
 // The split-bf16 router runs for bf16 activations with H a multiple of 64 and a
@@ -83,6 +83,11 @@ Layout layout_of(const moe_config* c) {
     L.count = L.utok + align_up(sizeof(int4) * (size_t)c->T);
     end = L.count + kAlign;
   }
+  // router training terms: per-64-token-block partial sums
+  L.lp = end;
+  L.lz = L.lp + align_up(sizeof(double) * (size_t)L.nb * (size_t)c->E);
+  L.lc = L.lz + align_up(sizeof(double) * (size_t)(L.nb > 0 ? L.nb : 1));
+  end = L.lc + align_up(sizeof(int32_t) * (size_t)L.nb * (size_t)c->E);
   L.route_end = end;
   L.h = 0;
   L.ffn_end = align_up(eb * (size_t)max_rows_of(c) * (size_t)c->F);
@@ -114,6 +119,8 @@ moe_status moe_validate(const moe_config* c) {
   if (c->dropless != 0 && c->dropless != 1) return MOE_ERR_INVALID_ARG;
   if (c->min_capacity < 0) return MOE_ERR_INVALID_ARG;
   if (!c->dropless && !(c->capacity_factor > 0.0 && isfinite(c->capacity_factor))) return MOE_ERR_INVALID_ARG;
+  if (c->aux_mode != MOE_AUX_ALL_CHOICES && c->aux_mode != MOE_AUX_FIRST_CHOICE) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(c->aux_coeff) || !isfinite(c->z_coeff)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -187,6 +194,12 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   if ((e = moe::launch_slot_finalize(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->kept, plan->dst_row,
                                      plan->row_token, plan->offsets, plan->n_dropped, (int)max_rows_of(c), st)) != hipSuccess)
     return hip_fail(e, "slot_finalize");
+  if (plan->losses &&
+      (e = moe::launch_router_losses(logits, plan->topk_idx, plan->demand, c->T, c->E, c->k, c->aux_mode,
+                                     c->aux_coeff, c->z_coeff, reinterpret_cast<double*>(w + L.lp),
+                                     reinterpret_cast<double*>(w + L.lz), reinterpret_cast<int32_t*>(w + L.lc),
+                                     plan->losses, st)) != hipSuccess)
+    return hip_fail(e, "router_losses");
   return MOE_OK;
 }
 
