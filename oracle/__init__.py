@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 F32, BF16 = 0, 1
 SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
 RELU, GELU, SWIGLU = 0, 1, 2
+SOFTMAX, SIGMOID = 0, 1
+DROP_POSITION, DROP_PROBS = 0, 1
 
 _lib = None
 
@@ -42,10 +44,10 @@ def lib():
         L.oracle_logits.restype = None
         L.oracle_logits.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp]
         L.oracle_route_from_logits.restype = i64
-        L.oracle_route_from_logits.argtypes = [i64, i64, i32, i32, i64, vp] + [vp] * 8
+        L.oracle_route_from_logits.argtypes = [i64, i64, i32, i32, i32, i32, i64, vp] + [vp] * 8
         L.oracle_dispatch.restype = None
         L.oracle_router_losses.restype = None
-        L.oracle_router_losses.argtypes = [i64, i64, i32, vp, vp, vp, i32, dbl, dbl, vp]
+        L.oracle_router_losses.argtypes = [i64, i64, i32, i32, vp, vp, vp, i32, dbl, dbl, vp]
         L.oracle_dispatch.argtypes = [i64, i64, i32, vp, vp, vp]
         L.oracle_expert_rows.restype = None
         L.oracle_expert_rows.argtypes = [i64, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]
@@ -91,7 +93,7 @@ def logits(x, dtype, wg, bias=None):
     return out
 
 
-def route_from_logits(lg, k, gate_mode, C):
+def route_from_logits(lg, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION):
     """C: capacity, or None for dropless.  Returns the routing plan as numpy arrays."""
     lg = _c(lg, np.float32)
     T, E = lg.shape
@@ -107,7 +109,7 @@ def route_from_logits(lg, k, gate_mode, C):
         row_token=np.full(max(tk, 1), -1, np.int32),
         n_dropped=np.zeros(1, np.int32),
     )
-    R = lib().oracle_route_from_logits(T, E, k, gate_mode, Cc, _p(lg), *[_p(plan[n]) for n in (
+    R = lib().oracle_route_from_logits(T, E, k, gate_mode, score_fn, drop_policy, Cc, _p(lg), *[_p(plan[n]) for n in (
         "topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets", "row_token", "n_dropped")])
     if R < 0:
         raise ValueError("bad routing arguments")
@@ -116,21 +118,21 @@ def route_from_logits(lg, k, gate_mode, C):
     return plan
 
 
-def router_losses(logits, topk_idx, demand, k, aux_mode=0, aux_coeff=1.0, z_coeff=1.0):
+def router_losses(logits, topk_idx, demand, k, aux_mode=0, aux_coeff=1.0, z_coeff=1.0, score_fn=SOFTMAX):
     """(load-balancing loss, z-loss) of a routing: see oracle_router_losses."""
     lg = _c(logits, np.float32)
     T, E = lg.shape
     idx = _c(np.asarray(topk_idx).reshape(T, k), np.int32)
     dem = _c(demand, np.int32)
     out = np.zeros(2, np.float64)
-    lib().oracle_router_losses(T, E, k, _p(lg), _p(idx), _p(dem), int(aux_mode), float(aux_coeff),
+    lib().oracle_router_losses(T, E, k, int(score_fn), _p(lg), _p(idx), _p(dem), int(aux_mode), float(aux_coeff),
                                float(z_coeff), _p(out))
     return float(out[0]), float(out[1])
 
 
-def route(x, dtype, wg, bias, k, gate_mode, C):
+def route(x, dtype, wg, bias, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION):
     lg = logits(x, dtype, wg, bias)
-    plan = route_from_logits(lg, k, gate_mode, C)
+    plan = route_from_logits(lg, k, gate_mode, C, score_fn, drop_policy)
     plan["logits"] = lg
     return plan
 
@@ -202,9 +204,10 @@ def token_outputs(tokens, x, dtype, act, plan, w1, w3, w2, residual=None):
     return y
 
 
-def forward(x, dtype, wg, bias, w1, w3, w2, k, gate_mode, act, C, residual=None):
+def forward(x, dtype, wg, bias, w1, w3, w2, k, gate_mode, act, C, residual=None, score_fn=SOFTMAX,
+            drop_policy=DROP_POSITION):
     """Whole layer: route -> dispatch -> expert FFN -> combine.  Returns (y float64, plan, X, Y)."""
-    plan = route(x, dtype, wg, bias, k, gate_mode, C)
+    plan = route(x, dtype, wg, bias, k, gate_mode, C, score_fn, drop_policy)
     X = dispatch(x, dtype, plan)
     Y = expert_ffn(X, plan["offsets"], dtype, act, w1, w3, w2)
     y = combine(Y, plan, dtype, residual)

@@ -42,6 +42,8 @@
 enum { OR_F32 = 0, OR_BF16 = 1 };
 enum { OR_SOFTMAX_TOPK = 0, OR_SOFTMAX_TOPK_RENORM = 1, OR_TOPK_SOFTMAX = 2 };
 enum { OR_RELU = 0, OR_GELU = 1, OR_SWIGLU = 2 };
+enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
+enum { OR_DROP_POSITION = 0, OR_DROP_PROBS = 1 };
 
 /* A bf16 number is the upper half of an IEEE binary32; its value is exact in binary64. */
 static double bf16_to_double(uint16_t b) {
@@ -107,7 +109,18 @@ static void select_topk(const float *l, int64_t E, int k, int32_t *idx) {
 /* Gate values of the k choices ([EP] router: softmax then top-k, or top-k then
  * normalise over the selected; [SW] §1.1 p_i = exp(h_i)/sum_j exp(h_j)), binary64
  * from the fp32 logits, rounded once to fp32. */
-static void gates(const float *l, int64_t E, int k, int mode, const int32_t *idx, float *g) {
+static void gates(const float *l, int64_t E, int k, int mode, int score, const int32_t *idx, float *g) {
+  if (score == OR_SIGMOID && mode != OR_TOPK_SOFTMAX) {
+    /* sigmoid scores ([EP] router: "softmax or sigmoid, then top-k"): the chosen
+     * scores themselves, or divided by their sum when renormalised */
+    double sc[16], sum = 0.0;
+    for (int r = 0; r < k; ++r) {
+      sc[r] = 1.0 / (1.0 + exp(-(double)l[idx[r]]));
+      sum += sc[r];
+    }
+    for (int r = 0; r < k; ++r) g[r] = (float)(mode == OR_SOFTMAX_TOPK ? sc[r] : sc[r] / sum);
+    return;
+  }
   double m = l[idx[0]]; /* the largest logit */
   if (mode == OR_TOPK_SOFTMAX) {
     double den = 0.0;
@@ -133,22 +146,35 @@ static void gates(const float *l, int64_t E, int k, int mode, const int32_t *idx
 /*
  * Routing plan from given fp32 logits: selection, gates, capacity, slot
  * assignment, packing.  C < 0 means dropless.
- *   - slot assignment ([EP] capacity / drop: "position" drops the assignments at
- *     the end of the batch; over-capacity assignments skip the expert): walk
- *     q = 0 .. T*k-1 with r = q / T, t = q % T; the assignment (t, r) to e = idx
- *     takes slot n_e, then n_e += 1; it is kept iff slot < C.
+ *   - selection is on the logits (softmax and sigmoid are both increasing, so
+ *     either score picks the same experts in the same order);
+ *   - slot assignment, "position" policy ([EP] capacity / drop: drop the
+ *     assignments at the end of the batch; over-capacity assignments skip the
+ *     expert): walk q = 0 .. T*k-1 with r = q / T, t = q % T; the assignment
+ *     (t, r) to e = idx takes slot n_e, then n_e += 1; it is kept iff slot < C.
+ *   - "probs" policy ([EP]: drop the lowest-probability ones): per expert, the C
+ *     assignments with the largest gate value are kept (equal gates: the earlier
+ *     q first); the kept ones take slots in q order.
  *   - packing: offsets = exclusive prefix sum of kept; a kept assignment goes to
  *     packed row offsets[e] + slot (-1 when dropped); row_token inverts it.
  * Returns R = offsets[E], or -1 on bad arguments.
  */
-int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int64_t C, const float *logits,
-                                 int32_t *topk_idx, float *topk_gate, int32_t *dst_row, int32_t *demand,
-                                 int32_t *kept, int32_t *offsets, int32_t *row_token, int32_t *n_dropped) {
+static int cmp_probs(const void *a, const void *b) {
+  /* entries are (gate, q) pairs: larger gate first, then smaller q */
+  const double *x = (const double *)a, *y = (const double *)b;
+  if (x[0] != y[0]) return x[0] > y[0] ? -1 : 1;
+  return x[1] < y[1] ? -1 : (x[1] > y[1] ? 1 : 0);
+}
+
+int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int score_fn, int drop_policy, int64_t C,
+                                 const float *logits, int32_t *topk_idx, float *topk_gate, int32_t *dst_row,
+                                 int32_t *demand, int32_t *kept, int32_t *offsets, int32_t *row_token,
+                                 int32_t *n_dropped) {
   if (k < 1 || k > 16 || k > E || T < 0) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     select_topk(logits + t * E, E, k, topk_idx + t * k);
-    gates(logits + t * E, E, k, gate_mode, topk_idx + t * k, topk_gate + t * k);
+    gates(logits + t * E, E, k, gate_mode, score_fn, topk_idx + t * k, topk_gate + t * k);
   }
   int64_t *n = (int64_t *)calloc((size_t)E, sizeof(int64_t));
   int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k > 0 ? T * k : 1));
@@ -157,6 +183,36 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
     int32_t e = topk_idx[t * k + r];
     slot[t * k + r] = n[e];
     n[e] += 1;
+  }
+  if (drop_policy == OR_DROP_PROBS && C >= 0) {
+    /* per expert: its assignments in q order, sorted by (gate desc, q asc); the
+     * first C are kept and renumbered in q order, the rest get slot C (dropped) */
+    double *ent = (double *)malloc(sizeof(double) * 2 * (size_t)(T * k > 0 ? T * k : 1));
+    char *keep = (char *)calloc((size_t)(T * k > 0 ? T * k : 1), 1);
+    for (int64_t e = 0; e < E; ++e) {
+      if (n[e] <= C) continue;
+      int64_t m = 0;
+      for (int64_t q = 0; q < T * k; ++q) {
+        const int64_t ch = q / T, tok = q % T; /* choice-major position q */
+        if (topk_idx[tok * k + ch] == (int32_t)e) {
+          ent[2 * m] = (double)topk_gate[tok * k + ch];
+          ent[2 * m + 1] = (double)q;
+          ++m;
+        }
+      }
+      qsort(ent, (size_t)m, 2 * sizeof(double), cmp_probs);
+      for (int64_t j = 0; j < C; ++j) {
+        int64_t q = (int64_t)ent[2 * j + 1];
+        keep[(q % T) * k + q / T] = 1;
+      }
+      int64_t next = 0;
+      for (int64_t q = 0; q < T * k; ++q) {
+        const int64_t ch = q / T, tok = q % T;
+        if (topk_idx[tok * k + ch] == (int32_t)e) slot[tok * k + ch] = keep[tok * k + ch] ? next++ : C;
+      }
+    }
+    free(ent);
+    free(keep);
   }
   offsets[0] = 0;
   for (int64_t e = 0; e < E; ++e) {
@@ -185,6 +241,7 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
  * Router training terms ([EP] router section, the auxiliary-loss and z-loss
  * paragraphs; [SW] "Load balance & capacity"), binary64 from the fp32 logits.
  *   P_e   = (1/T) sum_t softmax(l_t)_e          mean routing probability
+ *           (sigmoid scoring: the token's sigmoid scores divided by their sum)
  *   f_e   = demand_e / (T*k)   (aux_mode 0: every choice counts, k in the
  *           denominator -- Switch, Megatron-Core, DeepSpeed top-1 / top-k)
  *         = first_e / T        (aux_mode 1: only each token's first choice,
@@ -194,7 +251,7 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
  * demand is the number of choices per expert before any capacity limit.
  * T = 0 gives zeros.
  */
-void oracle_router_losses(int64_t T, int64_t E, int k, const float *logits, const int32_t *topk_idx,
+void oracle_router_losses(int64_t T, int64_t E, int k, int score_fn, const float *logits, const int32_t *topk_idx,
                           const int32_t *demand, int aux_mode, double aux_coeff, double z_coeff, double *out) {
   out[0] = out[1] = 0.0;
   if (T <= 0) return;
@@ -207,7 +264,13 @@ void oracle_router_losses(int64_t T, int64_t E, int k, const float *logits, cons
       if (l[e] > m) m = l[e];
     double den = 0.0;
     for (int64_t j = 0; j < E; ++j) den += exp((double)l[j] - m);
-    for (int64_t j = 0; j < E; ++j) P[j] += exp((double)l[j] - m) / den;
+    if (score_fn == OR_SIGMOID) { /* P from the token's sigmoid scores divided by their sum */
+      double ssum = 0.0;
+      for (int64_t j = 0; j < E; ++j) ssum += 1.0 / (1.0 + exp(-(double)l[j]));
+      for (int64_t j = 0; j < E; ++j) P[j] += (1.0 / (1.0 + exp(-(double)l[j]))) / ssum;
+    } else {
+      for (int64_t j = 0; j < E; ++j) P[j] += exp((double)l[j] - m) / den;
+    }
     const double lse = m + log(den);
     zsum += lse * lse;
   }

@@ -26,6 +26,10 @@ MUTANTS = {
     "down_proj_transposed": ("int64_t base = (e * H + n) * F;\n        double y = 0.0;\n        for (int64_t f = 0; f < F; ++f) y += hr[f] * elem(W2, dtype, base + f);",
                              "double y = 0.0;\n        for (int64_t f = 0; f < F; ++f) y += hr[f] * elem(W2, dtype, (e * F + f) * H + n);"),
     "combine_drops_residual": ("double acc = residual ? elem(residual, dtype, t * H + c) : 0.0;", "double acc = 0.0;"),
+    "probs_keeps_smallest": ("if (x[0] != y[0]) return x[0] > y[0] ? -1 : 1;", "if (x[0] != y[0]) return x[0] < y[0] ? -1 : 1;"),
+    "probs_tie_to_later": ("return x[1] < y[1] ? -1 : (x[1] > y[1] ? 1 : 0);", "return x[1] > y[1] ? -1 : (x[1] < y[1] ? 1 : 0);"),
+    "sigmoid_sign": ("sc[r] = 1.0 / (1.0 + exp(-(double)l[idx[r]]));", "sc[r] = 1.0 / (1.0 + exp((double)l[idx[r]]));"),
+    "sigmoid_not_renormalised": ("g[r] = (float)(mode == OR_SOFTMAX_TOPK ? sc[r] : sc[r] / sum);", "g[r] = (float)(sc[r]);"),
     "aux_without_k": ("f = (double)demand[e] / ((double)T * (double)k);", "f = (double)demand[e] / (double)T;"),
     "aux_without_E": ("out[0] = aux_coeff * (double)E * dot;", "out[0] = aux_coeff * dot;"),
     "zloss_not_squared": ("zsum += lse * lse;", "zsum += lse;"),
@@ -51,6 +55,10 @@ PINS = [
     lambda: P.test_aux_loss_is_coefficient_for_uniform_probabilities(2, 0),
     lambda: P.test_aux_loss_hand_examples(),
     lambda: P.test_z_loss_closed_forms(),
+    lambda: P.test_sigmoid_gates_closed_forms(),
+    lambda: P.test_probs_policy_hand_example(),
+    lambda: P.test_probs_policy_keeps_largest_gates(0),
+    lambda: P.test_probs_policy_equal_gates_is_position_policy(),
 ]
 
 

@@ -537,3 +537,88 @@ def test_router_losses_relabelling_invariance():
         a, z = oracle.router_losses(lg, idx, demand, k, mode)
         b, w = oracle.router_losses(lg2, idx2, dem2, k, mode)
         assert abs(a - b) <= 1e-12 and abs(z - w) <= 1e-12
+
+
+# --------------------------------------------------------------------------- routing variants
+
+
+def test_sigmoid_gates_closed_forms():
+    """[EP] router: scores by sigmoid instead of softmax.  Logits 0 and ln 3 score 1/2 and 3/4;
+    renormalised over the two chosen: 2/5 and 3/5; top-k-then-softmax ignores the score."""
+    lg = np.array([[0.0, math.log(3), -5.0]], np.float32)
+    p0 = oracle.route_from_logits(lg, 2, oracle.SOFTMAX_TOPK, None, oracle.SIGMOID)
+    assert (p0["topk_idx"] == [[1, 0]]).all()
+    assert np.allclose(p0["topk_gate"], [[0.75, 0.5]], rtol=1e-6, atol=0)
+    p1 = oracle.route_from_logits(lg, 2, oracle.SOFTMAX_TOPK_RENORM, None, oracle.SIGMOID)
+    assert np.allclose(p1["topk_gate"], [[0.6, 0.4]], rtol=1e-6, atol=0)
+    p2 = oracle.route_from_logits(lg, 2, oracle.TOPK_SOFTMAX, None, oracle.SIGMOID)
+    p3 = oracle.route_from_logits(lg, 2, oracle.TOPK_SOFTMAX, None, oracle.SOFTMAX)
+    assert np.array_equal(p2["topk_gate"], p3["topk_gate"])
+
+
+def test_sigmoid_selects_like_softmax():
+    lg = np.random.default_rng(4).normal(size=(300, 10)).astype(np.float32)
+    for mode in (0, 1, 2):
+        a = oracle.route_from_logits(lg, 3, mode, 90, oracle.SIGMOID)
+        b = oracle.route_from_logits(lg, 3, mode, 90, oracle.SOFTMAX)
+        for n in ("topk_idx", "dst_row", "demand", "kept", "offsets"):
+            assert np.array_equal(a[n], b[n]), n
+
+
+def test_sigmoid_aux_loss_uniform_scores_give_coefficient():
+    T, E, k = 40, 6, 2
+    idx, demand = _random_routing(T, E, k, 8)
+    lg = np.repeat(np.linspace(-2, 2, T, dtype=np.float32)[:, None], E, axis=1)
+    aux, _ = oracle.router_losses(lg, idx, demand, k, 0, 0.01, score_fn=oracle.SIGMOID)
+    assert abs(aux - 0.01) <= 1e-15
+
+
+def test_probs_policy_hand_example():
+    """[EP] "probs" drops the lowest-probability assignments: three tokens on one expert with
+    gates 0.2, 0.9, 0.5 and capacity 2 keep tokens 1 and 2, packed in token order."""
+    g = np.array([0.2, 0.9, 0.5])
+    lg = np.zeros((3, 8), np.float32)
+    lg[:, 0] = np.log(7 * g / (1 - g))  # eight experts: expert 0 leads with softmax gate g
+    plan = oracle.route_from_logits(lg, 1, oracle.SOFTMAX_TOPK, 2, drop_policy=oracle.DROP_PROBS)
+    assert (plan["topk_idx"].ravel() == 0).all()
+    assert np.allclose(plan["topk_gate"].ravel(), g, rtol=1e-6)
+    assert list(plan["dst_row"].ravel()) == [-1, 0, 1]
+    assert list(plan["row_token"]) == [1, 2] and plan["n_dropped"][0] == 1
+
+
+def test_probs_policy_equal_gates_is_position_policy():
+    """Equal gates everywhere leave only the position tie-break: the same plan as "position"."""
+    T, E, k = 200, 5, 2
+    lg = np.zeros((T, E), np.float32)
+    lg[:, 0] = 1.0  # every token: expert 0 then 1, gates equal across tokens
+    for C in (0, 7, 150):
+        a = oracle.route_from_logits(lg, k, oracle.SOFTMAX_TOPK, C, drop_policy=oracle.DROP_PROBS)
+        b = oracle.route_from_logits(lg, k, oracle.SOFTMAX_TOPK, C, drop_policy=oracle.DROP_POSITION)
+        for n in ("topk_idx", "dst_row", "demand", "kept", "offsets", "row_token"):
+            assert np.array_equal(a[n], b[n]), (C, n)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_probs_policy_keeps_largest_gates(mode):
+    """Definition, checked independently: per expert, kept = min(demand, C); every kept gate is
+    at least every dropped gate (equal gates: the earlier choice-major position is kept); kept
+    assignments are packed in position order; and dropless is the same under both policies."""
+    T, E, k, C = 400, 8, 2, 60
+    lg = np.random.default_rng(6).normal(size=(T, E)).astype(np.float32)
+    lg[::7] = np.round(lg[::7])  # some repeated logits -> equal gates across tokens
+    p = oracle.route_from_logits(lg, k, mode, C, drop_policy=oracle.DROP_PROBS)
+    idx, g, dst = p["topk_idx"], p["topk_gate"], p["dst_row"]
+    for e in range(E):
+        qs = [(r * T + t, t, r) for r in range(k) for t in range(T) if idx[t, r] == e]
+        assert p["demand"][e] == len(qs) and p["kept"][e] == min(len(qs), C)
+        kept = [(q, t, r) for q, t, r in qs if dst[t, r] >= 0]
+        drop = [(q, t, r) for q, t, r in qs if dst[t, r] < 0]
+        assert len(kept) == p["kept"][e]
+        for qk, tk, rk in kept:
+            for qd, td, rd in drop:
+                assert g[tk, rk] > g[td, rd] or (g[tk, rk] == g[td, rd] and qk < qd)
+        rows = [dst[t, r] for q, t, r in sorted(kept)]
+        assert rows == list(range(p["offsets"][e], p["offsets"][e] + len(kept)))
+    a = oracle.route_from_logits(lg, k, mode, None, drop_policy=oracle.DROP_PROBS)
+    b = oracle.route_from_logits(lg, k, mode, None, drop_policy=oracle.DROP_POSITION)
+    assert np.array_equal(a["dst_row"], b["dst_row"])
