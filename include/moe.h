@@ -93,6 +93,20 @@ typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
  * P_e is the mean over tokens of softmax(logits)_e in both. */
 typedef enum { MOE_AUX_ALL_CHOICES = 0, MOE_AUX_FIRST_CHOICE = 1 } moe_aux_mode;
 
+/* Router score ([EP] router: "softmax or sigmoid, then top-k").  Both are
+ * increasing in the logit, so the choices are the same; with SIGMOID the gate of
+ * a choice is its score s = 1/(1+exp(-l)) (MOE_SOFTMAX_TOPK) or s over the sum
+ * of the chosen scores (MOE_SOFTMAX_TOPK_RENORM); MOE_TOPK_SOFTMAX is the
+ * softmax over the chosen logits either way. */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+/* Which over-capacity assignments are dropped ([EP] capacity / drop section):
+ *   POSITION  the last ones in choice-major order (r*T + t)
+ *   PROBS     per expert, the ones with the smallest gate value; kept: the C
+ *             largest gates (equal gates: earlier position first), packed in
+ *             position order.  Same as POSITION when nothing is dropped. */
+typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
+
 typedef struct {
   int32_t T;              /* tokens, >= 0 (T = 0 is a valid no-op)            */
   int32_t H;              /* hidden size, >= 1                                 */
@@ -108,6 +122,8 @@ typedef struct {
   int32_t aux_mode;       /* moe_aux_mode (used when plan->losses != NULL)      */
   double aux_coeff;       /* alpha of the load-balancing loss, finite          */
   double z_coeff;         /* coefficient of the z-loss, finite                 */
+  int32_t score_fn;       /* moe_score_fn                                       */
+  int32_t drop_policy;    /* moe_drop_policy                                    */
 } moe_config;
 
 /* Routing plan: device arrays, allocated by the caller, written by moe_route. */
@@ -155,8 +171,9 @@ const char *moe_last_error(void);
  * plus bias rounded once to fp32), top-k selection (larger logit first, ties to
  * the lower expert index), gates (moe_gate_mode), capacity ([EP]; [DS7508]), and
  * slot assignment in choice-major priority — every token's first choice before
- * any second choice, token order inside each ([EP] "position" policy) — then
- * packing into expert-contiguous rows.  Every choice is the one the defined
+ * any second choice, token order inside each ([EP] "position" policy), or by
+ * gate value ("probs", moe_drop_policy) — then packing into expert-contiguous
+ * rows.  Every choice is the one the defined
  * logits make; logits written to plan->logits are the defined values for the
  * experts that decide a choice and within ~1e-7 relative of them otherwise.
  * With plan->losses set, also the router training terms (see moe_plan).

@@ -45,7 +45,7 @@ def _cfg(**kw):
     dict(T=2**30, k=2), dict(dtype=2), dict(gate_mode=3), dict(act=3), dict(dropless=2), dict(min_capacity=-1),
     dict(capacity_factor=0.0), dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")),
     dict(capacity_factor=float("inf")), dict(aux_mode=2), dict(aux_mode=-1), dict(aux_coeff=float("nan")),
-    dict(z_coeff=float("inf")),
+    dict(z_coeff=float("inf")), dict(score_fn=2), dict(drop_policy=2), dict(drop_policy=-1),
 ])
 def test_validate_rejects(kw):
     c = _cfg(**kw)

@@ -428,3 +428,124 @@ def test_router_losses_uniform_and_empty(gpu):
     r0 = r.scaled(name="loss-T0", T=0)
     got = U.host(_gpu_route_losses(r0, gpu, x[:0], wg, None, 0, 0.01, 0.001)["losses"])
     assert (got == 0).all()
+
+
+# --------------------------------------------------------------------------- routing variants
+
+
+def _gpu_route_cfg(cfg, gpu, x, wg, bias):
+    import torch
+
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.route(cfg, U.dev(x, gpu), U.dev(wg, gpu), U.dev(bias, gpu), plan, ws)
+    torch.cuda.synchronize()
+    return plan
+
+
+@pytest.mark.parametrize("name", ["1", "2", "3a", "4", "5"])
+@pytest.mark.parametrize("gate_mode", [0, 1, 2])
+def test_sigmoid_scoring_route(gpu, name, gate_mode):
+    """Sigmoid scores: same choices as softmax, gates are the scores (or renormalised)."""
+    r = recipes.SMALL[name].scaled(name=f"sig-{name}-{gate_mode}", gate_mode=gate_mode)
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.score_fn = 1
+    gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
+    oplan = oracle.route(x, r.dtype, wg, bias, r.k, gate_mode, _cap(r), oracle.SIGMOID)
+    _check_route(r, gplan, oplan)
+
+
+def test_sigmoid_scoring_forward(gpu):
+    import torch
+
+    r = recipes.SMALL["5"].scaled(name="sig-fwd")
+    d = recipes.gen_all(r)
+    yref, oplan, _, _ = oracle.forward(d["x"], r.dtype, d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], r.k,
+                                       r.gate_mode, r.act, _cap(r), score_fn=oracle.SIGMOID)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.score_fn = 1
+    gp = {"x": U.dev(d["x"], gpu), "wg": U.dev(d["wg"], gpu), "bias": U.dev(d["bias"], gpu),
+          "w1": U.dev(d["w1"], gpu), "w3": U.dev(d["w3"], gpu), "w2": U.dev(d["w2"], gpu)}
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    rmax = max(B.max_rows(cfg), 1)
+    X = torch.empty((rmax, r.H), dtype=torch.bfloat16, device=gpu)
+    Y = torch.empty_like(X)
+    y = torch.empty((r.T, r.H), dtype=torch.bfloat16, device=gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.forward(cfg, gp["x"], gp["wg"], gp["bias"], gp["w1"], gp["w3"], gp["w2"], None, y, plan, X, Y, ws)
+    torch.cuda.synchronize()
+    _check_route(r, plan, oplan)
+    U.assert_close(U.host(y), yref, True, "sigmoid forward")
+
+
+def _check_probs_plan(r, gplan, oplan, tol=2e-6):
+    """The kept sets must be the oracle's except for assignments whose oracle gate is within
+    `tol` (relative) of its expert's cut-off; whatever the GPU kept must be a valid "probs"
+    choice under the GPU's own gates; packing exact for what was kept."""
+    T, k = r.T, r.k
+    gi, gg, gd = (U.host(gplan[n]).reshape(T, k) for n in ("topk_idx", "topk_gate", "dst_row"))
+    assert np.array_equal(gi, oplan["topk_idx"])
+    for n in ("demand", "kept"):
+        assert np.array_equal(U.host(gplan[n]), oplan[n]), n
+    off = U.host(gplan["offsets"])
+    assert np.array_equal(off, oplan["offsets"])
+    rt = U.host(gplan["row_token"])
+    og, od = oplan["topk_gate"], oplan["dst_row"]
+    differing = 0
+    for e in range(r.E):
+        qs = [(rr * T + t, t, rr) for rr in range(k) for t in range(T) if gi[t, rr] == e]
+        gk = [(q, t, rr) for q, t, rr in qs if gd[t, rr] >= 0]
+        gdrop = [(q, t, rr) for q, t, rr in qs if gd[t, rr] < 0]
+        if gdrop and gk:  # valid under the GPU's own gates
+            lo = min((gg[t, rr], -q) for q, t, rr in gk)
+            hi = max((gg[t, rr], -q) for q, t, rr in gdrop)
+            assert lo > hi, (e, lo, hi)
+        rows = [gd[t, rr] for q, t, rr in sorted(gk)]
+        assert rows == list(range(off[e], off[e] + len(gk))), e
+        for q, t, rr in gk:
+            assert rt[gd[t, rr]] == t
+        okept = {(t, rr) for q, t, rr in qs if od[t, rr] >= 0}
+        diff = okept ^ {(t, rr) for q, t, rr in gk}
+        if diff:
+            cut = sorted((og[t, rr] for q, t, rr in qs), reverse=True)[int(oplan["kept"][e]) - 1]
+            for t, rr in diff:
+                assert abs(og[t, rr] - cut) <= tol * cut, (e, t, rr, og[t, rr], cut)
+            differing += len(diff)
+    print(f"[probs] run {r.name}: {differing} assignments differ from the oracle inside the gate tolerance",
+          flush=True)
+    gates_rel = np.abs(gg.astype(np.float64) - og) / np.maximum(og, 1e-30)
+    assert gates_rel.max() <= U.GATE_REL
+
+
+@pytest.mark.parametrize("name", ["1", "2", "3a", "3b", "3c", "full-3c"])
+def test_probs_drop_policy(gpu, name):
+    r = recipes.RUNS[name[5:]] if name.startswith("full-") else recipes.SMALL[name]
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.drop_policy = 1
+    gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
+    oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), drop_policy=oracle.DROP_PROBS)
+    assert oplan["n_dropped"][0] > 0
+    _check_probs_plan(r, gplan, oplan)
+
+
+def test_probs_drop_policy_ties_and_dropless(gpu):
+    """Repeated token rows give equal gates across tokens, so the position tie-break decides;
+    dropless, probs equals position."""
+    r = recipes.SMALL["3a"].scaled(name="probs-ties", cf=0.5)
+    x = recipes.gen_x(r)
+    x[:] = x[np.arange(r.T) % 37]
+    wg, bias = recipes.gen_router(r)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.drop_policy = 1
+    gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
+    oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), drop_policy=oracle.DROP_PROBS)
+    U.assert_plan_equal(gplan, oplan, "probs ties")
+    rd = r.scaled(name="probs-dropless", dropless=1)
+    cfg = B.MoEConfig.from_run(rd)
+    cfg.drop_policy = 1
+    gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
+    U.assert_plan_equal(gplan, _oracle_route(rd, x, wg, bias), "probs dropless")

@@ -31,7 +31,7 @@ class _Config(ctypes.Structure):
                 ("F", ctypes.c_int32), ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dropless", ctypes.c_int32), ("min_capacity", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_double), ("aux_mode", ctypes.c_int32), ("aux_coeff", ctypes.c_double),
-                ("z_coeff", ctypes.c_double)]
+                ("z_coeff", ctypes.c_double), ("score_fn", ctypes.c_int32), ("drop_policy", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -55,11 +55,13 @@ class MoEConfig:
     aux_mode: int = 0  # 0: every choice / (T*k); 1: first choice / T
     aux_coeff: float = 1e-2
     z_coeff: float = 1e-3
+    score_fn: int = 0  # 0: softmax, 1: sigmoid
+    drop_policy: int = 0  # 0: position, 1: probs
 
     def c(self):
         return _Config(self.T, self.H, self.E, self.k, self.F, self.dtype, self.gate_mode, self.act, self.dropless,
                        self.min_capacity, float(self.capacity_factor), self.aux_mode, float(self.aux_coeff),
-                       float(self.z_coeff))
+                       float(self.z_coeff), self.score_fn, self.drop_policy)
 
     @classmethod
     def from_run(cls, run):

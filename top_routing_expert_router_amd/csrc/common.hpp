@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -102,6 +104,26 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   *total = tmp[nw];
   __syncthreads();
   return ex;
+}
+
+// Gate value of choice r from the chosen logits sv[0..k) (sv[0] the largest) and
+// den: the softmax denominator over all E relative to sv[0] (gate mode 0) or over
+// the chosen (other modes).  With sigmoid scores (kSigmoidFlag in the mode) the
+// gate is the chosen score itself (mode 0) or the score over the chosen scores'
+// sum (mode 1); mode 2 is the softmax over the chosen either way.
+template <int KMAX>
+__device__ __forceinline__ float gate_value(int gate_mode, int k, const float (&sv)[KMAX], float den, int r) {
+  const int gm = gate_mode & (kSigmoidFlag - 1);
+  if ((gate_mode & kSigmoidFlag) && gm != 2) {
+    const float sc = 1.0f / (1.0f + expf(-sv[r]));
+    if (gm == 0) return sc;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) sum += 1.0f / (1.0f + expf(-sv[j]));
+    return sc / sum;
+  }
+  return expf(sv[r] - sv[0]) / den;
 }
 
 // Explicit waits for direct-to-LDS loads (vector memory operations complete in

@@ -6,6 +6,10 @@
 
 namespace moe {
 
+// Added to a moe_gate_mode passed to the router launchers: sigmoid scores
+// instead of softmax (the choices are the same; the gates differ).
+constexpr int kSigmoidFlag = 16;
+
 hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
                                 int H, int E, bool vec_ok, hipStream_t st);
 // Split-bf16 router (bf16 x, H % 64 == 0, 16-byte aligned x): logits with a
@@ -32,8 +36,14 @@ hipError_t launch_router_select(const float* logits, int T, int E, int k, int ga
 // Router training terms from the final logits and choices (see router_losses.hip).
 // Workspace: Ppart [ceil(T/64)][E] f64, Zpart [ceil(T/64)] f64, Cpart [ceil(T/64)][E] int32.
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,
-                                int k, int aux_mode, double aux_coeff, double z_coeff, double* Ppart, double* Zpart,
-                                int32_t* Cpart, double* losses, hipStream_t st);
+                                int k, int score_fn, int aux_mode, double aux_coeff, double z_coeff, double* Ppart,
+                                double* Zpart, int32_t* Cpart, double* losses, hipStream_t st);
+// "probs" drop policy: replaces launch_slot_finalize when a capacity limits.
+// Workspace: lkey, lq, newslot, each [T*k].
+hipError_t launch_slot_probs(const int32_t* base, int Q, int nb, int T, int E, int k, int C, const int32_t* topk_idx,
+                             const float* topk_gate, const int32_t* demand, const int32_t* kept, int32_t* dst_row,
+                             int32_t* row_token, int32_t* offsets, int32_t* n_dropped, int rmax, uint32_t* lkey,
+                             uint32_t* lq, int32_t* newslot, hipStream_t st);
 hipError_t launch_slot_scan(int32_t* hist, int Q, int E, int C, int32_t* demand, int32_t* kept, hipStream_t st);
 hipError_t launch_slot_finalize(const int32_t* base, int Q, int nb, int T, int E, int k, int C,
                                 const int32_t* topk_idx, const int32_t* kept, int32_t* dst_row, int32_t* row_token,

@@ -55,7 +55,7 @@ int effective_capacity(const moe_config* c) {
 struct Layout {
   int nb, Q;
   bool split;  // split-bf16 router buffers present
-  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, lp, lz, lc, route_end, h, ffn_end, total;
+  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, lp, lz, lc, lkey, lq, nslot, route_end, h, ffn_end, total;
 };
 
 // The split-bf16 router runs for bf16 activations with H a multiple of 64 and a
@@ -88,6 +88,12 @@ Layout layout_of(const moe_config* c) {
   L.lz = L.lp + align_up(sizeof(double) * (size_t)L.nb * (size_t)c->E);
   L.lc = L.lz + align_up(sizeof(double) * (size_t)(L.nb > 0 ? L.nb : 1));
   end = L.lc + align_up(sizeof(int32_t) * (size_t)L.nb * (size_t)c->E);
+  // "probs" drop policy: per-assignment key, position and slot
+  const size_t tk = (size_t)c->T * (size_t)c->k;
+  L.lkey = end;
+  L.lq = L.lkey + align_up(sizeof(uint32_t) * tk);
+  L.nslot = L.lq + align_up(sizeof(uint32_t) * tk);
+  end = L.nslot + align_up(sizeof(int32_t) * tk);
   L.route_end = end;
   L.h = 0;
   L.ffn_end = align_up(eb * (size_t)max_rows_of(c) * (size_t)c->F);
@@ -121,6 +127,8 @@ moe_status moe_validate(const moe_config* c) {
   if (!c->dropless && !(c->capacity_factor > 0.0 && isfinite(c->capacity_factor))) return MOE_ERR_INVALID_ARG;
   if (c->aux_mode != MOE_AUX_ALL_CHOICES && c->aux_mode != MOE_AUX_FIRST_CHOICE) return MOE_ERR_INVALID_ARG;
   if (!isfinite(c->aux_coeff) || !isfinite(c->z_coeff)) return MOE_ERR_INVALID_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->drop_policy != MOE_DROP_POSITION && c->drop_policy != MOE_DROP_PROBS) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -166,6 +174,7 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   float* logits = plan->logits ? plan->logits : reinterpret_cast<float*>(w + L.logits);
   const bool bf16 = c->dtype == MOE_BF16;
   const int C = effective_capacity(c);
+  const int gm = c->gate_mode | (c->score_fn == MOE_SCORE_SIGMOID ? moe::kSigmoidFlag : 0);
   hipError_t e;
   if (L.split && aligned16(x)) {
     moe::SplitScratch sc;
@@ -176,7 +185,7 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     sc.pairs = reinterpret_cast<int2*>(w + L.pairs);
     sc.utok = reinterpret_cast<int4*>(w + L.utok);
     sc.count = reinterpret_cast<int*>(w + L.count);
-    if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, c->gate_mode, plan->topk_idx,
+    if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, gm, plan->topk_idx,
                                       plan->topk_gate, sc, st)) != hipSuccess)
       return hip_fail(e, "router_split");
     if ((e = moe::launch_router_rank(plan->topk_idx, c->T, c->E, c->k, L.nb, plan->dst_row, hist, st)) != hipSuccess)
@@ -185,17 +194,26 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
                                        st)) != hipSuccess)
       return hip_fail(e, "router_logits");
-    if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, c->gate_mode, L.nb, plan->topk_idx,
+    if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, gm, L.nb, plan->topk_idx,
                                        plan->topk_gate, plan->dst_row, hist, st)) != hipSuccess)
       return hip_fail(e, "router_select");
   }
   if ((e = moe::launch_slot_scan(hist, L.Q, c->E, C, plan->demand, plan->kept, st)) != hipSuccess)
     return hip_fail(e, "slot_scan");
-  if ((e = moe::launch_slot_finalize(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->kept, plan->dst_row,
-                                     plan->row_token, plan->offsets, plan->n_dropped, (int)max_rows_of(c), st)) != hipSuccess)
+  if (c->drop_policy == MOE_DROP_PROBS && C != INT32_MAX) {
+    if ((e = moe::launch_slot_probs(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->topk_gate,
+                                    plan->demand, plan->kept, plan->dst_row, plan->row_token, plan->offsets,
+                                    plan->n_dropped, (int)max_rows_of(c), reinterpret_cast<uint32_t*>(w + L.lkey),
+                                    reinterpret_cast<uint32_t*>(w + L.lq), reinterpret_cast<int32_t*>(w + L.nslot),
+                                    st)) != hipSuccess)
+      return hip_fail(e, "slot_probs");
+  } else if ((e = moe::launch_slot_finalize(hist, L.Q, L.nb, c->T, c->E, c->k, C, plan->topk_idx, plan->kept,
+                                            plan->dst_row, plan->row_token, plan->offsets, plan->n_dropped,
+                                            (int)max_rows_of(c), st)) != hipSuccess) {
     return hip_fail(e, "slot_finalize");
+  }
   if (plan->losses &&
-      (e = moe::launch_router_losses(logits, plan->topk_idx, plan->demand, c->T, c->E, c->k, c->aux_mode,
+      (e = moe::launch_router_losses(logits, plan->topk_idx, plan->demand, c->T, c->E, c->k, c->score_fn, c->aux_mode,
                                      c->aux_coeff, c->z_coeff, reinterpret_cast<double*>(w + L.lp),
                                      reinterpret_cast<double*>(w + L.lz), reinterpret_cast<int32_t*>(w + L.lc),
                                      plan->losses, st)) != hipSuccess)

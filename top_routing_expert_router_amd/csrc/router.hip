@@ -275,7 +275,7 @@ __global__ void __launch_bounds__(64) router_select_kernel(const float* __restri
   const float m = tv[0];
   float den = 0.0f;
   if (valid) {
-    if (gate_mode == 0) {  // softmax over all E, no renormalisation
+    if (gate_mode == 0) {  // softmax scores over all E, no renormalisation
       if (vec) {
         for (int e = 0; e < E; e += 4) {
           f32x4_t v = *reinterpret_cast<const f32x4_t*>(l + e);
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(64) router_select_kernel(const float* __restri
     for (int r = 0; r < KMAX; ++r) {
       if (r < k) {
         topk_idx[(size_t)t * k + r] = ti[r];
-        topk_gate[(size_t)t * k + r] = expf(tv[r] - m) / den;
+        topk_gate[(size_t)t * k + r] = gate_value<KMAX>(gate_mode, k, tv, den, r);
       }
     }
   }

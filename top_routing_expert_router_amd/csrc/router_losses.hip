@@ -3,7 +3,8 @@
 // explainer, router section: the auxiliary-loss and z-loss paragraphs; Switch
 // Transformers explainer, "Load balance & capacity").
 //
-// P_e is the mean over tokens of softmax(l_t)_e; f_e is demand_e / (T k)
+// P_e is the mean over tokens of softmax(l_t)_e (sigmoid scoring: the token's
+// sigmoid scores over their sum); f_e is demand_e / (T k)
 // (aux_mode 0: every choice counts, k in the denominator) or the fraction of
 // tokens whose first choice is e (aux_mode 1, DeepSpeed's top-2 path).  Both are
 // computed from the routing's fp32 logits after the choices are final.
@@ -22,7 +23,7 @@ namespace moe {
 template <int JE>
 __global__ void __launch_bounds__(256) router_loss_partial_kernel(const float* __restrict__ logits,
                                                                   const int32_t* __restrict__ topk_idx, int T, int E,
-                                                                  int k, double* __restrict__ Ppart,
+                                                                  int k, int score_fn, double* __restrict__ Ppart,
                                                                   double* __restrict__ Zpart,
                                                                   int32_t* __restrict__ Cpart) {
   __shared__ double s_p[4][64 * JE];
@@ -59,8 +60,21 @@ __global__ void __launch_bounds__(256) router_loss_partial_kernel(const float* _
     }
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
+    if (score_fn) {  // sigmoid scores over their sum
+      float sc[JE], ssum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < JE; ++j) acc[j] += (double)(ex[j] / den);
+      for (int j = 0; j < JE; ++j) {
+        sc[j] = lane + 64 * j < E ? 1.0f / (1.0f + expf(-v[j])) : 0.0f;
+        ssum += sc[j];
+      }
+#pragma unroll
+      for (int d = 32; d > 0; d >>= 1) ssum += __shfl_xor(ssum, d, 64);
+#pragma unroll
+      for (int j = 0; j < JE; ++j) acc[j] += (double)(sc[j] / ssum);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JE; ++j) acc[j] += (double)(ex[j] / den);
+    }
     const double lse = (double)m + (double)logf(den);
     z += lse * lse;
     const int first = topk_idx[(size_t)t * k];
@@ -123,13 +137,14 @@ __global__ void __launch_bounds__(256) router_loss_final_kernel(const double* __
 }
 
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,
-                                int k, int aux_mode, double aux_coeff, double z_coeff, double* Ppart, double* Zpart,
-                                int32_t* Cpart, double* losses, hipStream_t st) {
+                                int k, int score_fn, int aux_mode, double aux_coeff, double z_coeff, double* Ppart,
+                                double* Zpart, int32_t* Cpart, double* losses, hipStream_t st) {
   const int nb = (T + 63) / 64;
   if (nb > 0) {
     const int je = (E + 63) / 64;
 #define MOE_LP(J) \
-  router_loss_partial_kernel<J><<<dim3(nb), dim3(256), 0, st>>>(logits, topk_idx, T, E, k, Ppart, Zpart, Cpart)
+  router_loss_partial_kernel<J><<<dim3(nb), dim3(256), 0, st>>>(logits, topk_idx, T, E, k, score_fn, Ppart, Zpart, \
+                                                                Cpart)
     if (je <= 1) MOE_LP(1);
     else if (je <= 2) MOE_LP(2);
     else if (je <= 4) MOE_LP(4);

@@ -157,7 +157,8 @@ __device__ __forceinline__ void group_topk(const float (&v)[JE], const float (&l
 }
 
 // Gates of the chosen experts (gate_mode 0: softmax over all E; otherwise the
-// softmax over the k chosen); choice r is written by lane r % G of the group.
+// softmax over the k chosen; kSigmoidFlag: sigmoid scores, see gate_value);
+// choice r is written by lane r % G of the group.
 template <int G, int JE, int KMAX>
 __device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, int gate_mode, const int (&se)[KMAX],
                                             const float (&sv)[KMAX], int t, bool active,
@@ -165,7 +166,7 @@ __device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, 
   const int lg = threadIdx.x & (G - 1);
   const float m = sv[0];
   float den = 0.0f;
-  if (gate_mode == 0) {
+  if (gate_mode == 0) {  // softmax scores, no renormalisation
 #pragma unroll
     for (int j = 0; j < JE; ++j)
       if (lg + G * j < E) den += expf(v[j] - m);
@@ -181,7 +182,7 @@ __device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, 
   for (int r = 0; r < KMAX; ++r)
     if (r < k && (r & (G - 1)) == lg) {  // every choice r < k has a writer, also when G < k
       topk_idx[(size_t)t * k + r] = se[r];
-      topk_gate[(size_t)t * k + r] = expf(sv[r] - m) / den;
+      topk_gate[(size_t)t * k + r] = gate_value<KMAX>(gate_mode, k, sv, den, r);
     }
 }
 
