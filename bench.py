@@ -266,6 +266,47 @@ def main():
         for i, s in enumerate(stages):
             acc[s] += ev[i].elapsed_time(ev[i + 1])
     stage_us = {s: acc[s] / args.steps * 1e3 for s in stages}
+
+    # ---- router training terms (load-balancing loss, z-loss): route with the
+    # optional losses output, against route without it
+    plan_l = dict(plan)
+    plan_l["losses"] = torch.empty(2, dtype=torch.float64, device=dev)
+    el = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_plain = t_loss = 0.0
+    for _ in range(args.steps):
+        el[0].record()
+        B.route(cfg, x, wg, bias, plan, ws)
+        el[1].record()
+        B.route(cfg, x, wg, bias, plan_l, ws)
+        el[2].record()
+        torch.cuda.synchronize()
+        t_plain += el[0].elapsed_time(el[1])
+        t_loss += el[1].elapsed_time(el[2])
+    losses_us = {"route_us": round(t_plain / args.steps * 1e3, 2),
+                 "route_with_losses_us": round(t_loss / args.steps * 1e3, 2),
+                 "losses": [float(v) for v in plan_l["losses"].cpu().tolist()]}
+
+    # ---- routing variants: "probs" drop policy and sigmoid scores, route alone
+    def route_time(c):
+        ws_c = B.alloc_workspace(c, dev)
+        plan_c = B.alloc_plan(c, dev)
+        B.route(c, x, wg, bias, plan_c, ws_c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            B.route(c, x, wg, bias, plan_c, ws_c)
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / args.steps * 1e3, 2), int(plan_c["n_dropped"].item())
+
+    variants = {}
+    for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
+        c = B.MoEConfig.from_run(run)
+        for key, val in kw.items():
+            setattr(c, key, val)
+        us, nd = route_time(c)
+        variants[name] = {"route_us": us, "dropped": nd}
     log("[bench] stages (us): " + ", ".join(f"{s}={v:.1f}" for s, v in stage_us.items()))
 
     # ---- algorithmic work per step (from the plan of this batch)
@@ -350,6 +391,8 @@ def main():
                                     "dispatch": stages_out["dispatch"]["hbm_frac"],
                                     "combine": stages_out["combine"]["hbm_frac"]},
         "stages": stages_out,
+        "router_training_terms": losses_us,
+        "routing_variants": variants,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

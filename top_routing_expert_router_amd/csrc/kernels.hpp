@@ -34,7 +34,7 @@ hipError_t launch_router_rank(const int32_t* topk_idx, int T, int E, int k, int 
 hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, int nb, int32_t* topk_idx,
                                 float* topk_gate, int32_t* dst_rank, int32_t* hist, hipStream_t st);
 // Router training terms from the final logits and choices (see router_losses.hip).
-// Workspace: Ppart [ceil(T/64)][E] f64, Zpart [ceil(T/64)] f64, Cpart [ceil(T/64)][E] int32.
+// Workspace: Ppart [E][ceil(T/64)] f64, Zpart [ceil(T/64)] + fP [E+1] f64, Cpart [E][ceil(T/64)] int32.
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,
                                 int k, int score_fn, int aux_mode, double aux_coeff, double z_coeff, double* Ppart,
                                 double* Zpart, int32_t* Cpart, double* losses, hipStream_t st);

@@ -86,7 +86,7 @@ Layout layout_of(const moe_config* c) {
   // router training terms: per-64-token-block partial sums
   L.lp = end;
   L.lz = L.lp + align_up(sizeof(double) * (size_t)L.nb * (size_t)c->E);
-  L.lc = L.lz + align_up(sizeof(double) * (size_t)(L.nb > 0 ? L.nb : 1));
+  L.lc = L.lz + align_up(sizeof(double) * ((size_t)(L.nb > 0 ? L.nb : 1) + (size_t)c->E + 1));
   end = L.lc + align_up(sizeof(int32_t) * (size_t)L.nb * (size_t)c->E);
   // "probs" drop policy: per-assignment key, position and slot
   const size_t tk = (size_t)c->T * (size_t)c->k;

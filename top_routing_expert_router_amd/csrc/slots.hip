@@ -206,14 +206,18 @@ __global__ void __launch_bounds__(256) slot_probs_kernel(const int32_t* __restri
       if ((kj & mask) == prefix) atomicAdd(&s_hist[(kj >> shift) & 0xFF], 1);
     }
     __syncthreads();
-    if (tid == 0) {  // bucket holding the need-th largest among the candidates
-      int need = s_need, b = 255;
-      for (; b > 0; --b) {
-        if (s_hist[b] >= need) break;
-        need -= s_hist[b];
+    {  // bucket holding the need-th largest among the candidates: counts from the
+       // top (thread i holds bucket 255 - i); exactly one bucket brackets need
+      const int b = 255 - tid;
+      const int h = s_hist[b];
+      int above_total;
+      const int above = block_exclusive_scan(h, s_tmp, &above_total);  // candidates in buckets > b
+      const int need = s_need;
+      __syncthreads();
+      if (above < need && above + h >= need) {
+        s_need = need - above;
+        s_prefix = prefix | ((uint64_t)b << shift);
       }
-      s_need = need;
-      s_prefix = prefix | ((uint64_t)b << shift);
     }
     mask |= (uint64_t)0xFF << shift;
     __syncthreads();
