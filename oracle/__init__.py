@@ -19,6 +19,7 @@ SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
 RELU, GELU, SWIGLU = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1
 DROP_POSITION, DROP_PROBS = 0, 1
+SECOND_ALWAYS, SECOND_RANDOM = 0, 1
 
 _lib = None
 
@@ -44,7 +45,7 @@ def lib():
         L.oracle_logits.restype = None
         L.oracle_logits.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp]
         L.oracle_route_from_logits.restype = i64
-        L.oracle_route_from_logits.argtypes = [i64, i64, i32, i32, i32, i32, i64, vp] + [vp] * 8
+        L.oracle_route_from_logits.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, i64, vp] + [vp] * 8
         L.oracle_dispatch.restype = None
         L.oracle_router_losses.restype = None
         L.oracle_router_losses.argtypes = [i64, i64, i32, i32, vp, vp, vp, i32, dbl, dbl, vp]
@@ -93,8 +94,9 @@ def logits(x, dtype, wg, bias=None):
     return out
 
 
-def route_from_logits(lg, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION):
-    """C: capacity, or None for dropless.  Returns the routing plan as numpy arrays."""
+def route_from_logits(lg, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION, second_u=None):
+    """C: capacity, or None for dropless; second_u: uniforms [T] for GShard's random second
+    choice (k = 2), or None.  Returns the routing plan as numpy arrays."""
     lg = _c(lg, np.float32)
     T, E = lg.shape
     Cc = -1 if C is None else int(C)
@@ -109,7 +111,9 @@ def route_from_logits(lg, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_PO
         row_token=np.full(max(tk, 1), -1, np.int32),
         n_dropped=np.zeros(1, np.int32),
     )
-    R = lib().oracle_route_from_logits(T, E, k, gate_mode, score_fn, drop_policy, Cc, _p(lg), *[_p(plan[n]) for n in (
+    su = None if second_u is None else _c(second_u, np.float32)
+    R = lib().oracle_route_from_logits(T, E, k, gate_mode, score_fn, drop_policy, 0 if su is None else 1,
+                                       None if su is None else _p(su), Cc, _p(lg), *[_p(plan[n]) for n in (
         "topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets", "row_token", "n_dropped")])
     if R < 0:
         raise ValueError("bad routing arguments")
@@ -130,9 +134,9 @@ def router_losses(logits, topk_idx, demand, k, aux_mode=0, aux_coeff=1.0, z_coef
     return float(out[0]), float(out[1])
 
 
-def route(x, dtype, wg, bias, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION):
+def route(x, dtype, wg, bias, k, gate_mode, C, score_fn=SOFTMAX, drop_policy=DROP_POSITION, second_u=None):
     lg = logits(x, dtype, wg, bias)
-    plan = route_from_logits(lg, k, gate_mode, C, score_fn, drop_policy)
+    plan = route_from_logits(lg, k, gate_mode, C, score_fn, drop_policy, second_u)
     plan["logits"] = lg
     return plan
 
@@ -205,9 +209,9 @@ def token_outputs(tokens, x, dtype, act, plan, w1, w3, w2, residual=None):
 
 
 def forward(x, dtype, wg, bias, w1, w3, w2, k, gate_mode, act, C, residual=None, score_fn=SOFTMAX,
-            drop_policy=DROP_POSITION):
+            drop_policy=DROP_POSITION, second_u=None):
     """Whole layer: route -> dispatch -> expert FFN -> combine.  Returns (y float64, plan, X, Y)."""
-    plan = route(x, dtype, wg, bias, k, gate_mode, C, score_fn, drop_policy)
+    plan = route(x, dtype, wg, bias, k, gate_mode, C, score_fn, drop_policy, second_u)
     X = dispatch(x, dtype, plan)
     Y = expert_ffn(X, plan["offsets"], dtype, act, w1, w3, w2)
     y = combine(Y, plan, dtype, residual)

@@ -44,6 +44,7 @@ enum { OR_SOFTMAX_TOPK = 0, OR_SOFTMAX_TOPK_RENORM = 1, OR_TOPK_SOFTMAX = 2 };
 enum { OR_RELU = 0, OR_GELU = 1, OR_SWIGLU = 2 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_DROP_POSITION = 0, OR_DROP_PROBS = 1 };
+enum { OR_SECOND_ALWAYS = 0, OR_SECOND_RANDOM = 1 };
 
 /* A bf16 number is the upper half of an IEEE binary32; its value is exact in binary64. */
 static double bf16_to_double(uint16_t b) {
@@ -152,6 +153,11 @@ static void gates(const float *l, int64_t E, int k, int mode, int score, const i
  *     assignments at the end of the batch; over-capacity assignments skip the
  *     expert): walk q = 0 .. T*k-1 with r = q / T, t = q % T; the assignment
  *     (t, r) to e = idx takes slot n_e, then n_e += 1; it is kept iff slot < C.
+ *   - GShard second choice ([EP] router: top-2, the second expert taken at random
+ *     by its weight; rule read as GShard's: with k = 2 and gates g1, g2, the
+ *     second assignment exists iff u_t * (g1 + g2) < 2 * g2 for the caller's
+ *     uniform u_t, in binary64 on the fp32 gates); an absent assignment takes no
+ *     slot, is not counted in demand and gets dst_row -1;
  *   - "probs" policy ([EP]: drop the lowest-probability ones): per expert, the C
  *     assignments with the largest gate value are kept (equal gates: the earlier
  *     q first); the kept ones take slots in q order.
@@ -166,11 +172,12 @@ static int cmp_probs(const void *a, const void *b) {
   return x[1] < y[1] ? -1 : (x[1] > y[1] ? 1 : 0);
 }
 
-int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int score_fn, int drop_policy, int64_t C,
-                                 const float *logits, int32_t *topk_idx, float *topk_gate, int32_t *dst_row,
-                                 int32_t *demand, int32_t *kept, int32_t *offsets, int32_t *row_token,
-                                 int32_t *n_dropped) {
+int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int score_fn, int drop_policy,
+                                 int second_policy, const float *second_u, int64_t C, const float *logits,
+                                 int32_t *topk_idx, float *topk_gate, int32_t *dst_row, int32_t *demand, int32_t *kept,
+                                 int32_t *offsets, int32_t *row_token, int32_t *n_dropped) {
   if (k < 1 || k > 16 || k > E || T < 0) return -1;
+  if (second_policy == OR_SECOND_RANDOM && (k != 2 || !second_u)) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     select_topk(logits + t * E, E, k, topk_idx + t * k);
@@ -178,9 +185,16 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
   }
   int64_t *n = (int64_t *)calloc((size_t)E, sizeof(int64_t));
   int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k > 0 ? T * k : 1));
+  char *absent = (char *)calloc((size_t)(T * k > 0 ? T * k : 1), 1);
+  if (second_policy == OR_SECOND_RANDOM)
+    for (int64_t t = 0; t < T; ++t) {
+      const double g1 = topk_gate[t * 2], g2 = topk_gate[t * 2 + 1];
+      absent[t * 2 + 1] = !((double)second_u[t] * (g1 + g2) < 2.0 * g2);
+    }
   for (int64_t q = 0; q < T * k; ++q) {
     int64_t r = q / T, t = q % T;
     int32_t e = topk_idx[t * k + r];
+    if (absent[t * k + r]) continue;
     slot[t * k + r] = n[e];
     n[e] += 1;
   }
@@ -194,7 +208,7 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
       int64_t m = 0;
       for (int64_t q = 0; q < T * k; ++q) {
         const int64_t ch = q / T, tok = q % T; /* choice-major position q */
-        if (topk_idx[tok * k + ch] == (int32_t)e) {
+        if (topk_idx[tok * k + ch] == (int32_t)e && !absent[tok * k + ch]) {
           ent[2 * m] = (double)topk_gate[tok * k + ch];
           ent[2 * m + 1] = (double)q;
           ++m;
@@ -208,7 +222,8 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
       int64_t next = 0;
       for (int64_t q = 0; q < T * k; ++q) {
         const int64_t ch = q / T, tok = q % T;
-        if (topk_idx[tok * k + ch] == (int32_t)e) slot[tok * k + ch] = keep[tok * k + ch] ? next++ : C;
+        if (topk_idx[tok * k + ch] == (int32_t)e && !absent[tok * k + ch])
+          slot[tok * k + ch] = keep[tok * k + ch] ? next++ : C;
       }
     }
     free(ent);
@@ -224,7 +239,7 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
     for (int r = 0; r < k; ++r) {
       int64_t i = t * k + r;
       int32_t e = topk_idx[i];
-      if (C < 0 || slot[i] < C) {
+      if (!absent[i] && (C < 0 || slot[i] < C)) {
         dst_row[i] = (int32_t)(offsets[e] + slot[i]);
         row_token[dst_row[i]] = (int32_t)t;
       } else {
@@ -234,6 +249,7 @@ int64_t oracle_route_from_logits(int64_t T, int64_t E, int k, int gate_mode, int
   *n_dropped = (int32_t)(T * k - offsets[E]);
   free(n);
   free(slot);
+  free(absent);
   return offsets[E];
 }
 

@@ -16,7 +16,7 @@ MUTANTS = {
     "tie_break_to_higher_index": ("l[e] > l[best]", "l[e] >= l[best]"),
     "token_major_priority": ("int64_t r = q / T, t = q % T;", "int64_t t = q / k, r = q % k;"),
     "capacity_floor": ("double c = ceil(", "double c = floor("),
-    "keep_one_past_capacity": ("if (C < 0 || slot[i] < C) {", "if (C < 0 || slot[i] <= C) {"),
+    "keep_one_past_capacity": ("if (!absent[i] && (C < 0 || slot[i] < C)) {", "if (!absent[i] && (C < 0 || slot[i] <= C)) {"),
     "softmax_over_selected_only": ("for (int64_t e = 0; e < E; ++e) den += exp((double)l[e] - m);",
                                    "for (int j = 0; j < k; ++j) den += exp((double)l[idx[j]] - m);"),
     "router_transposed": ("acc[e] += xv * (double)w[e];", "acc[e] += xv * (double)Wg[e * H + h];"),
@@ -30,6 +30,8 @@ MUTANTS = {
     "probs_tie_to_later": ("return x[1] < y[1] ? -1 : (x[1] > y[1] ? 1 : 0);", "return x[1] > y[1] ? -1 : (x[1] < y[1] ? 1 : 0);"),
     "sigmoid_sign": ("sc[r] = 1.0 / (1.0 + exp(-(double)l[idx[r]]));", "sc[r] = 1.0 / (1.0 + exp((double)l[idx[r]]));"),
     "sigmoid_not_renormalised": ("g[r] = (float)(mode == OR_SOFTMAX_TOPK ? sc[r] : sc[r] / sum);", "g[r] = (float)(sc[r]);"),
+    "second_rule_without_2": ("absent[t * 2 + 1] = !((double)second_u[t] * (g1 + g2) < 2.0 * g2);", "absent[t * 2 + 1] = !((double)second_u[t] * (g1 + g2) < g2);"),
+    "second_rule_reversed": ("absent[t * 2 + 1] = !((double)second_u[t] * (g1 + g2) < 2.0 * g2);", "absent[t * 2 + 1] = ((double)second_u[t] * (g1 + g2) < 2.0 * g2);"),
     "aux_without_k": ("f = (double)demand[e] / ((double)T * (double)k);", "f = (double)demand[e] / (double)T;"),
     "aux_without_E": ("out[0] = aux_coeff * (double)E * dot;", "out[0] = aux_coeff * dot;"),
     "zloss_not_squared": ("zsum += lse * lse;", "zsum += lse;"),
@@ -59,6 +61,7 @@ PINS = [
     lambda: P.test_probs_policy_hand_example(),
     lambda: P.test_probs_policy_keeps_largest_gates(0),
     lambda: P.test_probs_policy_equal_gates_is_position_policy(),
+    lambda: P.test_gshard_second_choice_rule(),
 ]
 
 

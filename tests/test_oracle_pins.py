@@ -622,3 +622,37 @@ def test_probs_policy_keeps_largest_gates(mode):
     a = oracle.route_from_logits(lg, k, mode, None, drop_policy=oracle.DROP_PROBS)
     b = oracle.route_from_logits(lg, k, mode, None, drop_policy=oracle.DROP_POSITION)
     assert np.array_equal(a["dst_row"], b["dst_row"])
+
+
+def _second_logits(T, ratio):
+    """T tokens, E = 6: expert 2 leads, expert 4 second with gate ratio g2/g1 = ratio."""
+    lg = np.full((T, 6), -4.0, np.float32)
+    lg[:, 2] = 1.0
+    lg[:, 4] = 1.0 + np.log(ratio)
+    return lg
+
+
+def test_gshard_second_choice_rule():
+    """[EP] router: GShard sends the second choice at random by its weight; with the gates
+    renormalised over the pair, p(second) = 2 g2 / (g1 + g2).  Gates 3/4, 1/4 (ratio 1/3):
+    threshold 1/2.  u = 0 keeps every second choice, u -> 1 none."""
+    T = 4
+    lg = _second_logits(T, 1 / 3)
+    u = np.array([0.49, 0.51, 0.0, 0.999999], np.float32)
+    p = oracle.route_from_logits(lg, 2, oracle.SOFTMAX_TOPK_RENORM, None, second_u=u)
+    assert np.allclose(p["topk_gate"], [[0.75, 0.25]] * T, rtol=1e-6)
+    assert list(p["dst_row"][:, 1] >= 0) == [True, False, True, False]
+    assert list(p["demand"]) == [0, 0, 4, 0, 2, 0] and p["n_dropped"][0] == 2
+    full = oracle.route_from_logits(lg, 2, oracle.SOFTMAX_TOPK_RENORM, None)
+    p0 = oracle.route_from_logits(lg, 2, oracle.SOFTMAX_TOPK_RENORM, None, second_u=np.zeros(T, np.float32))
+    for n in ("dst_row", "demand", "offsets", "row_token"):
+        assert np.array_equal(p0[n], full[n])
+
+
+def test_gshard_second_choice_frequency():
+    """With g2 / (g1 + g2) = 1/4 the second choice is taken with probability 1/2."""
+    T = 20000
+    u = np.random.default_rng(12).random(T).astype(np.float32)
+    p = oracle.route_from_logits(_second_logits(T, 1 / 3), 2, oracle.SOFTMAX_TOPK_RENORM, None, second_u=u)
+    frac = float((p["dst_row"][:, 1] >= 0).mean())
+    assert abs(frac - 0.5) < 0.015
