@@ -107,6 +107,15 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
  *             position order.  Same as POSITION when nothing is dropped. */
 typedef enum { MOE_DROP_POSITION = 0, MOE_DROP_PROBS = 1 } moe_drop_policy;
 
+/* Second choice with k = 2 ([EP] router: GShard uses top-2 and sends a token
+ * to its second expert at random, by that expert's weight):
+ *   ALWAYS  plain top-k
+ *   RANDOM  the second assignment exists iff u_t * (g1 + g2) < 2 * g2 (binary64
+ *           on the fp32 gates; GShard's rule), u_t from plan->second_u; an
+ *           absent assignment takes no slot, is not counted in demand, gets
+ *           dst_row -1, and the first gate is not renormalised. */
+typedef enum { MOE_SECOND_ALWAYS = 0, MOE_SECOND_RANDOM = 1 } moe_second_policy;
+
 typedef struct {
   int32_t T;              /* tokens, >= 0 (T = 0 is a valid no-op)            */
   int32_t H;              /* hidden size, >= 1                                 */
@@ -124,6 +133,7 @@ typedef struct {
   double z_coeff;         /* coefficient of the z-loss, finite                 */
   int32_t score_fn;       /* moe_score_fn                                       */
   int32_t drop_policy;    /* moe_drop_policy                                    */
+  int32_t second_policy;  /* moe_second_policy (RANDOM requires k = 2)         */
 } moe_config;
 
 /* Routing plan: device arrays, allocated by the caller, written by moe_route. */
@@ -141,6 +151,9 @@ typedef struct {
                        *         [0] = aux_coeff * E * sum_e f_e P_e   (load balancing, moe_aux_mode)
                        *         [1] = z_coeff * mean_t logsumexp(logits_t)^2   (z-loss)
                        *         ([EP] router section: auxiliary-loss and z-loss paragraphs)        */
+  const float *second_u; /* [T] input: uniforms in [0, 1) for MOE_SECOND_RANDOM (the caller draws
+                          *     them: the library consumes random numbers, it does not make them);
+                          *     required iff second_policy is RANDOM and T > 0                     */
 } moe_plan;
 
 /* ---- host-only helpers (no HIP call; usable without a GPU) ------------------ */
@@ -178,7 +191,8 @@ const char *moe_last_error(void);
  * experts that decide a choice and within ~1e-7 relative of them otherwise.
  * With plan->losses set, also the router training terms (see moe_plan).
  * x: device [T][H] dtype.  Wg: device [H][E] fp32.  bias: device [E] fp32 or NULL.
- * plan: every pointer but logits and losses required.  ws: device, >= moe_workspace_bytes. */
+ * plan: every pointer but logits, losses and second_u required (second_u: see
+ * moe_second_policy).  ws: device, >= moe_workspace_bytes. */
 moe_status moe_route(const moe_config *cfg, const void *x, const float *Wg, const float *bias,
                      const moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
 

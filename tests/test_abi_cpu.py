@@ -46,6 +46,7 @@ def _cfg(**kw):
     dict(capacity_factor=0.0), dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")),
     dict(capacity_factor=float("inf")), dict(aux_mode=2), dict(aux_mode=-1), dict(aux_coeff=float("nan")),
     dict(z_coeff=float("inf")), dict(score_fn=2), dict(drop_policy=2), dict(drop_policy=-1),
+    dict(second_policy=2), dict(second_policy=1, k=1), dict(second_policy=1, k=3),
 ])
 def test_validate_rejects(kw):
     c = _cfg(**kw)

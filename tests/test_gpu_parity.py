@@ -549,3 +549,63 @@ def test_probs_drop_policy_ties_and_dropless(gpu):
     cfg.drop_policy = 1
     gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
     U.assert_plan_equal(gplan, _oracle_route(rd, x, wg, bias), "probs dropless")
+
+
+def _second_u(r, x, wg, bias, seed):
+    """Seeded uniforms for GShard's second choice, moved out of the band where the fp32 gates
+    of the two sides (which may differ in the last bit) could decide differently."""
+    u = np.random.default_rng(seed).random(r.T).astype(np.float32)
+    g = _oracle_route(r, x, wg, bias)["topk_gate"].astype(np.float64)
+    s = g[:, 0] + g[:, 1]
+    near = np.abs(u * s - 2 * g[:, 1]) <= 1e-5 * s
+    u[near] = np.minimum(u[near] + 1e-3, 0.999).astype(np.float32)
+    return u
+
+
+@pytest.mark.parametrize("name", ["4", "3a-k2", "2-k2", "1-k2"])
+def test_gshard_random_second_choice(gpu, name):
+    base = {"4": recipes.SMALL["4"], "3a-k2": recipes.SMALL["3a"].scaled(name="3a-k2", k=2),
+            "2-k2": recipes.SMALL["2"].scaled(name="2-k2", k=2, gate_mode=recipes.SOFTMAX_TOPK_RENORM),
+            "1-k2": recipes.RUNS["1"].scaled(name="1-k2", k=2, T=500)}[name]
+    r = base
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    u = _second_u(r, x, wg, bias, 21)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.second_policy = 1
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    plan["second_u"] = U.dev(u, gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    import torch
+
+    B.route(cfg, U.dev(x, gpu), U.dev(wg, gpu), U.dev(bias, gpu), plan, ws)
+    torch.cuda.synchronize()
+    oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), second_u=u)
+    absent = int((oplan["dst_row"][:, 1] < 0).sum())
+    print(f"[gshard] run {r.name}: {absent} of {r.T} second choices not taken", flush=True)
+    assert 0 < absent < r.T
+    _check_route(r, plan, oplan)
+
+
+def test_gshard_random_second_choice_forward(gpu):
+    import torch
+
+    r = recipes.SMALL["4"].scaled(name="gshard-fwd", dropless=0, cf=1.0)
+    d = recipes.gen_all(r)
+    u = _second_u(r, d["x"], d["wg"], d["bias"], 5)
+    yref, oplan, _, _ = oracle.forward(d["x"], r.dtype, d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], r.k,
+                                       r.gate_mode, r.act, _cap(r), second_u=u)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.second_policy = 1
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    plan["second_u"] = U.dev(u, gpu)
+    rmax = max(B.max_rows(cfg), 1)
+    X = torch.empty((rmax, r.H), dtype=torch.bfloat16, device=gpu)
+    Y = torch.empty_like(X)
+    y = torch.empty((r.T, r.H), dtype=torch.bfloat16, device=gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.forward(cfg, U.dev(d["x"], gpu), U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), U.dev(d["w1"], gpu),
+              U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), None, y, plan, X, Y, ws)
+    torch.cuda.synchronize()
+    _check_route(r, plan, oplan)
+    U.assert_close(U.host(y), yref, True, "gshard forward")

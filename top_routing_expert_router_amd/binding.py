@@ -31,12 +31,13 @@ class _Config(ctypes.Structure):
                 ("F", ctypes.c_int32), ("dtype", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("dropless", ctypes.c_int32), ("min_capacity", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_double), ("aux_mode", ctypes.c_int32), ("aux_coeff", ctypes.c_double),
-                ("z_coeff", ctypes.c_double), ("score_fn", ctypes.c_int32), ("drop_policy", ctypes.c_int32)]
+                ("z_coeff", ctypes.c_double), ("score_fn", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
+                ("second_policy", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets",
-                                               "row_token", "n_dropped", "logits", "losses")]
+                                               "row_token", "n_dropped", "logits", "losses", "second_u")]
 
 
 @dataclass
@@ -57,11 +58,12 @@ class MoEConfig:
     z_coeff: float = 1e-3
     score_fn: int = 0  # 0: softmax, 1: sigmoid
     drop_policy: int = 0  # 0: position, 1: probs
+    second_policy: int = 0  # 0: plain top-k, 1: GShard's random second choice (k = 2, plan["second_u"])
 
     def c(self):
         return _Config(self.T, self.H, self.E, self.k, self.F, self.dtype, self.gate_mode, self.act, self.dropless,
                        self.min_capacity, float(self.capacity_factor), self.aux_mode, float(self.aux_coeff),
-                       float(self.z_coeff), self.score_fn, self.drop_policy)
+                       float(self.z_coeff), self.score_fn, self.drop_policy, self.second_policy)
 
     @classmethod
     def from_run(cls, run):
@@ -148,7 +150,7 @@ def workspace_bytes(cfg: MoEConfig):
 
 def _plan_struct(plan):
     return _Plan(*[_ptr(plan.get(n)) for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets",
-                                               "row_token", "n_dropped", "logits", "losses")])
+                                               "row_token", "n_dropped", "logits", "losses", "second_u")])
 
 
 def alloc_plan(cfg: MoEConfig, device, logits=False, losses=False):

@@ -126,6 +126,13 @@ __device__ __forceinline__ float gate_value(int gate_mode, int k, const float (&
   return expf(sv[r] - sv[0]) / den;
 }
 
+// GShard's random second choice ("Expert-parallel MoE training" explainer,
+// router: top-2 with the second expert taken at random by its weight): taken iff
+// u * (g1 + g2) < 2 * g2, in binary64 on the fp32 gates.
+__device__ __forceinline__ bool second_choice_taken(float u, float g1, float g2) {
+  return (double)u * ((double)g1 + (double)g2) < 2.0 * (double)g2;
+}
+
 // Explicit waits for direct-to-LDS loads (vector memory operations complete in
 // issue order, so `vmcnt <= N` means all but the last N issued have landed).
 template <int N>

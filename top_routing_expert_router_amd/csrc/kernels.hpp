@@ -10,6 +10,10 @@ namespace moe {
 // instead of softmax (the choices are the same; the gates differ).
 constexpr int kSigmoidFlag = 16;
 
+// dst_row value the rank step leaves for an absent choice (GShard's second
+// choice not taken); the finalize steps turn it into -1.
+constexpr int32_t kAbsentChoice = INT32_MIN;
+
 hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
                                 int H, int E, bool vec_ok, hipStream_t st);
 // Split-bf16 router (bf16 x, H % 64 == 0, 16-byte aligned x): logits with a
@@ -29,10 +33,11 @@ int split_router_hs(int H);
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
                                int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
                                hipStream_t st);
-hipError_t launch_router_rank(const int32_t* topk_idx, int T, int E, int k, int nb, int32_t* dst_rank, int32_t* hist,
-                              hipStream_t st);
-hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, int nb, int32_t* topk_idx,
-                                float* topk_gate, int32_t* dst_rank, int32_t* hist, hipStream_t st);
+hipError_t launch_router_rank(const int32_t* topk_idx, const float* topk_gate, const float* second_u, int T, int E,
+                              int k, int nb, int32_t* dst_rank, int32_t* hist, hipStream_t st);
+hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, const float* second_u,
+                                int nb, int32_t* topk_idx, float* topk_gate, int32_t* dst_rank, int32_t* hist,
+                                hipStream_t st);
 // Router training terms from the final logits and choices (see router_losses.hip).
 // Workspace: Ppart [E][ceil(T/64)] f64, Zpart [ceil(T/64)] + fP [E+1] f64, Cpart [E][ceil(T/64)] int32.
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,

@@ -129,6 +129,8 @@ moe_status moe_validate(const moe_config* c) {
   if (!isfinite(c->aux_coeff) || !isfinite(c->z_coeff)) return MOE_ERR_INVALID_ARG;
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (c->drop_policy != MOE_DROP_POSITION && c->drop_policy != MOE_DROP_PROBS) return MOE_ERR_INVALID_ARG;
+  if (c->second_policy != MOE_SECOND_ALWAYS && c->second_policy != MOE_SECOND_RANDOM) return MOE_ERR_INVALID_ARG;
+  if (c->second_policy == MOE_SECOND_RANDOM && c->k != 2) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -166,6 +168,8 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   if (s != MOE_OK) return s;
   if ((s = check_plan(c, plan)) != MOE_OK) return s;
   if ((c->T > 0 && !x) || !Wg) return MOE_ERR_INVALID_ARG;
+  if (c->second_policy == MOE_SECOND_RANDOM && c->T > 0 && !plan->second_u) return MOE_ERR_INVALID_ARG;
+  const float* su = c->second_policy == MOE_SECOND_RANDOM ? plan->second_u : nullptr;
   const Layout L = layout_of(c);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -188,13 +192,14 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, gm, plan->topk_idx,
                                       plan->topk_gate, sc, st)) != hipSuccess)
       return hip_fail(e, "router_split");
-    if ((e = moe::launch_router_rank(plan->topk_idx, c->T, c->E, c->k, L.nb, plan->dst_row, hist, st)) != hipSuccess)
+    if ((e = moe::launch_router_rank(plan->topk_idx, plan->topk_gate, su, c->T, c->E, c->k, L.nb, plan->dst_row, hist,
+                                     st)) != hipSuccess)
       return hip_fail(e, "router_rank");
   } else {
     if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
                                        st)) != hipSuccess)
       return hip_fail(e, "router_logits");
-    if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, gm, L.nb, plan->topk_idx,
+    if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, gm, su, L.nb, plan->topk_idx,
                                        plan->topk_gate, plan->dst_row, hist, st)) != hipSuccess)
       return hip_fail(e, "router_select");
   }

@@ -186,9 +186,12 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const void* __restri
 // For every choice r: the token's rank among the block's 64 tokens that chose
 // the same expert at the same r (ballot peeling over the expert id bits; no
 // atomics), parked in dst_rank, and the block histogram hist[e][r*nb + blk].
+// An absent choice (GShard's random second choice not taken) ranks under the
+// virtual expert E, which has no histogram row, and gets kAbsentChoice in dst_rank.
 template <int KMAX>
-__device__ __forceinline__ void block_ranks(const int (&ti)[KMAX], bool valid, int k, int E, int nbits, int nb, int t,
-                                            int32_t* __restrict__ dst_rank, int32_t* __restrict__ hist, int* s_cnt) {
+__device__ __forceinline__ void block_ranks(const int (&ti)[KMAX], const bool (&absent)[KMAX], bool valid, int k,
+                                            int E, int nbits, int nb, int t, int32_t* __restrict__ dst_rank,
+                                            int32_t* __restrict__ hist, int* s_cnt) {
   const int lane = threadIdx.x;
   const int blk = blockIdx.x;
   const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
@@ -196,9 +199,9 @@ __device__ __forceinline__ void block_ranks(const int (&ti)[KMAX], bool valid, i
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
     if (r < k) {
-      for (int e = lane; e < E; e += 64) s_cnt[e] = 0;
+      for (int e = lane; e <= E; e += 64) s_cnt[e] = 0;
       __syncthreads();
-      const int my_e = ti[r];
+      const int my_e = absent[r] ? E : ti[r];
       uint64_t same = valid_mask;
       for (int b = 0; b < nbits; ++b) {
         const bool bit = (my_e >> b) & 1;
@@ -207,7 +210,7 @@ __device__ __forceinline__ void block_ranks(const int (&ti)[KMAX], bool valid, i
       }
       if (valid) {
         const int rank = __popcll(same & lt_mask);
-        dst_rank[(size_t)t * k + r] = rank;
+        dst_rank[(size_t)t * k + r] = absent[r] ? kAbsentChoice : rank;
         if (rank == 0) s_cnt[my_e] = __popcll(same);
       }
       __syncthreads();
@@ -220,7 +223,8 @@ __device__ __forceinline__ void block_ranks(const int (&ti)[KMAX], bool valid, i
 
 template <int KMAX>
 __global__ void __launch_bounds__(64) router_select_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                           int gate_mode, int nbits, int nb,
+                                                           int gate_mode, const float* __restrict__ second_u,
+                                                           int nbits, int nb,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_gate,
                                                            int32_t* __restrict__ dst_rank,
@@ -274,6 +278,9 @@ __global__ void __launch_bounds__(64) router_select_kernel(const float* __restri
   // gates (fp32)
   const float m = tv[0];
   float den = 0.0f;
+  float gv[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) gv[r] = 0.0f;
   if (valid) {
     if (gate_mode == 0) {  // softmax scores over all E, no renormalisation
       if (vec) {
@@ -295,28 +302,41 @@ __global__ void __launch_bounds__(64) router_select_kernel(const float* __restri
 #pragma unroll
     for (int r = 0; r < KMAX; ++r) {
       if (r < k) {
+        gv[r] = gate_value<KMAX>(gate_mode, k, tv, den, r);
         topk_idx[(size_t)t * k + r] = ti[r];
-        topk_gate[(size_t)t * k + r] = gate_value<KMAX>(gate_mode, k, tv, den, r);
+        topk_gate[(size_t)t * k + r] = gv[r];
       }
     }
   }
 
-  block_ranks<KMAX>(ti, valid, k, E, nbits, nb, t, dst_rank, hist, s_cnt);
+  bool absent[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) absent[r] = false;
+  if (KMAX >= 2 && second_u && valid) absent[1] = !second_choice_taken(second_u[t], gv[0], gv[1]);
+  block_ranks<KMAX>(ti, absent, valid, k, E, nbits, nb, t, dst_rank, hist, s_cnt);
 }
 
 // Ranks and block histogram from a finished topk_idx (the split router writes
 // the choices itself; this is the rank part of the kernel above).
 template <int KMAX>
-__global__ void __launch_bounds__(64) router_rank_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
+__global__ void __launch_bounds__(64) router_rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                         const float* __restrict__ topk_gate,
+                                                         const float* __restrict__ second_u, int T, int E, int k,
                                                          int nbits, int nb, int32_t* __restrict__ dst_rank,
                                                          int32_t* __restrict__ hist) {
-  extern __shared__ int s_cnt[];  // [E]
+  extern __shared__ int s_cnt[];  // [E + 1]
   const int t = blockIdx.x * 64 + threadIdx.x;
   const bool valid = t < T;
   int ti[KMAX];
+  bool absent[KMAX];
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) ti[r] = (valid && r < k) ? topk_idx[(size_t)t * k + r] : 0;
-  block_ranks<KMAX>(ti, valid, k, E, nbits, nb, t, dst_rank, hist, s_cnt);
+  for (int r = 0; r < KMAX; ++r) {
+    ti[r] = (valid && r < k) ? topk_idx[(size_t)t * k + r] : 0;
+    absent[r] = false;
+  }
+  if (KMAX >= 2 && second_u && valid)
+    absent[1] = !second_choice_taken(second_u[t], topk_gate[(size_t)t * k], topk_gate[(size_t)t * k + 1]);
+  block_ranks<KMAX>(ti, absent, valid, k, E, nbits, nb, t, dst_rank, hist, s_cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,16 +369,17 @@ hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const
   return hipGetLastError();
 }
 
-hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, int nb, int32_t* topk_idx,
-                                float* topk_gate, int32_t* dst_rank, int32_t* hist, hipStream_t st) {
+hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, const float* second_u,
+                                int nb, int32_t* topk_idx, float* topk_gate, int32_t* dst_rank, int32_t* hist,
+                                hipStream_t st) {
   if (T == 0) return hipSuccess;
   int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
+  while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
   dim3 grid(nb), block(64);
-  size_t shm = sizeof(int) * (size_t)E;
-#define MOE_SEL(KM)                                                                                              \
-  router_select_kernel<KM><<<grid, block, shm, st>>>(logits, T, E, k, gate_mode, nbits, nb, topk_idx, topk_gate, \
-                                                     dst_rank, hist)
+  size_t shm = sizeof(int) * (size_t)(E + 1);
+#define MOE_SEL(KM)                                                                                            \
+  router_select_kernel<KM><<<grid, block, shm, st>>>(logits, T, E, k, gate_mode, second_u, nbits, nb, topk_idx, \
+                                                     topk_gate, dst_rank, hist)
   if (k <= 1) MOE_SEL(1);
   else if (k <= 2) MOE_SEL(2);
   else if (k <= 4) MOE_SEL(4);
@@ -368,14 +389,16 @@ hipError_t launch_router_select(const float* logits, int T, int E, int k, int ga
   return hipGetLastError();
 }
 
-hipError_t launch_router_rank(const int32_t* topk_idx, int T, int E, int k, int nb, int32_t* dst_rank, int32_t* hist,
-                              hipStream_t st) {
+hipError_t launch_router_rank(const int32_t* topk_idx, const float* topk_gate, const float* second_u, int T, int E,
+                              int k, int nb, int32_t* dst_rank, int32_t* hist, hipStream_t st) {
   if (T == 0) return hipSuccess;
   int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
+  while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
   dim3 grid(nb), block(64);
-  size_t shm = sizeof(int) * (size_t)E;
-#define MOE_RANK(KM) router_rank_kernel<KM><<<grid, block, shm, st>>>(topk_idx, T, E, k, nbits, nb, dst_rank, hist)
+  size_t shm = sizeof(int) * (size_t)(E + 1);
+#define MOE_RANK(KM)                                                                                          \
+  router_rank_kernel<KM><<<grid, block, shm, st>>>(topk_idx, topk_gate, second_u, T, E, k, nbits, nb, dst_rank, \
+                                                   hist)
   if (k <= 1) MOE_RANK(1);
   else if (k <= 2) MOE_RANK(2);
   else if (k <= 4) MOE_RANK(4);

@@ -82,6 +82,10 @@ __global__ void __launch_bounds__(64) slot_finalize_kernel(const int32_t* __rest
   if (t >= T) return;
   for (int r = 0; r < k; ++r) {
     const size_t i = (size_t)t * k + r;
+    if (dst_row[i] == kAbsentChoice) {
+      dst_row[i] = -1;
+      continue;
+    }
     const int e = topk_idx[i];
     const int slot = base[(size_t)e * Q + r * nb + blk] + dst_row[i];
     const int d = s_off[e] + slot;
@@ -160,6 +164,7 @@ __global__ void __launch_bounds__(64) slot_list_kernel(const int32_t* __restrict
   if (t >= T) return;
   for (int r = 0; r < k; ++r) {
     const size_t i = (size_t)t * k + r;
+    if (dst_row[i] == kAbsentChoice) continue;
     const int e = topk_idx[i];
     const int L = s_off[e] + base[(size_t)e * Q + r * nb + blk] + dst_row[i];
     dst_row[i] = L;
@@ -254,6 +259,10 @@ __global__ void __launch_bounds__(64) slot_finalize_probs_kernel(int T, int E, i
   if (t >= T) return;
   for (int r = 0; r < k; ++r) {
     const size_t i = (size_t)t * k + r;
+    if (dst_row[i] == kAbsentChoice) {
+      dst_row[i] = -1;
+      continue;
+    }
     const int e = topk_idx[i];
     const int slot = newslot[dst_row[i]];
     const int d = s_off[e] + slot;
