@@ -93,7 +93,8 @@ typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
  * P_e is the mean over tokens of softmax(logits)_e in both. */
 typedef enum { MOE_AUX_ALL_CHOICES = 0, MOE_AUX_FIRST_CHOICE = 1 } moe_aux_mode;
 
-/* Router score ([EP] router: "softmax or sigmoid, then top-k").  Both are
+/* Router score ([EP] router: logits pass through softmax or sigmoid before the
+ * top-k).  Both are
  * increasing in the logit, so the choices are the same; with SIGMOID the gate of
  * a choice is its score s = 1/(1+exp(-l)) (MOE_SOFTMAX_TOPK) or s over the sum
  * of the chosen scores (MOE_SOFTMAX_TOPK_RENORM); MOE_TOPK_SOFTMAX is the

@@ -112,7 +112,7 @@ static void select_topk(const float *l, int64_t E, int k, int32_t *idx) {
  * from the fp32 logits, rounded once to fp32. */
 static void gates(const float *l, int64_t E, int k, int mode, int score, const int32_t *idx, float *g) {
   if (score == OR_SIGMOID && mode != OR_TOPK_SOFTMAX) {
-    /* sigmoid scores ([EP] router: "softmax or sigmoid, then top-k"): the chosen
+    /* sigmoid scores ([EP] router: softmax or sigmoid before the top-k): the chosen
      * scores themselves, or divided by their sum when renormalised */
     double sc[16], sum = 0.0;
     for (int r = 0; r < k; ++r) {
