@@ -58,6 +58,12 @@ def build_hip(verbose=False):
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    # every kernel the library launches must be defined in it (a template whose
+    # host-side instantiation is dropped shows up only as an undefined symbol)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "_ZN3moe" in ln]
+    if nm.returncode == 0 and missing:
+        raise RuntimeError(f"libmoe_hip.so would leave library symbols undefined: {missing[:3]}")
     os.replace(tmp, LIB)
 
 

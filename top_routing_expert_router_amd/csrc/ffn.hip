@@ -390,28 +390,35 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
   // get different chunk slots.
   auto lds_pos = [](int r, int c) { return (r * CPR + (c ^ ((r >> RSH) & (CPR - 1)))) * 8; };
 
-  auto issue = [&](int buf, const PipeTile& t, int kstep) {
-    uint16_t* st = smem + buf * STAGE;
-    const int k0 = kstep * BK;
+  // Row pointers of this wave's L loads for the tile being loaded, fixed for
+  // the whole tile; a stage only adds its k offset.
+  uintptr_t rowp[L];
+  auto set_rows = [&](const PipeTile& t) {
 #pragma unroll
     for (int q = 0; q < L; ++q) {
       const int blk = q * NW + w;  // 64 lanes = 64 / CPR rows; never straddles the two regions
       const int p = blk * 64 + lane;
       const int r = p / CPR;
       const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
-      const uint16_t* g;
       if (r < BM) {
         const int rr = r < t.rows ? r : 0;
-        g = A + (size_t)(t.row0 + rr) * K + k0 + c * 8;
+        rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)(t.row0 + rr) * K + c * 8);
       } else {
         const int wr = r - BM;
         const uint16_t* base = (kGated && wr >= WR / 2) ? W2 : W;
         int n = t.n0 + (kGated ? (wr & (WR / 2 - 1)) : wr);
         n = n < N ? n : N - 1;
-        g = base + ((size_t)t.e * N + n) * K + k0 + c * 8;
+        rowp[q] = reinterpret_cast<uintptr_t>(base + ((size_t)t.e * N + n) * K + c * 8);
       }
-      __builtin_amdgcn_global_load_lds(g, st + blk * 512, 16, 0, 0);
     }
+  };
+  auto issue = [&](int buf, int kstep) {
+    uint16_t* st = smem + buf * STAGE;
+    const int k0 = kstep * BK;
+#pragma unroll
+    for (int q = 0; q < L; ++q)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rowp[q]) + k0, st + (q * NW + w) * 512, 16, 0,
+                                       0);
   };
 
   f32x16_t acc[NF][MF];
@@ -478,14 +485,14 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
     }
   };
 
-  PipeTile lt = decode(0);  // tile of the next stage to load
+  set_rows(decode(0));  // rows of the tile of the next stage to load
   int lt_i = 0, lt_k = 0, issued = 0;
   auto issue_next = [&]() {
-    issue(issued % S, lt, lt_k);
+    issue(issued % S, lt_k);
     ++issued;
     if (++lt_k == nk) {
       lt_k = 0;
-      if (++lt_i < my_tiles) lt = decode(lt_i);
+      if (++lt_i < my_tiles) set_rows(decode(lt_i));
     }
   };
 #pragma unroll
