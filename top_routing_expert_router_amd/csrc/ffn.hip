@@ -541,6 +541,283 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same tiles with separate LDS rings for the two operands: token rows in a
+// ring of 2 stages, weight rows in a ring of SW >= 3.  Per step j the loads go
+// out token group first (stage j + 1), then weight group (stage j + SW - 1), so
+// that waiting for the token stage j + 1 leaves the newest weight group in
+// flight (vector memory operations complete in issue order): the weight rows,
+// streamed from HBM once per tile, get SW - 1 steps to arrive, the token rows
+// (shared by the tiles of one expert, mostly L2 hits) one step.  BK = 64, 8
+// waves.
+// ---------------------------------------------------------------------------
+template <int BM, int WR, int SW, int WGM, int EPI>
+__global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_t* __restrict__ A,
+                                                                   const uint16_t* __restrict__ W,
+                                                                   const uint16_t* __restrict__ W2,
+                                                                   uint16_t* __restrict__ C,
+                                                                   const int32_t* __restrict__ offsets, int E,
+                                                                   int N, int K, int rmax) {
+  constexpr int NW = 8, BK = 64, CPR = 8, RSH = 1;
+  constexpr bool kGated = EPI == EPI_SWIGLU;
+  constexpr int BN = kGated ? WR / 2 : WR;
+  constexpr int ASTAGE = BM * BK, WSTAGE = WR * BK;  // bf16 elements per stage of each ring
+  constexpr int LA = BM * CPR / (64 * NW), LW = WR * CPR / (64 * NW);  // loads per wave per stage
+  constexpr int WGN = NW / WGM;
+  constexpr int MF = BM / WGM / 32, NF = WR / WGN / 32;
+  constexpr int HF = kGated ? NF / 2 : NF;
+  constexpr int KS = BK / 16;
+  static_assert(BM * CPR % (64 * NW) == 0 && WR * CPR % (64 * NW) == 0, "whole load groups");
+  static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
+  static_assert(MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
+  static_assert(SW >= 3 && LA + (SW - 2) * LW < 64, "rings");
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* s_a = smem;                                     // [2][BM][BK]
+  uint16_t* s_w = smem + 2 * ASTAGE;                        // [SW][WR][BK]
+  int* s_ts = reinterpret_cast<int*>(s_w + SW * WSTAGE);   // [E+1]
+  int* s_off = s_ts + (E + 1);                              // [E+1]
+  __shared__ int s_scan[NW + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int ntn = (N + BN - 1) / BN;
+  {
+    const int per = (E + 64 * NW - 1) / (64 * NW);
+    const int e0 = tid * per;
+    int cnt = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) cnt += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+    }
+    int total;
+    int run = block_exclusive_scan(cnt, s_scan, &total);
+    for (int j = 0; j < per; ++j) {
+      const int e = e0 + j;
+      if (e < E) {
+        s_ts[e] = run;
+        s_off[e] = offsets[e];
+        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+      }
+    }
+    if (tid == 0) {
+      s_ts[E] = total;
+      s_off[E] = offsets[E];
+    }
+    __syncthreads();
+  }
+  const int G = gridDim.x;
+  const int total_tiles = s_ts[E];
+  const int slot = (G % 8 == 0) ? ((int)blockIdx.x % 8) * (G / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int my_tiles = total_tiles > slot ? (total_tiles - 1 - slot) / G + 1 : 0;
+  const int nk = K / BK;
+  const int total_steps = my_tiles * nk;
+  if (total_steps == 0) return;
+
+  auto decode = [&](int i) {
+    const int g = slot + i * G;
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_ts[mid] <= g) lo = mid;
+      else hi = mid;
+    }
+    const int mt_e = (s_off[lo + 1] - s_off[lo] + BM - 1) / BM;
+    const int local = g - s_ts[lo];
+    const int nt = local / mt_e;
+    PipeTile t;
+    t.e = lo;
+    t.row0 = s_off[lo] + (local - nt * mt_e) * BM;
+    t.rows = min(min(BM, s_off[lo + 1] - t.row0), rmax - t.row0);
+    if (t.rows <= 0) {
+      t.rows = 0;
+      t.row0 = 0;
+    }
+    t.n0 = nt * BN;
+    return t;
+  };
+  auto lds_pos = [](int r, int c) { return (r * CPR + (c ^ ((r >> RSH) & (CPR - 1)))) * 8; };
+
+  // per-tile row addresses of this wave's loads (integers: see the pipe kernel)
+  uintptr_t rowA[LA], rowW[LW];
+  auto set_rows_a = [&](const PipeTile& t) {
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int p = (q * NW + w) * 64 + lane;
+      const int r = p / CPR, c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
+      const int rr = r < t.rows ? r : 0;
+      rowA[q] = reinterpret_cast<uintptr_t>(A + (size_t)(t.row0 + rr) * K + c * 8);
+    }
+  };
+  auto set_rows_w = [&](const PipeTile& t) {
+#pragma unroll
+    for (int q = 0; q < LW; ++q) {
+      const int p = (q * NW + w) * 64 + lane;
+      const int r = p / CPR, c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
+      const uint16_t* base = (kGated && r >= WR / 2) ? W2 : W;
+      int n = t.n0 + (kGated ? (r & (WR / 2 - 1)) : r);
+      n = n < N ? n : N - 1;
+      rowW[q] = reinterpret_cast<uintptr_t>(base + ((size_t)t.e * N + n) * K + c * 8);
+    }
+  };
+  // load trackers: next stage index, its tile and k-step, per operand
+  int a_next = 0, a_tile = 0, a_k = 0;
+  int w_next = 0, w_tile = 0, w_k = 0;
+  set_rows_a(decode(0));
+  set_rows_w(decode(0));
+  auto issue_a = [&]() {
+    uint16_t* st = s_a + (a_next & 1) * ASTAGE;
+#pragma unroll
+    for (int q = 0; q < LA; ++q)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rowA[q]) + a_k * BK,
+                                       st + (q * NW + w) * 512, 16, 0, 0);
+    ++a_next;
+    if (++a_k == nk) {
+      a_k = 0;
+      if (++a_tile < my_tiles) set_rows_a(decode(a_tile));
+    }
+  };
+  auto issue_w = [&]() {
+    uint16_t* st = s_w + (w_next % SW) * WSTAGE;
+#pragma unroll
+    for (int q = 0; q < LW; ++q)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rowW[q]) + w_k * BK,
+                                       st + (q * NW + w) * 512, 16, 0, 0);
+    ++w_next;
+    if (++w_k == nk) {
+      w_k = 0;
+      if (++w_tile < my_tiles) set_rows_w(decode(w_tile));
+    }
+  };
+
+  f32x16_t acc[NF][MF];
+  auto zero = [&]() {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[f][i][v] = 0.0f;
+  };
+  struct Frags {
+    bf16x8_t w[NF], x[MF];
+  };
+  auto read_frags = [&](int j, int kk, Frags& fr) {
+    const uint16_t* sa = s_a + (j & 1) * ASTAGE;
+    const uint16_t* sw = s_w + (j % SW) * WSTAGE;
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int r = (kGated ? (f / HF) * (WR / 2) + wn * (HF * 32) + (f % HF) * 32 : wn * (NF * 32) + f * 32) +
+                    (lane & 31);
+      fr.w[f] = *reinterpret_cast<const bf16x8_t*>(sw + lds_pos(r, c));
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int r = wm * (MF * 32) + i * 32 + (lane & 31);
+      fr.x[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_pos(r, c));
+    }
+  };
+  auto mfma = [&](const Frags& fr) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+        acc[f][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.w[f], fr.x[i], acc[f][i], 0, 0, 0);
+  };
+  auto store = [&](const PipeTile& t) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+      const int m = wm * (MF * 32) + i * 32 + (lane & 31);
+      if (m < t.rows) {
+        uint16_t* crow = C + (size_t)(t.row0 + m) * N;
+#pragma unroll
+        for (int f = 0; f < HF; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
+            if (n < N) {
+              float v[4];
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj)
+                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
+                               : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
+              uint2 pk;
+              pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+              pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              *reinterpret_cast<uint2*>(crow + n) = pk;
+            }
+          }
+      }
+    }
+  };
+
+  // prologue: weight stages 0 .. SW-2, then token stage 0 (so that waiting for
+  // a token stage covers the older weight stage of the same index)
+#pragma unroll
+  for (int s2 = 0; s2 < SW - 1; ++s2)
+    if (w_next < total_steps) issue_w();
+  issue_a();
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  PipeTile ct = decode(0);
+  zero();
+  Frags fr[2];
+  read_frags(0, 0, fr[0]);
+  for (int j = 0; j < total_steps; ++j) {
+    // buffers (j+1) & 1 and (j + SW - 1) % SW were last read in step j - 1
+    const bool more_a = a_next < total_steps;
+    if (more_a) issue_a();  // stage j + 1
+    const bool more_w = w_next < total_steps;
+    if (more_w) issue_w();  // stage j + SW - 1
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk + 1 < KS) read_frags(j, kk + 1, fr[(kk + 1) & 1]);
+      mfma(fr[kk & 1]);
+      if (kk + 1 < KS) {
+#pragma unroll
+        for (int q = 0; q < MF + NF; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - (MF + NF), 0);
+      }
+    }
+    if (j + 1 < total_steps) {
+      // token stage j+1 (issued this step, before the weight group) and weight
+      // stage j+1 (issued SW - 2 steps ago) complete; the weight group of this
+      // step may stay in flight
+      if (more_a && more_w) wait_vmcnt<LW>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      read_frags(j + 1, 0, fr[0]);
+    }
+    if ((j + 1) % nk == 0) {
+      store(ct);
+      zero();
+      if (j + 1 < total_steps) ct = decode((j + 1) / nk);
+    }
+  }
+}
+
+template <int BM, int WR, int SW, int WGM, int EPI>
+static hipError_t launch_ring(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
+                              int N, int K, int64_t R_max, int cus, hipStream_t st) {
+  constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
+  const int ntn = (N + BN - 1) / BN;
+  const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
+  if (tiles <= 0) return hipSuccess;
+  const int grid = (int)(tiles < cus ? tiles : cus);
+  const size_t shm = sizeof(uint16_t) * ((size_t)2 * BM + (size_t)SW * WR) * 64 + sizeof(int) * 2 * (size_t)(E + 1);
+  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (err != hipSuccess) return err;
+  grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI><<<dim3(grid), dim3(512), shm, st>>>(
+      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max);
+  return hipGetLastError();
+}
+
 template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, hipStream_t st) {
@@ -595,10 +872,11 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
-    // 256-row tiles (two stages of 256 + WR rows) for experts with more than
-    // 128 rows on average, with 256 or 192 weight rows per tile, whichever
-    // fills the CUs more evenly in whole waves of tiles; else 128 x 256 tiles
-    // (three 48 KB stages).
+    // Experts with more than 128 rows on average take 256-row tiles: 256 x 256
+    // (two stages of 512 rows), or, where 192 weight rows per tile fill the
+    // CUs more evenly in whole waves of tiles, 256 x 192 with split rings (two
+    // token stages, three weight stages).  Otherwise 128 x 256 tiles (three
+    // 48 KB stages).
     constexpr bool kGated = EPI == EPI_SWIGLU;
     if (R_max / E > 128) {
       auto fill = [&](int bn) {
@@ -608,7 +886,7 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       };
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
-          return launch_pipe<256, 192, 64, 2, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
       return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
     }
     return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
