@@ -247,43 +247,33 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
-    # ---- per-stage durations: the same kernels through the stage entry points,
-    # HIP events recorded on the stream the kernels run on (torch's current stream)
-    stages = ("route", "dispatch", "expert_ffn", "combine")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-    acc = {s: 0.0 for s in stages}
-    for _ in range(args.steps):
-        ev[0].record()
-        B.route(cfg, x, wg, bias, plan, ws)
-        ev[1].record()
-        B.dispatch(cfg, x, plan, X)
-        ev[2].record()
-        B.expert_ffn(cfg, X, plan, w1, w3, w2, Y, ws)
-        ev[3].record()
-        B.combine(cfg, Y, plan, x, y)
-        ev[4].record()
+    # ---- per-stage durations: each stage entry point called K times back to back
+    # (the plan and buffers of this batch stay valid across repeats), HIP events
+    # recorded on the stream the kernels run on (torch's current stream)
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        for i, s in enumerate(stages):
-            acc[s] += ev[i].elapsed_time(ev[i + 1])
-    stage_us = {s: acc[s] / args.steps * 1e3 for s in stages}
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    stage_us = {
+        "route": timed(lambda: B.route(cfg, x, wg, bias, plan, ws)),
+        "dispatch": timed(lambda: B.dispatch(cfg, x, plan, X)),
+        "expert_ffn": timed(lambda: B.expert_ffn(cfg, X, plan, w1, w3, w2, Y, ws)),
+        "combine": timed(lambda: B.combine(cfg, Y, plan, x, y)),
+    }
 
     # ---- router training terms (load-balancing loss, z-loss): route with the
     # optional losses output, against route without it
     plan_l = dict(plan)
     plan_l["losses"] = torch.empty(2, dtype=torch.float64, device=dev)
-    el = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    t_plain = t_loss = 0.0
-    for _ in range(args.steps):
-        el[0].record()
-        B.route(cfg, x, wg, bias, plan, ws)
-        el[1].record()
-        B.route(cfg, x, wg, bias, plan_l, ws)
-        el[2].record()
-        torch.cuda.synchronize()
-        t_plain += el[0].elapsed_time(el[1])
-        t_loss += el[1].elapsed_time(el[2])
-    losses_us = {"route_us": round(t_plain / args.steps * 1e3, 2),
-                 "route_with_losses_us": round(t_loss / args.steps * 1e3, 2),
+    losses_us = {"route_us": round(stage_us["route"], 2),
+                 "route_with_losses_us": round(timed(lambda: B.route(cfg, x, wg, bias, plan_l, ws)), 2),
                  "losses": [float(v) for v in plan_l["losses"].cpu().tolist()]}
 
     # ---- routing variants: "probs" drop policy and sigmoid scores, route alone

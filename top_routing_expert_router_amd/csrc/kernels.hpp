@@ -18,7 +18,7 @@ hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const
                                 int H, int E, bool vec_ok, hipStream_t st);
 // Split-bf16 router (bf16 x, H % 64 == 0, 16-byte aligned x): logits with a
 // certified radius, choices and gates per token, exact recomputation of the
-// undecided tokens.  Ranks come from launch_router_rank afterwards.
+// undecided tokens.
 struct SplitScratch {
   void* wp;       // [3][Ep][H] bf16 weight pieces
   double* wsq;    // [H/64][Ep] partial sums of w^2
@@ -30,9 +30,22 @@ struct SplitScratch {
 };
 int split_router_ep(int E);
 int split_router_hs(int H);
+// Work the router's last kernel may take over (null pointers: not wanted):
+// the ranks and block histogram of launch_router_rank, and the per-block
+// partials of launch_router_losses.  *fused reports what was done (1: ranks,
+// 2: loss partials); the caller launches the rest.
+struct SplitEpilogue {
+  const float* second_u;
+  int32_t* dst_rank;
+  int32_t* hist;
+  double* Ppart;
+  double* Zpart;
+  int32_t* Cpart;
+  int score_fn;
+};
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
                                int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
-                               hipStream_t st);
+                               const SplitEpilogue& ep, int* fused, hipStream_t st);
 hipError_t launch_router_rank(const int32_t* topk_idx, const float* topk_gate, const float* second_u, int T, int E,
                               int k, int nb, int32_t* dst_rank, int32_t* hist, hipStream_t st);
 hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, const float* second_u,
@@ -40,9 +53,10 @@ hipError_t launch_router_select(const float* logits, int T, int E, int k, int ga
                                 hipStream_t st);
 // Router training terms from the final logits and choices (see router_losses.hip).
 // Workspace: Ppart [E][ceil(T/64)] f64, Zpart [ceil(T/64)] + fP [E+1] f64, Cpart [E][ceil(T/64)] int32.
+// partials_done: Ppart, Zpart and Cpart are already filled (by the split router).
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,
                                 int k, int score_fn, int aux_mode, double aux_coeff, double z_coeff, double* Ppart,
-                                double* Zpart, int32_t* Cpart, double* losses, hipStream_t st);
+                                double* Zpart, int32_t* Cpart, double* losses, bool partials_done, hipStream_t st);
 // "probs" drop policy: replaces launch_slot_finalize when a capacity limits.
 // Workspace: lkey, lq, newslot, each [T*k].
 hipError_t launch_slot_probs(const int32_t* base, int Q, int nb, int T, int E, int k, int C, const int32_t* topk_idx,

@@ -180,6 +180,7 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   const int C = effective_capacity(c);
   const int gm = c->gate_mode | (c->score_fn == MOE_SCORE_SIGMOID ? moe::kSigmoidFlag : 0);
   hipError_t e;
+  int fused = 0;  // work the split router's epilogue took over (1: ranks, 2: loss partials)
   if (L.split && aligned16(x)) {
     moe::SplitScratch sc;
     sc.wp = w + L.wp;
@@ -189,11 +190,18 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     sc.pairs = reinterpret_cast<int2*>(w + L.pairs);
     sc.utok = reinterpret_cast<int4*>(w + L.utok);
     sc.count = reinterpret_cast<int*>(w + L.count);
+    const moe::SplitEpilogue ep{su,
+                                plan->dst_row,
+                                hist,
+                                plan->losses ? reinterpret_cast<double*>(w + L.lp) : nullptr,
+                                reinterpret_cast<double*>(w + L.lz),
+                                reinterpret_cast<int32_t*>(w + L.lc),
+                                c->score_fn};
     if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, gm, plan->topk_idx,
-                                      plan->topk_gate, sc, st)) != hipSuccess)
+                                      plan->topk_gate, sc, ep, &fused, st)) != hipSuccess)
       return hip_fail(e, "router_split");
-    if ((e = moe::launch_router_rank(plan->topk_idx, plan->topk_gate, su, c->T, c->E, c->k, L.nb, plan->dst_row, hist,
-                                     st)) != hipSuccess)
+    if (!(fused & 1) && (e = moe::launch_router_rank(plan->topk_idx, plan->topk_gate, su, c->T, c->E, c->k, L.nb,
+                                                     plan->dst_row, hist, st)) != hipSuccess)
       return hip_fail(e, "router_rank");
   } else {
     if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
@@ -221,7 +229,7 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
       (e = moe::launch_router_losses(logits, plan->topk_idx, plan->demand, c->T, c->E, c->k, c->score_fn, c->aux_mode,
                                      c->aux_coeff, c->z_coeff, reinterpret_cast<double*>(w + L.lp),
                                      reinterpret_cast<double*>(w + L.lz), reinterpret_cast<int32_t*>(w + L.lc),
-                                     plan->losses, st)) != hipSuccess)
+                                     plan->losses, (fused & 2) != 0, st)) != hipSuccess)
     return hip_fail(e, "router_losses");
   return MOE_OK;
 }

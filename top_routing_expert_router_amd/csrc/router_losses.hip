@@ -175,11 +175,13 @@ __global__ void __launch_bounds__(256) router_loss_final_kernel(const double* __
 
 hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, const int32_t* demand, int T, int E,
                                 int k, int score_fn, int aux_mode, double aux_coeff, double z_coeff, double* Ppart,
-                                double* Zpart, int32_t* Cpart, double* losses, hipStream_t st) {
+                                double* Zpart, int32_t* Cpart, double* losses, bool partials_done,
+                                hipStream_t st) {
   const int nb = (T + 63) / 64;
   double* fP = Zpart + (nb > 0 ? nb : 1);  // [E + 1] after the z partials
   if (nb > 0) {
     const int je = (E + 63) / 64;
+    if (!partials_done) {
 #define MOE_LP(J)                                                                                                \
   router_loss_partial_kernel<J><<<dim3(nb), dim3(256), 0, st>>>(logits, topk_idx, T, E, k, score_fn, nb, Ppart, \
                                                                 Zpart, Cpart)
@@ -189,6 +191,7 @@ hipError_t launch_router_losses(const float* logits, const int32_t* topk_idx, co
     else if (je <= 8) MOE_LP(8);
     else MOE_LP(16);
 #undef MOE_LP
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     router_loss_expert_kernel<<<dim3((E + 1 + 3) / 4), dim3(256), 0, st>>>(Ppart, Zpart, Cpart, demand, nb, T, E,

@@ -162,7 +162,8 @@ __device__ __forceinline__ void group_topk(const float (&v)[JE], const float (&l
 template <int G, int JE, int KMAX>
 __device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, int gate_mode, const int (&se)[KMAX],
                                             const float (&sv)[KMAX], int t, bool active,
-                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+                                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                                            int* m_idx = nullptr, float* m_gate = nullptr) {
   const int lg = threadIdx.x & (G - 1);
   const float m = sv[0];
   float den = 0.0f;
@@ -181,8 +182,13 @@ __device__ __forceinline__ void group_gates(const float (&v)[JE], int E, int k, 
 #pragma unroll
   for (int r = 0; r < KMAX; ++r)
     if (r < k && (r & (G - 1)) == lg) {  // every choice r < k has a writer, also when G < k
+      const float g = gate_value<KMAX>(gate_mode, k, sv, den, r);
       topk_idx[(size_t)t * k + r] = se[r];
-      topk_gate[(size_t)t * k + r] = gate_value<KMAX>(gate_mode, k, sv, den, r);
+      topk_gate[(size_t)t * k + r] = g;
+      if (m_idx) {  // the token's row of a workgroup-local copy
+        m_idx[r] = se[r];
+        m_gate[r] = g;
+      }
     }
 }
 
@@ -199,7 +205,8 @@ __device__ __forceinline__ void certify_token(const float (&v)[JE], const float 
                                               int E, int H, int k, int gate_mode, float c1, bool active, int t,
                                               float xn, int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_gate, int2* __restrict__ pairs,
-                                              int4* __restrict__ utok, int* __restrict__ count) {
+                                              int4* __restrict__ utok, int* __restrict__ count,
+                                              int* m_idx = nullptr, float* m_gate = nullptr) {
   const int lane = threadIdx.x & 63, lg = lane & (G - 1);
   constexpr float up = 1.0f + 0x1p-20f;
   const float c2 = 0x1p-24f + 0x1p-44f;
@@ -223,7 +230,7 @@ __device__ __forceinline__ void certify_token(const float (&v)[JE], const float 
   int se[KMAX];
   float sv[KMAX], slo[KMAX], shi[KMAX];
   group_topk<G, JE, KMAX, true>(v, lo, hi, taken, k, se, sv, slo, shi);
-  group_gates<G, JE, KMAX>(v, E, k, gate_mode, se, sv, t, active, topk_idx, topk_gate);
+  group_gates<G, JE, KMAX>(v, E, k, gate_mode, se, sv, t, active, topk_idx, topk_gate, m_idx, m_gate);
 
   float tau = slo[0];
   bool ordered = true;
@@ -282,11 +289,57 @@ __device__ __forceinline__ void certify_token(const float (&v)[JE], const float 
   }
 }
 
+// sum_h x[h] * (hi + mid + lo)[e][h] in binary64 over one wave (lanes over h);
+// every lane returns the sum.
+__device__ __forceinline__ double exact_dot(const uint16_t* __restrict__ xr, const uint16_t* __restrict__ wp, int e,
+                                            int H, int Ep) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* w0 = wp + (size_t)e * H;
+  const uint16_t* w1 = wp + ((size_t)Ep + e) * H;
+  const uint16_t* w2 = wp + ((size_t)2 * Ep + e) * H;
+  double s = 0.0;
+  for (int h = 8 * lane; h < H; h += 512) {
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + h);
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(w0 + h);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(w1 + h);
+    const u32x4_t cc = *reinterpret_cast<const u32x4_t*>(w2 + h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int sh = half ? 0 : 16;
+        const uint32_t m = half ? 0xFFFF0000u : 0xFFFFFFFFu;
+        const double xd = (double)__uint_as_float((xv[q] << sh) & m);
+        const double wd = (double)__uint_as_float((a[q] << sh) & m) + (double)__uint_as_float((b[q] << sh) & m) +
+                          (double)__uint_as_float((cc[q] << sh) & m);
+        s = __builtin_fma(xd, wd, s);
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+  return s;
+}
+
 // Bound on ||x|| from the fp32 sum of squares (each of the <= H additions errs
 // by at most 2^-24 relative) and on the rounding of the square root.
 __device__ __forceinline__ float xnorm_bound(float sq, int H) {
   return sqrtf(sq * (1.0f + (float)H * 0x1p-22f + 0x1p-20f)) * (1.0f + 0x1p-20f);
 }
+
+// Work the fused epilogue takes over from later kernels when its token tile
+// is a whole number of 64-token blocks: the ranks and per-block expert counts
+// (dst_rank non-null) and the per-block loss partials (Ppart non-null).
+struct SplitTail {
+  const float* second_u;  // GShard second-choice draws (k = 2), or null
+  int32_t* dst_rank;      // [T][k] rank among the block's tokens with the same choice
+  int32_t* hist;          // [E][k][nb] choices per expert, choice and block
+  int nbits, nb;          // bits of an expert id 0..E; 64-token blocks
+  double* Ppart;          // [E][nb] sum over the block of P(e | t)
+  double* Zpart;          // [nb] sum over the block of logsumexp^2
+  int32_t* Cpart;         // [E][nb] first choices per expert
+  int score_fn;           // 0: softmax, 1: sigmoid over their sum
+};
 
 // ---------------------------------------------------------------------------
 // Approximate logits: v_mfma_f32_16x16x32_bf16 on x (bf16, exact) times the
@@ -305,7 +358,8 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wp, const float* __restrict__ bias,
     const double* __restrict__ wsq, float* __restrict__ logits, float* __restrict__ xsq, double* __restrict__ wn,
     int T, int H, int E, int Ep, int k, int gate_mode, double c1, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_gate, int2* __restrict__ pairs, int4* __restrict__ utok, int* __restrict__ count) {
+    float* __restrict__ topk_gate, int2* __restrict__ pairs, int4* __restrict__ utok, int* __restrict__ count,
+    SplitTail tail) {
   static_assert(TG * EG * KS == 8, "8 waves");
   constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
   constexpr int SR = BM + 3 * BN;  // rows per slice per stage
@@ -322,6 +376,22 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   const int nks = nk / KS;  // stages (chunks per slice)
 
   auto lds_pos = [](int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; };
+
+  // Operands of the fused epilogue, loaded now so that their latency overlaps
+  // the main loop: the bias of expert tid, and the squared weight norms of two
+  // h chunks per thread (thread tid: expert tid % BN, chunks tid / BN + 8 q).
+  constexpr int NG = 512 / BN;
+  __shared__ float s_bias[BN];
+  float bpre = 0.0f;
+  double wpre[2] = {0.0, 0.0};
+  if constexpr (FUSE) {
+    if (bias && tid < BN && e0 + tid < E) bpre = bias[e0 + tid];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int hb = tid / BN + q * NG;
+      if (hb < nk) wpre[q] = wsq[(size_t)hb * Ep + e0 + tid % BN];
+    }
+  }
 
   auto issue = [&](int buf, int j) {
     uint16_t* st = smem + buf * STAGE;
@@ -477,6 +547,7 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   float* s_x = s_v + BM * SV;
   if (FUSE) {
     if (KS == 1) wait_vmcnt<0>();
+    if (tid < BN) s_bias[tid] = bpre;
     __syncthreads();  // every wave is done with the stage buffers (and slice partials)
   }
   if (ks == 0) {
@@ -485,7 +556,7 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
       const int el = (eg * WN + n) * 16 + (lane & 15);
       const int e = e0 + el;
       if (e >= E) continue;
-      const double b = bias ? (double)bias[e] : 0.0;
+      const double b = FUSE ? (double)s_bias[el] : (bias ? (double)bias[e] : 0.0);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -515,19 +586,28 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     const int lg = lane & (G - 1);
     const int tl = tid / G;  // token of this group
     __shared__ float s_wn[BN];  // ||w_e||, rounded up
+    double* s_wpart = reinterpret_cast<double*>(s_x + BM);  // [NG][BN] partial sums
+    {
+      double sw = wpre[0] + wpre[1];
+      for (int hb = tid / BN + 2 * NG; hb < nk; hb += NG) sw += wsq[(size_t)hb * Ep + tid % BN];
+      s_wpart[tid] = sw;
+    }
+    __syncthreads();
     if (tid < BN) {
       double sw = 0.0;
-      if (tid < E)
-        for (int hb = 0; hb < nk; ++hb) sw += wsq[(size_t)hb * Ep + tid];
-      s_wn[tid] = (float)sqrt(sw * (1.0 + 0x1p-40)) * (1.0f + 0x1p-20f);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) sw += s_wpart[g * BN + tid];
+      s_wn[tid] = tid < E ? (float)sqrt(sw * (1.0 + 0x1p-40)) * (1.0f + 0x1p-20f) : 0.0f;
     }
+    __shared__ int s_cnt[2];  // candidate pairs, queued tokens of this workgroup
+    if (tid < 2) s_cnt[tid] = 0;
     __syncthreads();
     float wne[JE], be[JE], v[JE];
 #pragma unroll
     for (int j = 0; j < JE; ++j) {
       const int e = lg + G * j;
       wne[j] = e < E ? s_wn[e] : 0.0f;
-      be[j] = (bias && e < E) ? bias[e] : 0.0f;
+      be[j] = e < E ? s_bias[e] : 0.0f;
     }
     const int t = t0 + tl;
     const bool active = tl < BM && t < T;
@@ -537,8 +617,148 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
       v[j] = (active && e < E) ? s_v[tl * SV + e] : -__builtin_inff();
     }
     const float xn = active ? xnorm_bound(s_x[tl], H) : 0.0f;
+    int4* s_utok = reinterpret_cast<int4*>(s_wpart + 512);  // [BM]
+    int2* s_pairs = reinterpret_cast<int2*>(s_utok + BM);     // [BM * BN]
+    double* s_lp = reinterpret_cast<double*>(s_pairs + BM * BN);  // [8][64] loss partials
+    int* s_lc = reinterpret_cast<int*>(s_lp + 512);               // [8][64]
+    double* s_lz = reinterpret_cast<double*>(s_lc + 512);         // [8]
+    int* s_idx = reinterpret_cast<int*>(s_lz + 8);                // [BM][k] final choices
+    float* s_gt = reinterpret_cast<float*>(s_idx + BM * KMAX);    // [BM][k] their gates
+    int* s_rc = reinterpret_cast<int*>(s_gt + BM * KMAX);         // [BM / 64][64 + 1] expert counts
+    const bool mirror = tail.dst_rank != nullptr || tail.Ppart != nullptr;
     certify_token<G, JE, KMAX>(v, wne, be, E, H, k, gate_mode, (float)c1 * (1.0f + 0x1p-20f), active,
-                               active ? t : 0, xn, topk_idx, topk_gate, pairs, utok, count);
+                               active ? t : 0, xn, topk_idx, topk_gate, s_pairs, s_utok, s_cnt,
+                               mirror && active ? s_idx + tl * k : nullptr, s_gt + tl * k);
+    __syncthreads();
+    // refine the queued tokens here: exact logits of the candidates (a wave
+    // per pair), then the selection again over the patched rows (a wave per token)
+    const int npairs = s_cnt[0], ntok = s_cnt[1];
+    if (ntok > 0) {
+      for (int c = w; c < npairs; c += 8) {
+        const int2 pr = s_pairs[c];
+        const double sx = exact_dot(x + (size_t)pr.x * H, wp, pr.y, H, Ep);
+        if (lane == 0) {
+          const float lv = (float)(sx + (double)s_bias[pr.y]);
+          logits[(size_t)pr.x * E + pr.y] = lv;
+          s_v[(pr.x - t0) * SV + pr.y] = lv;
+        }
+      }
+      __syncthreads();
+      for (int u = w; u < ntok; u += 8) {
+        const int tq = s_utok[u].x;
+        float rv[1], dummy[1];
+        bool taken[1];
+        rv[0] = lane < E ? s_v[(tq - t0) * SV + lane] : -__builtin_inff();
+        dummy[0] = 0.f;
+        taken[0] = lane >= E;
+        int se[KMAX];
+        float sv[KMAX], s1[KMAX], s2[KMAX];
+        group_topk<64, 1, KMAX, false>(rv, dummy, dummy, taken, k, se, sv, s1, s2);
+        group_gates<64, 1, KMAX>(rv, E, k, gate_mode, se, sv, tq, true, topk_idx, topk_gate,
+                                 mirror ? s_idx + (tq - t0) * k : nullptr, s_gt + (tq - t0) * k);
+      }
+    }
+    if (tail.dst_rank || tail.Ppart) {
+      __syncthreads();  // every token's final choices are written
+      constexpr int RB = BM / 64 > 0 ? BM / 64 : 1;  // 64-token blocks of this workgroup
+      const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+      if (tail.dst_rank && w < RB && (blockIdx.x * RB + w) * 64 < T) {
+        // ranks: position among the block's earlier tokens with the same choice
+        // (expert E marks an absent GShard second choice); counts per expert
+        const int b = blockIdx.x * RB + w, tr = b * 64 + lane;
+        const bool valid = tr < T;
+        const int Q = k * tail.nb;
+        const uint64_t vmask = __ballot(valid);
+        int ti[KMAX];
+        bool absent[KMAX];
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r) {
+          ti[r] = (valid && r < k) ? s_idx[(w * 64 + lane) * k + r] : 0;
+          absent[r] = false;
+        }
+        if (KMAX >= 2 && tail.second_u && valid)
+          absent[1] = !second_choice_taken(tail.second_u[tr], s_gt[(w * 64 + lane) * k],
+                                           s_gt[(w * 64 + lane) * k + 1]);
+        int* cnt_e = s_rc + w * 65;  // this wave's counts, expert E: absent
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r) {
+          if (r >= k) break;
+          const int my_e = absent[r] ? E : ti[r];
+          uint64_t same = vmask;
+          for (int bit = 0; bit < tail.nbits; ++bit) {
+            const uint64_t mb = __ballot((my_e >> bit) & 1);
+            same &= ((my_e >> bit) & 1) ? mb : ~mb;
+          }
+          if (valid) tail.dst_rank[(size_t)tr * k + r] = absent[r] ? kAbsentChoice : __popcll(same & lt);
+          // the first lane of each choice group writes the group's size (the
+          // wave's LDS operations complete in order)
+          cnt_e[lane] = 0;
+          if (lane == 0) cnt_e[64] = 0;
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          if (valid && (same & lt) == 0) cnt_e[my_e] = __popcll(same);
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          if (lane < E) tail.hist[(size_t)lane * Q + r * tail.nb + b] = cnt_e[lane];
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+      if (tail.Ppart) {
+        // loss partials: P(e | t) (softmax, or sigmoid scores over their sum),
+        // logsumexp^2 and first choices, lane = expert; each wave sums its
+        // tokens in order, the waves of a block are added in wave order
+        constexpr int WPB = 8 / RB, TPW = 64 / WPB;
+        const int rb = w / WPB;
+        double acc = 0.0, z = 0.0;
+        int cnt = 0;
+        for (int u = 0; u < TPW; ++u) {
+          const int tl = rb * 64 + (w % WPB) * TPW + u, tt = t0 + tl;
+          if (tt >= T) break;
+          const float vv = lane < E ? s_v[tl * SV + lane] : -__builtin_inff();
+          float m = vv;
+#pragma unroll
+          for (int d = 32; d > 0; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+          const float ex = lane < E ? expf(vv - m) : 0.0f;
+          float den = ex;
+#pragma unroll
+          for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
+          if (tail.score_fn) {
+            const float sc = lane < E ? 1.0f / (1.0f + expf(-vv)) : 0.0f;
+            float ssum = sc;
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) ssum += __shfl_xor(ssum, d, 64);
+            acc += (double)(sc / ssum);
+          } else {
+            acc += (double)(ex / den);
+          }
+          const double lse = (double)m + (double)logf(den);
+          z += lse * lse;
+          cnt += lane == s_idx[tl * k];
+        }
+        s_lp[w * 64 + lane] = acc;
+        s_lc[w * 64 + lane] = cnt;
+        if (lane == 0) s_lz[w] = z;
+        __syncthreads();
+        if (tid < RB * 64) {
+          const int rb2 = tid / 64, e = tid % 64, b = blockIdx.x * RB + rb2;
+          if (b * 64 < T) {
+            double ps = 0.0, zs = 0.0;
+            int cs = 0;
+            for (int q = 0; q < WPB; ++q) {
+              ps += s_lp[(rb2 * WPB + q) * 64 + e];
+              cs += s_lc[(rb2 * WPB + q) * 64 + e];
+              zs += s_lz[rb2 * WPB + q];
+            }
+            if (e < E) {
+              tail.Ppart[(size_t)e * tail.nb + b] = ps;
+              tail.Cpart[(size_t)e * tail.nb + b] = cs;
+            }
+            if (e == 0) tail.Zpart[b] = zs;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -596,31 +816,7 @@ __global__ void __launch_bounds__(256) router_refine_kernel(const uint16_t* __re
     const uint16_t* xr = x + (size_t)t * H;
     for (int c = w; c < rec.z; c += 4) {
       const int e = pairs[rec.y + c].y;
-      const uint16_t* w0 = wp + (size_t)e * H;
-      const uint16_t* w1 = wp + ((size_t)Ep + e) * H;
-      const uint16_t* w2 = wp + ((size_t)2 * Ep + e) * H;
-      double s = 0.0;
-      for (int h = 8 * lane; h < H; h += 512) {
-        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + h);
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(w0 + h);
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(w1 + h);
-        const u32x4_t cc = *reinterpret_cast<const u32x4_t*>(w2 + h);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int sh = half ? 0 : 16;
-            const uint32_t m = half ? 0xFFFF0000u : 0xFFFFFFFFu;
-            const double xd = (double)__uint_as_float((xv[q] << sh) & m);
-            const double wd = (double)__uint_as_float((a[q] << sh) & m) +
-                              (double)__uint_as_float((b[q] << sh) & m) +
-                              (double)__uint_as_float((cc[q] << sh) & m);
-            s = __builtin_fma(xd, wd, s);
-          }
-        }
-      }
-#pragma unroll
-      for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+      const double s = exact_dot(xr, wp, e, H, Ep);
       if (lane == 0) logits[(size_t)t * E + e] = (float)(s + (bias ? (double)bias[e] : 0.0));
     }
     __syncthreads();
@@ -664,6 +860,8 @@ struct SplitArgs {
   const SplitScratch* sc;
   int T, H, E, Ep, k, gate_mode;
   double c1;
+  SplitTail tail;  // requested epilogue work (null pointers: none)
+  int* fused;      // out: 1 ranks done, 2 loss partials done
 };
 
 template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX>
@@ -674,7 +872,16 @@ static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   const size_t red = (KS > 1) ? (sizeof(double) * (size_t)(KS - 1) * TG * EG * MF * WN * 4 * 64 +
                                  sizeof(float) * (size_t)(KS - 1) * TG * MF * 64)
                               : 0;
-  const size_t fz = FUSE ? sizeof(float) * (size_t)BM * (BN + 2) : 0;
+  // fused epilogue: staged logits and x norms, norm partials, local queue
+  const size_t fz = FUSE ? sizeof(float) * (size_t)BM * (BN + 2) + sizeof(double) * 512 + 16 * (size_t)BM +
+                               8 * (size_t)BM * BN + 8 * 512 + 4 * 512 + 8 * 8 + 8 * (size_t)BM * KMAX +
+                               4 * (size_t)(BM / 64 + 1) * 65
+                         : 0;
+  // the epilogue ranks and loss partials need whole 64-token blocks
+  constexpr bool kTail = FUSE && BM % 64 == 0;
+  SplitTail tail{};
+  if (kTail) tail = a.tail;
+  *a.fused = kTail ? ((tail.dst_rank ? 1 : 0) | (tail.Ppart ? 2 : 0)) : 0;
   if (red > shm) shm = red;
   if (fz > shm) shm = fz;
   auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX>;
@@ -683,7 +890,7 @@ static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   dim3 grid((a.T + BM - 1) / BM, a.Ep / BN);
   kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
                                      a.k, a.gate_mode, a.c1, a.topk_idx, a.topk_gate, a.sc->pairs, a.sc->utok,
-                                     a.sc->count);
+                                     a.sc->count, tail);
   return hipGetLastError();
 }
 
@@ -699,7 +906,8 @@ static hipError_t launch_split_fused(const SplitArgs& a, hipStream_t st) {
 
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
                                int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
-                               hipStream_t st) {
+                               const SplitEpilogue& ep, int* fused, hipStream_t st) {
+  *fused = 0;
   if (T == 0) return hipSuccess;
   const int Ep = split_router_ep(E), nk = H / kChunk;
   uint16_t* wp = static_cast<uint16_t*>(sc.wp);
@@ -713,7 +921,11 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   // slack; binary64 sums (here and in the exact definition) add at most
   // 4 H 2^-53 relative to sum|x*w|.
   const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
-  SplitArgs a{xb, wp, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1};
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
+  const SplitTail tail{ep.second_u, ep.dst_rank, ep.hist, nbits, (T + 63) / 64, ep.Ppart, ep.Zpart, ep.Cpart,
+                       ep.score_fn};
+  SplitArgs a{xb, wp, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
 
   if (E <= 16) {
     // 16 experts per wave; split h across waves when there are few tokens
@@ -732,17 +944,17 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
 
   const int je = (E + 63) / 64;
   const dim3 cgrid((T + 3) / 4), rgrid(T < 256 ? T : 256);
-  const bool fused = E <= 64;
+  const bool fused_tile = E <= 64;
 #define MOE_CR(J, K)                                                                                               \
   do {                                                                                                             \
-    if (!fused) {                                                                                                  \
+    if (!fused_tile) {                                                                                             \
       router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(logits, sc.xsq, sc.wn, bias, T, H, E, k, gate_mode, \
                                                                c1, topk_idx, topk_gate, sc.pairs, sc.utok,        \
                                                                sc.count);                                          \
       if ((err = hipGetLastError()) != hipSuccess) return err;                                                     \
+      router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,  \
+                                                              H, E, Ep, k, gate_mode, topk_idx, topk_gate);        \
     }                                                                                                              \
-    router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,    \
-                                                            H, E, Ep, k, gate_mode, topk_idx, topk_gate);          \
   } while (0)
 #define MOE_CR_K(J)              \
   if (k <= 1) MOE_CR(J, 1);      \
