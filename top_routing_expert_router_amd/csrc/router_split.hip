@@ -712,29 +712,56 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
         const int rb = w / WPB;
         double acc = 0.0, z = 0.0;
         int cnt = 0;
-        for (int u = 0; u < TPW; ++u) {
-          const int tl = rb * 64 + (w % WPB) * TPW + u, tt = t0 + tl;
-          if (tt >= T) break;
-          const float vv = lane < E ? s_v[tl * SV + lane] : -__builtin_inff();
-          float m = vv;
+        // the TPW tokens' reductions side by side (independent shuffle chains);
+        // tokens past T contribute nothing
+        constexpr int TU = TPW < 8 ? TPW : 8;
+        for (int u0 = 0; u0 < TPW; u0 += TU) {
+          float vv[TU], m[TU], den[TU];
+          bool ok[TU];
 #pragma unroll
-          for (int d = 32; d > 0; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-          const float ex = lane < E ? expf(vv - m) : 0.0f;
-          float den = ex;
-#pragma unroll
-          for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
-          if (tail.score_fn) {
-            const float sc = lane < E ? 1.0f / (1.0f + expf(-vv)) : 0.0f;
-            float ssum = sc;
-#pragma unroll
-            for (int d = 32; d > 0; d >>= 1) ssum += __shfl_xor(ssum, d, 64);
-            acc += (double)(sc / ssum);
-          } else {
-            acc += (double)(ex / den);
+          for (int u = 0; u < TU; ++u) {
+            const int tl = rb * 64 + (w % WPB) * TPW + u0 + u;
+            ok[u] = t0 + tl < T;
+            vv[u] = (ok[u] && lane < E) ? s_v[tl * SV + lane] : -__builtin_inff();
+            m[u] = vv[u];
           }
-          const double lse = (double)m + (double)logf(den);
-          z += lse * lse;
-          cnt += lane == s_idx[tl * k];
+#pragma unroll
+          for (int d = 32; d > 0; d >>= 1)
+#pragma unroll
+            for (int u = 0; u < TU; ++u) m[u] = fmaxf(m[u], __shfl_xor(m[u], d, 64));
+#pragma unroll
+          for (int u = 0; u < TU; ++u) den[u] = (ok[u] && lane < E) ? expf(vv[u] - m[u]) : 0.0f;
+          float ex[TU];
+#pragma unroll
+          for (int u = 0; u < TU; ++u) ex[u] = den[u];
+#pragma unroll
+          for (int d = 32; d > 0; d >>= 1)
+#pragma unroll
+            for (int u = 0; u < TU; ++u) den[u] += __shfl_xor(den[u], d, 64);
+          if (tail.score_fn) {
+            float sc[TU], ss[TU];
+#pragma unroll
+            for (int u = 0; u < TU; ++u) ss[u] = sc[u] = (ok[u] && lane < E) ? 1.0f / (1.0f + expf(-vv[u])) : 0.0f;
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1)
+#pragma unroll
+              for (int u = 0; u < TU; ++u) ss[u] += __shfl_xor(ss[u], d, 64);
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+              if (ok[u]) acc += (double)(sc[u] / ss[u]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+              if (ok[u]) acc += (double)(ex[u] / den[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < TU; ++u) {
+            if (!ok[u]) continue;
+            const int tl = rb * 64 + (w % WPB) * TPW + u0 + u;
+            const double lse = (double)m[u] + (double)logf(den[u]);
+            z += lse * lse;
+            cnt += lane == s_idx[tl * k];
+          }
         }
         s_lp[w * 64 + lane] = acc;
         s_lc[w * 64 + lane] = cnt;
@@ -923,8 +950,8 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
   int nbits = 0;
   while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
-  const SplitTail tail{ep.second_u, ep.dst_rank, ep.hist, nbits, (T + 63) / 64, ep.Ppart, ep.Zpart, ep.Cpart,
-                       ep.score_fn};
+  const SplitTail tail{ep.second_u, ep.dst_rank, ep.hist,  nbits,      (T + 63) / 64,
+                       ep.Ppart,    ep.Zpart,    ep.Cpart, ep.score_fn};
   SplitArgs a{xb, wp, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
 
   if (E <= 16) {
