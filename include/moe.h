@@ -218,8 +218,11 @@ moe_status moe_expert_ffn(const moe_config *cfg, const void *X, const moe_plan *
 moe_status moe_combine(const moe_config *cfg, const void *Y, const moe_plan *plan, const void *residual,
                        void *y, void *stream);
 
-/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn, moe_combine, in
- * that order on `stream`.  X and Y: device [R_max][H] dtype. */
+/* The whole layer on `stream`: moe_route, moe_dispatch, moe_expert_ffn,
+ * moe_combine.  Where the expert GEMMs run on the tiled bf16 path (bf16, H % 64
+ * == 0, 16-byte aligned buffers), the first GEMM reads the token rows of x
+ * through plan->row_token itself and the dispatch copy is not made.  X and Y:
+ * device [R_max][H] dtype scratch; their contents afterwards are unspecified. */
 moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, const float *bias, const void *W1,
                        const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,
                        void *X, void *Y, void *ws, size_t ws_bytes, void *stream);

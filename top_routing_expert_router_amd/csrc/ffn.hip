@@ -292,6 +292,27 @@ struct PipeTile {
   int e, row0, rows, n0;
 };
 
+// Row of A that packed row `row0 + r` reads when A is gathered (A = the token
+// rows x, gather = row_token): the 64 / CPR rows one load instruction covers
+// (rb .. rb + RPI - 1, wave-uniform) are looked up with scalar loads and each
+// lane takes its own; rows past the tile's `rows` read the tile's first row.
+template <int CPR>
+__device__ __forceinline__ int gathered_row(const int32_t* __restrict__ gather, int xrows, const PipeTile& t, int rb,
+                                            int lane) {
+  constexpr int RPI = 64 / CPR;
+  const int row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  const int rows = __builtin_amdgcn_readfirstlane(t.rows);
+  const int rbu = __builtin_amdgcn_readfirstlane(rb);
+  int v[RPI];
+#pragma unroll
+  for (int i = 0; i < RPI; ++i) v[i] = gather[row0 + (rbu + i < rows ? rbu + i : 0)];
+  const int sel = lane / CPR;
+  int tok = v[0];
+#pragma unroll
+  for (int i = 1; i < RPI; ++i) tok = sel == i ? v[i] : tok;
+  return tok < 0 ? 0 : (tok < xrows ? tok : xrows - 1);
+}
+
 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
 // as WGM (token direction) x NW / WGM (weight direction).
@@ -301,7 +322,8 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
                                                                    const uint16_t* __restrict__ W2,
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
-                                                                   int N, int K, int rmax) {
+                                                                   int N, int K, int rmax,
+                                                                   const int32_t* __restrict__ gather, int xrows) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -402,7 +424,8 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
       const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       if (r < BM) {
         const int rr = r < t.rows ? r : 0;
-        rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)(t.row0 + rr) * K + c * 8);
+        const int src = gather ? gathered_row<CPR>(gather, xrows, t, blk * 64 / CPR, lane) : t.row0 + rr;
+        rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
       } else {
         const int wr = r - BM;
         const uint16_t* base = (kGated && wr >= WR / 2) ? W2 : W;
@@ -557,7 +580,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
                                                                    const uint16_t* __restrict__ W2,
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
-                                                                   int N, int K, int rmax) {
+                                                                   int N, int K, int rmax,
+                                                                   const int32_t* __restrict__ gather, int xrows) {
   constexpr int NW = 8, BK = 64, CPR = 8, RSH = 1;
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;
@@ -645,7 +669,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
       const int p = (q * NW + w) * 64 + lane;
       const int r = p / CPR, c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       const int rr = r < t.rows ? r : 0;
-      rowA[q] = reinterpret_cast<uintptr_t>(A + (size_t)(t.row0 + rr) * K + c * 8);
+      const int src = gather ? gathered_row<CPR>(gather, xrows, t, (q * NW + w) * 64 / CPR, lane) : t.row0 + rr;
+      rowA[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
     }
   };
   auto set_rows_w = [&](const PipeTile& t) {
@@ -802,7 +827,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
 
 template <int BM, int WR, int SW, int WGM, int EPI>
 static hipError_t launch_ring(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
-                              int N, int K, int64_t R_max, int cus, hipStream_t st) {
+                              int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
+                              hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -814,13 +840,14 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI><<<dim3(grid), dim3(512), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
 }
 
 template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
-                              int N, int K, int64_t R_max, int cus, hipStream_t st) {
+                              int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
+                              hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -832,7 +859,7 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
 }
 
@@ -866,7 +893,8 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
 
 template <int EPI>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
-                             const int32_t* offsets, int E, int N, int K, int64_t R_max, hipStream_t st) {
+                             const int32_t* offsets, int E, int N, int K, int64_t R_max, hipStream_t st,
+                             const int32_t* gather = nullptr, int xrows = 0) {
   if (vec && bf16 && K % 64 == 0) {
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -886,25 +914,31 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       };
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
-          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
-      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
+      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
     }
-    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, st);
+    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
   }
+  if (gather) return hipErrorInvalidValue;  // only the tiled kernels read gathered rows
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
 }
 
+bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 64 == 0; }
+
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st) {
+                             int64_t R_max, hipStream_t st, const int32_t* gather, int xrows) {
   if (R_max == 0) return hipSuccess;
+  if (gather && !expert_ffn_gathers(bf16, vec, H)) return hipErrorInvalidValue;
   hipError_t err;
   switch (act) {
-    case 0: err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st); break;
-    case 1: err = launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st); break;
-    default: err = launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, st); break;
+    case 0: err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st, gather, xrows); break;
+    case 1: err = launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st, gather, xrows); break;
+    default:
+      err = launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, st, gather, xrows);
+      break;
   }
   if (err != hipSuccess) return err;
   return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, st);

@@ -69,9 +69,13 @@ hipError_t launch_slot_finalize(const int32_t* base, int Q, int nb, int T, int E
                                 int32_t* offsets, int32_t* n_dropped, int rmax, hipStream_t st);
 hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T, int H, int k, int rmax, bool bf16,
                            bool vec_ok, hipStream_t st);
+// gather (optional, when expert_ffn_gathers): X is the token rows x [xrows][H]
+// and packed row r of the first GEMM reads x[gather[r]] (the dispatch folded
+// into the GEMM's loads).
+bool expert_ffn_gathers(bool bf16, bool vec, int H);
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st);
+                             int64_t R_max, hipStream_t st, const int32_t* gather = nullptr, int xrows = 0);
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
                           int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st);
 

@@ -286,8 +286,21 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
   if (c->T > 0 && (!x || !y || !X || !Y)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
   if ((s = moe_route(c, x, Wg, bias, plan, ws, ws_bytes, stream)) != MOE_OK) return s;
-  if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
-  if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
+  // Where the tiled bf16 GEMMs run, the first one reads the token rows of x
+  // through plan->row_token itself and the dispatch copy is skipped (X unused).
+  const int64_t R_max = max_rows_of(c);
+  void* h = static_cast<char*>(ws) + layout_of(c).h;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(x) && aligned16(Y) && aligned16(W1) &&
+                   aligned16(W3) && aligned16(W2) && aligned16(h);
+  if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
+    hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
+                                          R_max, static_cast<hipStream_t>(stream), plan->row_token, c->T);
+    if (e != hipSuccess) return hip_fail(e, "expert_ffn");
+  } else {
+    if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
+    if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
+  }
   return moe_combine(c, Y, plan, residual, y, stream);
 }
 
