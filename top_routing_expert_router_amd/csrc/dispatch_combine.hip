@@ -51,19 +51,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ Y
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ residual, void* __restrict__ y,
                                                       int64_t total, int nch, int H, int k, int rmax,
-                                                      int vec_ok, int dropped_only) {
+                                                      int vec_ok) {
   const size_t eb = kBF16 ? 2 : 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / nch;
     const int64_t c = (i - t * nch) * 8;
-    if (dropped_only) {  // tokens with a kept assignment are written elsewhere
-      bool kept = false;
-      for (int r = 0; r < k; ++r) {
-        const int d = dst_row[t * k + r];
-        kept |= d >= 0 && d < rmax;
-      }
-      if (kept) continue;
-    }
     float acc[8];
     if (residual) {
       load8_f32<kBF16>(static_cast<const char*>(residual) + (size_t)t * H * eb, c, H, vec_ok, acc);
@@ -133,16 +125,16 @@ hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T
 }
 
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
-                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st, bool dropped_only) {
+                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int nch = (H + 7) / 8;
   const int64_t total = (int64_t)T * nch;
   if (bf16)
     combine_kernel<true><<<grid_for(total, 256), 256, 0, st>>>(Y, dst_row, gate, residual, y, total, nch, H, k,
-                                                                rmax, vec_ok, dropped_only);
+                                                                rmax, vec_ok);
   else
     combine_kernel<false><<<grid_for(total, 256), 256, 0, st>>>(Y, dst_row, gate, residual, y, total, nch, H, k,
-                                                                 rmax, vec_ok, dropped_only);
+                                                                 rmax, vec_ok);
   return hipGetLastError();
 }
 

@@ -313,19 +313,6 @@ __device__ __forceinline__ int gathered_row(const int32_t* __restrict__ gather, 
   return tok < 0 ? 0 : (tok < xrows ? tok : xrows - 1);
 }
 
-// Second-GEMM epilogue that finishes the layer for top-1 routing: packed row
-// `row` is the only assignment of token tok = row_token[row], so the output
-// y[tok] = residual[tok] + gate[tok] * Y[row] is written directly, with Y
-// rounded to bf16 first and one fused multiply-add per element, as the
-// separate combine computes it.
-struct CombineOut {
-  const int32_t* row_token;
-  const float* gate;        // topk_gate [T] (k = 1)
-  const uint16_t* residual;  // [T][N] or null
-  uint16_t* y;               // [T][N]
-};
-
-
 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
 // as WGM (token direction) x NW / WGM (weight direction).
@@ -336,8 +323,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows,
-                                                                   CombineOut co) {
+                                                                   const int32_t* __restrict__ gather, int xrows) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -496,56 +482,6 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
 
   // accumulator element 4g + jj of lane l: weight row 8g + 4(l / 32) + jj, token row l % 32
   auto store = [&](const PipeTile& t) {
-    if constexpr (EPI == EPI_NONE) {
-      if (co.y) {  // finish the layer: every load first, then the stores
-        int tok[MF];
-        float gv[MF];
-        uint2 rv[MF][HF][4];
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          const int m = wm * (MF * 32) + i * 32 + (lane & 31);
-          tok[i] = m < t.rows ? co.row_token[t.row0 + m] : -1;
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          gv[i] = tok[i] >= 0 ? co.gate[tok[i]] : 0.0f;
-#pragma unroll
-          for (int f = 0; f < HF; ++f)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-              rv[i][f][g] = (tok[i] >= 0 && n < N && co.residual)
-                                ? *reinterpret_cast<const uint2*>(co.residual + (size_t)tok[i] * N + n)
-                                : uint2{0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          if (tok[i] < 0) continue;
-#pragma unroll
-          for (int f = 0; f < HF; ++f)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-              if (n < N) {
-                const uint32_t rw[2] = {rv[i][f][g].x, rv[i][f][g].y};
-                float o[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                  const float yv = bf16_bits_to_f32(f32_to_bf16_bits(acc[f][i][4 * g + jj]));
-                  const float res = bf16_bits_to_f32((rw[jj / 2] >> (16 * (jj & 1))) & 0xFFFFu);
-                  o[jj] = __builtin_fmaf(gv[i], yv, res);
-                }
-                uint2 pk;
-                pk.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-                pk.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-                *reinterpret_cast<uint2*>(co.y + (size_t)tok[i] * N + n) = pk;
-              }
-            }
-        }
-        return;
-      }
-    }
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int m = wm * (MF * 32) + i * 32 + (lane & 31);
@@ -645,8 +581,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows,
-                                                                   CombineOut co) {
+                                                                   const int32_t* __restrict__ gather, int xrows) {
   constexpr int NW = 8, BK = 64, CPR = 8, RSH = 1;
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;
@@ -815,56 +750,6 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
         acc[f][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.w[f], fr.x[i], acc[f][i], 0, 0, 0);
   };
   auto store = [&](const PipeTile& t) {
-    if constexpr (EPI == EPI_NONE) {
-      if (co.y) {  // finish the layer: every load first, then the stores
-        int tok[MF];
-        float gv[MF];
-        uint2 rv[MF][HF][4];
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          const int m = wm * (MF * 32) + i * 32 + (lane & 31);
-          tok[i] = m < t.rows ? co.row_token[t.row0 + m] : -1;
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          gv[i] = tok[i] >= 0 ? co.gate[tok[i]] : 0.0f;
-#pragma unroll
-          for (int f = 0; f < HF; ++f)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-              rv[i][f][g] = (tok[i] >= 0 && n < N && co.residual)
-                                ? *reinterpret_cast<const uint2*>(co.residual + (size_t)tok[i] * N + n)
-                                : uint2{0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          if (tok[i] < 0) continue;
-#pragma unroll
-          for (int f = 0; f < HF; ++f)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-              if (n < N) {
-                const uint32_t rw[2] = {rv[i][f][g].x, rv[i][f][g].y};
-                float o[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                  const float yv = bf16_bits_to_f32(f32_to_bf16_bits(acc[f][i][4 * g + jj]));
-                  const float res = bf16_bits_to_f32((rw[jj / 2] >> (16 * (jj & 1))) & 0xFFFFu);
-                  o[jj] = __builtin_fmaf(gv[i], yv, res);
-                }
-                uint2 pk;
-                pk.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-                pk.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-                *reinterpret_cast<uint2*>(co.y + (size_t)tok[i] * N + n) = pk;
-              }
-            }
-        }
-        return;
-      }
-    }
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int m = wm * (MF * 32) + i * 32 + (lane & 31);
@@ -943,7 +828,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
 template <int BM, int WR, int SW, int WGM, int EPI>
 static hipError_t launch_ring(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              const CombineOut& co, hipStream_t st) {
+                              hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -955,14 +840,14 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI><<<dim3(grid), dim3(512), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, co);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
 }
 
 template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              const CombineOut& co, hipStream_t st) {
+                              hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -974,7 +859,7 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, co);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
 }
 
@@ -1009,7 +894,7 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
 template <int EPI>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
                              const int32_t* offsets, int E, int N, int K, int64_t R_max, hipStream_t st,
-                             const int32_t* gather = nullptr, int xrows = 0, const CombineOut& co = CombineOut{}) {
+                             const int32_t* gather = nullptr, int xrows = 0) {
   if (vec && bf16 && K % 64 == 0) {
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -1029,28 +914,24 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       };
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
-          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, co, st);
-      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, co, st);
+          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
+      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
     }
-    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, co, st);
+    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
   }
-  if (gather || co.y) return hipErrorInvalidValue;  // only the tiled kernels gather rows or finish the layer
+  if (gather) return hipErrorInvalidValue;  // only the tiled kernels read gathered rows
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
 }
 
 bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 64 == 0; }
-bool expert_ffn_combines(bool bf16, bool vec, int H, int F) { return bf16 && vec && F % 64 == 0 && H % 4 == 0; }
 
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st, const int32_t* gather, int xrows,
-                             const int32_t* row_token, const float* gate, const void* residual, void* y) {
+                             int64_t R_max, hipStream_t st, const int32_t* gather, int xrows) {
   if (R_max == 0) return hipSuccess;
   if (gather && !expert_ffn_gathers(bf16, vec, H)) return hipErrorInvalidValue;
-  if (y && !expert_ffn_combines(bf16, vec, H, F)) return hipErrorInvalidValue;
-  const CombineOut co{row_token, gate, static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y)};
   hipError_t err;
   switch (act) {
     case 0: err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st, gather, xrows); break;
@@ -1060,7 +941,7 @@ hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, cons
       break;
   }
   if (err != hipSuccess) return err;
-  return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, st, nullptr, 0, co);
+  return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, st);
 }
 
 }  // namespace moe

@@ -72,19 +72,11 @@ hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T
 // gather (optional, when expert_ffn_gathers): X is the token rows x [xrows][H]
 // and packed row r of the first GEMM reads x[gather[r]] (the dispatch folded
 // into the GEMM's loads).
-// y (optional, top-1 routing, when expert_ffn_combines): the second GEMM
-// writes y[row_token[r]] = residual + gate * Y[r] instead of Y (the combine of
-// kept tokens; dropped tokens are the caller's).
 bool expert_ffn_gathers(bool bf16, bool vec, int H);
-bool expert_ffn_combines(bool bf16, bool vec, int H, int F);
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st, const int32_t* gather = nullptr, int xrows = 0,
-                             const int32_t* row_token = nullptr, const float* gate = nullptr,
-                             const void* residual = nullptr, void* y = nullptr);
-// dropped_only: write only the tokens with no kept assignment (y = residual).
+                             int64_t R_max, hipStream_t st, const int32_t* gather = nullptr, int xrows = 0);
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
-                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st,
-                          bool dropped_only = false);
+                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st);
 
 }  // namespace moe

@@ -294,20 +294,9 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
   const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(x) && aligned16(Y) && aligned16(W1) &&
                    aligned16(W3) && aligned16(W2) && aligned16(h);
   if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
-    // With top-1 routing the second GEMM also finishes the kept tokens' rows of
-    // y; a light pass writes the dropped ones.
-    const bool fin = c->k == 1 && moe::expert_ffn_combines(bf16, vec, c->H, c->F) && aligned16(y) &&
-                     aligned16(residual);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
-                                          R_max, st, plan->row_token, c->T, plan->row_token, plan->topk_gate,
-                                          fin ? residual : nullptr, fin ? y : nullptr);
+                                          R_max, static_cast<hipStream_t>(stream), plan->row_token, c->T);
     if (e != hipSuccess) return hip_fail(e, "expert_ffn");
-    if (fin) {
-      e = moe::launch_combine(Y, plan->dst_row, plan->topk_gate, residual, y, c->T, c->H, c->k, (int)R_max, bf16,
-                              c->H % 8 == 0 && aligned16(residual) && aligned16(y), st, true);
-      return e == hipSuccess ? MOE_OK : hip_fail(e, "combine");
-    }
   } else {
     if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
     if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
