@@ -208,11 +208,26 @@ def token_outputs(tokens, x, dtype, act, plan, w1, w3, w2, residual=None):
     return y
 
 
+def shared_expert(x, dtype, act, ws1, ws3, ws2, tokens=None):
+    """The shared expert ("Expert-parallel MoE training" explainer, layer walk-through:
+    a dense MLP outside the router and the all-to-all, computed on every token and
+    added to the routed experts' output; Megatron-Core SharedExpertMLP, DeepSpeed's
+    Residual-MoE dense branch).  Read here as one more FFN of the routed experts' form
+    (same activation; ws1/ws3 [1, Fs, H], ws2 [1, H, Fs]) applied to every token (or
+    to the listed tokens), in binary64 like expert_rows.  Returns [n, H] float64."""
+    x = _c(x, _act_np(dtype))
+    rows = x if tokens is None else x[np.asarray(tokens, np.int64)]
+    return expert_rows(rows, np.zeros(rows.shape[0], np.int32), dtype, act, ws1, ws3, ws2)
+
+
 def forward(x, dtype, wg, bias, w1, w3, w2, k, gate_mode, act, C, residual=None, score_fn=SOFTMAX,
-            drop_policy=DROP_POSITION, second_u=None):
-    """Whole layer: route -> dispatch -> expert FFN -> combine.  Returns (y float64, plan, X, Y)."""
+            drop_policy=DROP_POSITION, second_u=None, shared=None):
+    """Whole layer: route -> dispatch -> expert FFN -> combine (+ the shared expert's
+    output when shared = (ws1, ws3, ws2)).  Returns (y float64, plan, X, Y)."""
     plan = route(x, dtype, wg, bias, k, gate_mode, C, score_fn, drop_policy, second_u)
     X = dispatch(x, dtype, plan)
     Y = expert_ffn(X, plan["offsets"], dtype, act, w1, w3, w2)
     y = combine(Y, plan, dtype, residual)
+    if shared is not None:
+        y = y + shared_expert(x, dtype, act, *shared)
     return y, plan, X, Y

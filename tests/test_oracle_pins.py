@@ -344,6 +344,53 @@ def test_single_expert_is_dense_ffn(act, dtype):
     assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("act,dtype", [(oracle.RELU, oracle.F32), (oracle.GELU, oracle.BF16),
+                                       (oracle.SWIGLU, oracle.BF16)])
+def test_shared_expert_is_dense_ffn_added_to_every_token(act, dtype):
+    # The shared expert bypasses the router and is added to the routed output for
+    # every token ("Expert-parallel MoE training" explainer, layer walk-through).
+    T, H, F, E, k, Fs = 30, 16, 20, 4, 2, 24
+    dt = "f32" if dtype == oracle.F32 else "bf16"
+    x = synth.normal(61, T * H, 1.0, dt).reshape(T, H)
+    wg = synth.normal(62, H * E, 0.5, "f32").reshape(H, E)
+    w1 = synth.normal(63, E * F * H, 0.3, dt).reshape(E, F, H)
+    w3 = synth.normal(64, E * F * H, 0.3, dt).reshape(E, F, H) if act == oracle.SWIGLU else None
+    w2 = synth.normal(65, E * H * F, 0.3, dt).reshape(E, H, F)
+    s1 = synth.normal(66, Fs * H, 0.3, dt).reshape(1, Fs, H)
+    s3 = synth.normal(67, Fs * H, 0.3, dt).reshape(1, Fs, H) if act == oracle.SWIGLU else None
+    s2 = synth.normal(68, H * Fs, 0.3, dt).reshape(1, H, Fs)
+    dense = _dense_ffn_np(_decode(x, dtype), _decode(s1[0], dtype), None if s3 is None else _decode(s3[0], dtype),
+                          _decode(s2[0], dtype), act)
+    assert np.allclose(oracle.shared_expert(x, dtype, act, s1, s3, s2), dense, rtol=1e-12, atol=1e-12)
+    C = oracle.capacity(T, k, E, 1.0)
+    y0, plan0, _, _ = oracle.forward(x, dtype, wg, None, w1, w3, w2, k, oracle.SOFTMAX_TOPK, act, C, residual=x)
+    y1, plan1, _, _ = oracle.forward(x, dtype, wg, None, w1, w3, w2, k, oracle.SOFTMAX_TOPK, act, C, residual=x,
+                                     shared=(s1, s3, s2))
+    assert np.array_equal(plan0["dst_row"], plan1["dst_row"])
+    assert np.allclose(y1 - y0, dense, rtol=1e-12, atol=1e-12)
+    # dropped tokens get residual + shared output only
+    dropped = (plan1["dst_row"] < 0).all(1)
+    assert np.allclose(y1[dropped], _decode(x, dtype)[dropped] + dense[dropped], rtol=1e-12, atol=1e-12)
+
+
+def test_shared_expert_closed_forms():
+    T, H = 12, 8
+    x = synth.normal(71, T * H, 1.0, "f32").reshape(T, H)
+    eye = np.eye(H, dtype=np.float32)[None]
+    # ReLU with identity weights: the shared output is relu(x)
+    got = oracle.shared_expert(x, oracle.F32, oracle.RELU, eye, None, eye)
+    assert np.array_equal(got, np.maximum(x.astype(np.float64), 0.0))
+    # a zero output projection adds nothing
+    wg = synth.normal(72, H * 3, 0.5, "f32").reshape(H, 3)
+    w1 = synth.normal(73, 3 * 5 * H, 0.3, "f32").reshape(3, 5, H)
+    w2 = synth.normal(74, 3 * H * 5, 0.3, "f32").reshape(3, H, 5)
+    s1 = synth.normal(75, 6 * H, 0.3, "f32").reshape(1, 6, H)
+    y0, *_ = oracle.forward(x, oracle.F32, wg, None, w1, None, w2, 1, oracle.SOFTMAX_TOPK, oracle.GELU, None)
+    y1, *_ = oracle.forward(x, oracle.F32, wg, None, w1, None, w2, 1, oracle.SOFTMAX_TOPK, oracle.GELU, None,
+                            shared=(s1, None, np.zeros((1, H, 6), np.float32)))
+    assert np.array_equal(y0, y1)
+
+
 def test_identical_experts_renormalised_equal_dense():
     T, H, F, E, k = 30, 16, 20, 5, 3
     x = synth.normal(41, T * H, 1.0, "bf16").reshape(T, H)

@@ -27,6 +27,7 @@ SOFTMAX_TOPK, SOFTMAX_TOPK_RENORM, TOPK_SOFTMAX = 0, 1, 2
 RELU, GELU, SWIGLU = 0, 1, 2
 
 J_X, J_WG, J_BIAS, J_W1, J_W3, J_W2 = 0, 1, 2, 3, 4, 5
+J_S1, J_S3, J_S2 = 6, 7, 8  # shared expert
 
 
 @dataclass(frozen=True)
@@ -122,6 +123,15 @@ def gen_expert_weight(run: Run, which: str, experts=None):
     if experts is None:
         return normal(seed, run.E * per, sigma, dt).reshape(run.E, out_f, in_f)
     return {int(e): normal(seed, per, sigma, dt, first=int(e) * per).reshape(out_f, in_f) for e in experts}
+
+
+def gen_shared_weight(run: Run, which: str, Fs: int):
+    """Shared-expert weights (one dense FFN of width Fs, same initialisation rule as the
+    routed experts): "s1" [1,Fs,H], "s3" (SwiGLU up) [1,Fs,H], "s2" [1,H,Fs]."""
+    j = {"s1": J_S1, "s3": J_S3, "s2": J_S2}[which]
+    out_f, in_f = (Fs, run.H) if which in ("s1", "s3") else (run.H, Fs)
+    return normal(tensor_seed(run.run_id, j), out_f * in_f, math.sqrt(run.s / in_f),
+                  act_dtype(run)).reshape(1, out_f, in_f)
 
 
 def gen_all(run: Run):
