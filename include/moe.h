@@ -135,6 +135,7 @@ typedef struct {
   int32_t score_fn;       /* moe_score_fn                                       */
   int32_t drop_policy;    /* moe_drop_policy                                    */
   int32_t second_policy;  /* moe_second_policy (RANDOM requires k = 2)         */
+  int32_t shared_F;       /* width of the shared expert, 0 = none (see moe_shared_expert) */
 } moe_config;
 
 /* Routing plan: device arrays, allocated by the caller, written by moe_route. */
@@ -170,8 +171,9 @@ int64_t moe_capacity(const moe_config *cfg);
  * must hold.  -1 when the configuration is invalid. */
 int64_t moe_max_rows(const moe_config *cfg);
 
-/* Device workspace bytes that moe_route / moe_expert_ffn / moe_forward need
- * (0 when the configuration is invalid). */
+/* Device workspace bytes that moe_route / moe_expert_ffn / moe_forward need, and
+ * with shared_F > 0 also moe_shared_expert / moe_forward_shared (0 when the
+ * configuration is invalid). */
 size_t moe_workspace_bytes(const moe_config *cfg);
 
 const char *moe_status_str(moe_status s);
@@ -226,6 +228,31 @@ moe_status moe_combine(const moe_config *cfg, const void *Y, const moe_plan *pla
 moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, const float *bias, const void *W1,
                        const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,
                        void *X, void *Y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- shared expert ([EP] layer walk-through: a dense MLP outside the router
+ * and the all-to-all, run on every token, its output added to the routed
+ * experts' output; Megatron-Core SharedExpertMLP, DeepSpeed Residual-MoE).  Taken
+ * as one more FFN of the routed experts' form: activation cfg->act, width
+ * cfg->shared_F (> 0 for these calls), weights Ws1 (and Ws3 iff SwiGLU)
+ * [shared_F][H], Ws2 [H][shared_F], all dtype, [out][in] row-major like W1/W2. */
+
+/* Ys[t] = S(x[t]) for every token.  x: device [T][H]; Ys: device [T][H] dtype
+ * (bf16 runs: bf16 MFMA, fp32 accumulation, hidden activation rounded to dtype).
+ * ws: device, >= moe_workspace_bytes (holds the hidden activation). */
+moe_status moe_shared_expert(const moe_config *cfg, const void *x, const void *Ws1, const void *Ws3,
+                             const void *Ws2, void *Ys, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_combine plus the shared output: y[t] = residual[t] + sum_r g[t][r] Y[dst_row[t][r]]
+ * + Ys[t], in that order in fp32, rounded once to dtype.  Ys: device [T][H] dtype. */
+moe_status moe_combine_shared(const moe_config *cfg, const void *Y, const moe_plan *plan, const void *residual,
+                              const void *Ys, void *y, void *stream);
+
+/* moe_forward with the shared expert: route, dispatch, routed experts, shared
+ * expert (its output kept in the workspace), moe_combine_shared. */
+moe_status moe_forward_shared(const moe_config *cfg, const void *x, const float *Wg, const float *bias,
+                              const void *W1, const void *W3, const void *W2, const void *Ws1, const void *Ws3,
+                              const void *Ws2, const void *residual, void *y, const moe_plan *plan, void *X, void *Y,
+                              void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -46,7 +46,7 @@ def _cfg(**kw):
     dict(capacity_factor=0.0), dict(capacity_factor=-1.0), dict(capacity_factor=float("nan")),
     dict(capacity_factor=float("inf")), dict(aux_mode=2), dict(aux_mode=-1), dict(aux_coeff=float("nan")),
     dict(z_coeff=float("inf")), dict(score_fn=2), dict(drop_policy=2), dict(drop_policy=-1),
-    dict(second_policy=2), dict(second_policy=1, k=1), dict(second_policy=1, k=3),
+    dict(second_policy=2), dict(second_policy=1, k=1), dict(second_policy=1, k=3), dict(shared_F=-1),
 ])
 def test_validate_rejects(kw):
     c = _cfg(**kw)
@@ -111,6 +111,25 @@ def test_entry_points_reject_before_launch():
     assert L.moe_forward(ctypes.byref(cc), 256, None, None, 256, None, 256, None, 256, ctypes.byref(good), 256, 256,
                          256, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_validate(None) == B.MOE_ERR_INVALID_ARG
+    # shared expert: needs shared_F > 0, its weights (Ws3 iff SwiGLU) and the workspace
+    sh = _cfg(shared_F=384)
+    shc = sh.c()
+    ws_need = B.workspace_bytes(sh)
+    assert ws_need >= sh.T * sh.shared_F * 2 + sh.T * sh.H * 2
+    assert L.moe_shared_expert(ctypes.byref(cc), 256, 256, None, 256, 256, 256, 1 << 40, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_shared_expert(ctypes.byref(shc), 256, None, None, 256, 256, 256, 1 << 40, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_shared_expert(ctypes.byref(shc), 256, 256, 256, 256, 256, 256, 1 << 40, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_shared_expert(ctypes.byref(shc), 256, 256, None, 256, 256, 256, ws_need - 1, None) == \
+        B.MOE_ERR_WORKSPACE
+    assert L.moe_combine_shared(ctypes.byref(shc), 256, ctypes.byref(good), None, None, 256, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_shared(ctypes.byref(cc), 256, 256, None, 256, None, 256, 256, None, 256, None, 256,
+                                ctypes.byref(good), 256, 256, 256, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_shared(ctypes.byref(shc), 256, 256, None, 256, None, 256, 256, None, 256, None, 256,
+                                ctypes.byref(good), 256, 256, 256, ws_need - 1, None) == B.MOE_ERR_WORKSPACE
 
 
 def test_status_strings():

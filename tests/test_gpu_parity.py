@@ -609,3 +609,95 @@ def test_gshard_random_second_choice_forward(gpu):
     torch.cuda.synchronize()
     _check_route(r, plan, oplan)
     U.assert_close(U.host(y), yref, True, "gshard forward")
+
+
+# ---- shared expert: a dense FFN on every token, added to the routed output
+def _shared_weights(r, Fs):
+    s1 = recipes.gen_shared_weight(r, "s1", Fs)
+    s3 = recipes.gen_shared_weight(r, "s3", Fs) if r.act == recipes.SWIGLU else None
+    s2 = recipes.gen_shared_weight(r, "s2", Fs)
+    return s1, s3, s2
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("width", ["F", "ragged"])
+def test_shared_expert(gpu, name, width):
+    import torch
+
+    r = recipes.SMALL[name]
+    Fs = r.F if width == "F" else r.F + 40  # ragged: not a whole number of 64-wide k steps
+    x = recipes.gen_x(r)
+    sw = _shared_weights(r, Fs)
+    cfg = B.MoEConfig.from_run(r)
+    cfg.shared_F = Fs
+    tdt = torch.bfloat16 if r.dtype == recipes.BF16 else torch.float32
+    Ys = torch.empty((r.T, r.H), dtype=tdt, device=gpu)
+    B.shared_expert(cfg, U.dev(x, gpu), *(U.dev(a, gpu) for a in sw), Ys, B.alloc_workspace(cfg, gpu))
+    torch.cuda.synchronize()
+    ref = oracle.shared_expert(x, r.dtype, r.act, *sw)
+    U.assert_close(U.host(Ys), ref, r.dtype == recipes.BF16, f"shared expert run {r.name} Fs={Fs}")
+
+
+def _gpu_forward_shared(r, gpu, d, sw, Fs, weights=None, residual=False):
+    import torch
+
+    cfg = B.MoEConfig.from_run(r)
+    cfg.shared_F = Fs
+    tdt = torch.bfloat16 if r.dtype == recipes.BF16 else torch.float32
+    rmax = B.max_rows(cfg)
+    xd = U.dev(d["x"], gpu)
+    if weights is None:
+        weights = (U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu))
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    X = torch.empty((max(rmax, 1), r.H), dtype=tdt, device=gpu)
+    Y = torch.empty_like(X)
+    y = torch.empty((r.T, r.H), dtype=tdt, device=gpu)
+    B.forward_shared(cfg, xd, U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), *weights, *(U.dev(a, gpu) for a in sw),
+                     xd if residual else None, y, plan, X, Y, B.alloc_workspace(cfg, gpu))
+    torch.cuda.synchronize()
+    return plan, y
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_forward_shared_small(gpu, name):
+    r = recipes.SMALL[name]
+    d = recipes.gen_all(r)
+    Fs = r.F
+    sw = _shared_weights(r, Fs)
+    yref, oplan, _, _ = oracle.forward(d["x"], r.dtype, d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], r.k,
+                                       r.gate_mode, r.act, _cap(r), shared=sw)
+    gplan, y = _gpu_forward_shared(r, gpu, d, sw, Fs)
+    _check_route(r, gplan, oplan)
+    U.assert_close(U.host(y), yref, r.dtype == recipes.BF16, f"forward+shared run {r.name}")
+
+
+@pytest.mark.parametrize("name", ["2", "5"])
+def test_forward_shared_full_size_sampled(gpu, name):
+    """Full workload with a shared expert of the routed experts' width (one shared expert
+    next to the routed ones, as in the DeepSeek-R1 shape); routing on every token,
+    outputs on a sample of tokens."""
+    r = recipes.RUNS[name]
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    oplan = _oracle_route(r, x, wg, bias)
+    rng = np.random.default_rng(int(r.run_id) + 7)
+    toks = set(rng.choice(r.T, size=16, replace=False).tolist()) | {0, r.T - 1}
+    dropped = np.nonzero((oplan["dst_row"] < 0).all(1))[0]
+    toks |= set(dropped[:4].tolist())
+    toks = np.array(sorted(toks), np.int64)
+    need = sorted(set(oplan["topk_idx"][toks].ravel().tolist()))
+    w1, k1 = U.upload_expert_weight(r, "w1", gpu, keep=need)
+    w3, k3 = U.upload_expert_weight(r, "w3", gpu, keep=need) if r.act == recipes.SWIGLU else (None, {})
+    w2, k2 = U.upload_expert_weight(r, "w2", gpu, keep=need)
+    sw = _shared_weights(r, r.F)
+    gplan, y = _gpu_forward_shared(r, gpu, dict(x=x, wg=wg, bias=bias), sw, r.F, weights=(w1, w3, w2))
+    _check_route(r, gplan, oplan)
+    remap = {e: i for i, e in enumerate(need)}
+    sub = {n: oplan[n][toks] for n in ("topk_gate", "dst_row")}
+    sub["topk_idx"] = np.vectorize(remap.get)(oplan["topk_idx"][toks]).astype(np.int32)
+    cw1 = np.stack([k1[e] for e in need])
+    cw3 = np.stack([k3[e] for e in need]) if w3 is not None else None
+    cw2 = np.stack([k2[e] for e in need])
+    yref = oracle.token_outputs(np.arange(len(toks)), x[toks], r.dtype, r.act, sub, cw1, cw3, cw2)
+    yref = yref + oracle.shared_expert(x, r.dtype, r.act, *sw, tokens=toks)
+    U.assert_close(U.host(y)[toks], yref, r.dtype == recipes.BF16, f"forward+shared full-size run {r.name} sample")

@@ -17,7 +17,8 @@ RELU, GELU, SWIGLU = 0, 1, 2
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 
 EXPORTS = ("moe_validate", "moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_status_str",
-           "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward")
+           "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_shared_expert", "moe_combine_shared", "moe_forward_shared")
 
 
 class MoEError(RuntimeError):
@@ -32,7 +33,7 @@ class _Config(ctypes.Structure):
                 ("act", ctypes.c_int32), ("dropless", ctypes.c_int32), ("min_capacity", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_double), ("aux_mode", ctypes.c_int32), ("aux_coeff", ctypes.c_double),
                 ("z_coeff", ctypes.c_double), ("score_fn", ctypes.c_int32), ("drop_policy", ctypes.c_int32),
-                ("second_policy", ctypes.c_int32)]
+                ("second_policy", ctypes.c_int32), ("shared_F", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -59,11 +60,12 @@ class MoEConfig:
     score_fn: int = 0  # 0: softmax, 1: sigmoid
     drop_policy: int = 0  # 0: position, 1: probs
     second_policy: int = 0  # 0: plain top-k, 1: GShard's random second choice (k = 2, plan["second_u"])
+    shared_F: int = 0  # width of the shared expert, 0 = none
 
     def c(self):
         return _Config(self.T, self.H, self.E, self.k, self.F, self.dtype, self.gate_mode, self.act, self.dropless,
                        self.min_capacity, float(self.capacity_factor), self.aux_mode, float(self.aux_coeff),
-                       float(self.z_coeff), self.score_fn, self.drop_policy, self.second_policy)
+                       float(self.z_coeff), self.score_fn, self.drop_policy, self.second_policy, self.shared_F)
 
     @classmethod
     def from_run(cls, run):
@@ -106,6 +108,12 @@ def lib():
         L.moe_combine.argtypes = [cfgp, vp, planp, vp, vp, vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, planp, vp, vp, vp, sz, vp]
+        L.moe_shared_expert.restype = ctypes.c_int
+        L.moe_shared_expert.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_combine_shared.restype = ctypes.c_int
+        L.moe_combine_shared.argtypes = [cfgp, vp, planp, vp, vp, vp, vp]
+        L.moe_forward_shared.restype = ctypes.c_int
+        L.moe_forward_shared.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, planp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -214,3 +222,24 @@ def forward(cfg, x, wg, bias, w1, w3, w2, residual, y, plan, X, Y, ws, stream=No
                            _ptr(residual), _ptr(y), ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(ws),
                            ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "moe_forward")
+
+
+def shared_expert(cfg, x, ws1, ws3, ws2, Ys, ws, stream=None):
+    c = cfg.c()
+    st = lib().moe_shared_expert(ctypes.byref(c), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(Ys), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream))
+    _check(st, "moe_shared_expert")
+
+
+def combine_shared(cfg, Y, plan, residual, Ys, y, stream=None):
+    c, p = cfg.c(), _plan_struct(plan)
+    _check(lib().moe_combine_shared(ctypes.byref(c), _ptr(Y), ctypes.byref(p), _ptr(residual), _ptr(Ys), _ptr(y),
+                                    _stream(stream)), "moe_combine_shared")
+
+
+def forward_shared(cfg, x, wg, bias, w1, w3, w2, ws1, ws3, ws2, residual, y, plan, X, Y, ws, stream=None):
+    c, p = cfg.c(), _plan_struct(plan)
+    st = lib().moe_forward_shared(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2),
+                                  _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(residual), _ptr(y), ctypes.byref(p), _ptr(X),
+                                  _ptr(Y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(st, "moe_forward_shared")

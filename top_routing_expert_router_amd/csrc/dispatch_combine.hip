@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ Y
                                                       const float* __restrict__ gate,
                                                       const void* __restrict__ residual, void* __restrict__ y,
                                                       int64_t total, int nch, int H, int k, int rmax,
-                                                      int vec_ok) {
+                                                      int vec_ok, const void* __restrict__ shared) {
   const size_t eb = kBF16 ? 2 : 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / nch;
@@ -71,6 +71,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ Y
       load8_f32<kBF16>(static_cast<const char*>(Y) + (size_t)d * H * eb, c, H, vec_ok, v);
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(g, v[j], acc[j]);
+    }
+    if (shared) {  // the shared expert's output, added last
+      float v[8];
+      load8_f32<kBF16>(static_cast<const char*>(shared) + (size_t)t * H * eb, c, H, vec_ok, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += v[j];
     }
     if (kBF16) {
       uint16_t* out = static_cast<uint16_t*>(y) + (size_t)t * H;
@@ -124,17 +130,29 @@ hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T
   return hipGetLastError();
 }
 
+__global__ void dense_offsets_kernel(int32_t* off, int T) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+  }
+}
+
+hipError_t launch_dense_offsets(int32_t* off, int T, hipStream_t st) {
+  dense_offsets_kernel<<<1, 64, 0, st>>>(off, T);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
-                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st) {
+                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st, const void* shared) {
   if (T == 0) return hipSuccess;
   const int nch = (H + 7) / 8;
   const int64_t total = (int64_t)T * nch;
   if (bf16)
     combine_kernel<true><<<grid_for(total, 256), 256, 0, st>>>(Y, dst_row, gate, residual, y, total, nch, H, k,
-                                                                rmax, vec_ok);
+                                                                rmax, vec_ok, shared);
   else
     combine_kernel<false><<<grid_for(total, 256), 256, 0, st>>>(Y, dst_row, gate, residual, y, total, nch, H, k,
-                                                                 rmax, vec_ok);
+                                                                 rmax, vec_ok, shared);
   return hipGetLastError();
 }
 

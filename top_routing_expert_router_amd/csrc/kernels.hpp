@@ -76,7 +76,11 @@ bool expert_ffn_gathers(bool bf16, bool vec, int H);
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
                              int64_t R_max, hipStream_t st, const int32_t* gather = nullptr, int xrows = 0);
+// shared (optional): the shared expert's output [T][H], added after the routed terms.
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
-                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st);
+                          int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st,
+                          const void* shared = nullptr);
+// off[0] = 0, off[1] = T: the offsets of one expert holding every token.
+hipError_t launch_dense_offsets(int32_t* off, int T, hipStream_t st);
 
 }  // namespace moe

@@ -56,6 +56,7 @@ struct Layout {
   int nb, Q;
   bool split;  // split-bf16 router buffers present
   size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, lp, lz, lc, lkey, lq, nslot, route_end, h, ffn_end, total;
+  size_t hs, ys, soff, shared_end;  // shared expert: hidden [T][Fs], output [T][H], offsets {0, T}
 };
 
 // The split-bf16 router runs for bf16 activations with H a multiple of 64 and a
@@ -98,6 +99,15 @@ Layout layout_of(const moe_config* c) {
   L.h = 0;
   L.ffn_end = align_up(eb * (size_t)max_rows_of(c) * (size_t)c->F);
   L.total = L.route_end > L.ffn_end ? L.route_end : L.ffn_end;
+  // the shared expert runs after the routed experts: its buffers reuse the same space
+  L.hs = L.ys = L.soff = L.shared_end = 0;
+  if (c->shared_F > 0) {
+    L.hs = 0;
+    L.ys = align_up(eb * (size_t)c->T * (size_t)c->shared_F);
+    L.soff = L.ys + align_up(eb * (size_t)c->T * (size_t)c->H);
+    L.shared_end = L.soff + kAlign;
+    if (L.shared_end > L.total) L.total = L.shared_end;
+  }
   if (L.total == 0) L.total = kAlign;
   return L;
 }
@@ -131,6 +141,7 @@ moe_status moe_validate(const moe_config* c) {
   if (c->drop_policy != MOE_DROP_POSITION && c->drop_policy != MOE_DROP_PROBS) return MOE_ERR_INVALID_ARG;
   if (c->second_policy != MOE_SECOND_ALWAYS && c->second_policy != MOE_SECOND_RANDOM) return MOE_ERR_INVALID_ARG;
   if (c->second_policy == MOE_SECOND_RANDOM && c->k != 2) return MOE_ERR_INVALID_ARG;
+  if (c->shared_F < 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -302,6 +313,73 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
     if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
   }
   return moe_combine(c, Y, plan, residual, y, stream);
+}
+
+moe_status moe_shared_expert(const moe_config* c, const void* x, const void* Ws1, const void* Ws3, const void* Ws2,
+                             void* Ys, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (c->shared_F < 1 || !Ws1 || !Ws2 || (c->act == MOE_SWIGLU) != (Ws3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && (!x || !Ys)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(c);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (c->T == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  void* hs = w + L.hs;
+  int32_t* off = reinterpret_cast<int32_t*>(w + L.soff);
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && c->shared_F % 8 == 0 && aligned16(x) && aligned16(Ys) && aligned16(Ws1) &&
+                   aligned16(Ws3) && aligned16(Ws2) && aligned16(hs);
+  // one expert holding every token: rows [0, T)
+  hipError_t e = moe::launch_dense_offsets(off, c->T, st);
+  if (e == hipSuccess)
+    e = moe::launch_expert_ffn(x, Ws1, Ws3, Ws2, hs, Ys, off, 1, c->H, c->shared_F, c->act, bf16, vec, c->T, st);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "shared_expert");
+}
+
+moe_status moe_combine_shared(const moe_config* c, const void* Y, const moe_plan* plan, const void* residual,
+                              const void* Ys, void* y, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (!plan || (c->T > 0 && (!plan->dst_row || !plan->topk_gate || !y || !Ys))) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && !Y && max_rows_of(c) > 0) return MOE_ERR_INVALID_ARG;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && aligned16(Y) && aligned16(residual) && aligned16(y) && aligned16(Ys);
+  hipError_t e = moe::launch_combine(Y, plan->dst_row, plan->topk_gate, residual, y, c->T, c->H, c->k,
+                                     (int)max_rows_of(c), bf16, vec, static_cast<hipStream_t>(stream), Ys);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "combine_shared");
+}
+
+moe_status moe_forward_shared(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
+                              const void* W3, const void* W2, const void* Ws1, const void* Ws3, const void* Ws2,
+                              const void* residual, void* y, const moe_plan* plan, void* X, void* Y, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if ((s = check_plan(c, plan)) != MOE_OK) return s;
+  if (c->shared_F < 1 || !Ws1 || !Ws2 || (c->act == MOE_SWIGLU) != (Ws3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr) || !Wg) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && (!x || !y || !X || !Y)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(c);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if ((s = moe_route(c, x, Wg, bias, plan, ws, ws_bytes, stream)) != MOE_OK) return s;
+  const int64_t R_max = max_rows_of(c);
+  void* h = static_cast<char*>(ws) + L.h;
+  const bool bf16 = c->dtype == MOE_BF16;
+  const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(x) && aligned16(Y) && aligned16(W1) &&
+                   aligned16(W3) && aligned16(W2) && aligned16(h);
+  if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
+    hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
+                                          R_max, static_cast<hipStream_t>(stream), plan->row_token, c->T);
+    if (e != hipSuccess) return hip_fail(e, "expert_ffn");
+  } else {
+    if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
+    if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
+  }
+  void* Ys = static_cast<char*>(ws) + L.ys;
+  if ((s = moe_shared_expert(c, x, Ws1, Ws3, Ws2, Ys, ws, ws_bytes, stream)) != MOE_OK) return s;
+  return moe_combine_shared(c, Y, plan, residual, Ys, y, stream);
 }
 
 }  // extern "C"
