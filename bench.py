@@ -290,6 +290,22 @@ def main():
         torch.cuda.synchronize()
         return round(e0.elapsed_time(e1) / args.steps * 1e3, 2), int(plan_c["n_dropped"].item())
 
+    # ---- shared expert (one dense FFN of the routed experts' width on every token,
+    # added to the routed output): the layer with it, and its FFN alone
+    cfg_s = B.MoEConfig.from_run(run)
+    cfg_s.shared_F = run.F
+    sws = [up(recipes.gen_shared_weight(run, n, run.F)) if (n != "s3" or run.act == recipes.SWIGLU) else None
+           for n in ("s1", "s3", "s2")]
+    ws_s = B.alloc_workspace(cfg_s, dev)
+    Ys = torch.empty((run.T, run.H), dtype=tdt, device=dev)
+    fwd_s_us = timed(lambda: B.forward_shared(cfg_s, x, wg, bias, w1, w3, w2, *sws, x, y, plan, X, Y, ws_s))
+    shared_ffn_us = timed(lambda: B.shared_expert(cfg_s, x, *sws, Ys, ws_s))
+    shared_flops = 2.0 * run.T * run.H * run.F * run.m
+    shared_out = {"workload": workload + f"+shared-F{run.F}", "ms_per_step": round(fwd_s_us / 1e3, 5),
+                  "tokens_per_s": round(run.T / (fwd_s_us * 1e-6), 1), "shared_ffn_us": round(shared_ffn_us, 2),
+                  "shared_ffn_tflops": round(shared_flops / (shared_ffn_us * 1e-6) / 1e12, 1)}
+    del ws_s, Ys, sws
+
     variants = {}
     for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
         c = B.MoEConfig.from_run(run)
@@ -383,6 +399,7 @@ def main():
         "stages": stages_out,
         "router_training_terms": losses_us,
         "routing_variants": variants,
+        "shared_expert": shared_out,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
