@@ -247,6 +247,17 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
+    # ---- per-step spread: the same K steps with an event between steps (no syncs)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2]
+
     # ---- per-stage durations: each stage entry point called K times back to back
     # (the plan and buffers of this batch stay valid across repeats), HIP events
     # recorded on the stream the kernels run on (torch's current stream)
@@ -267,6 +278,30 @@ def main():
         "expert_ffn": timed(lambda: B.expert_ffn(cfg, X, plan, w1, w3, w2, Y, ws)),
         "combine": timed(lambda: B.combine(cfg, Y, plan, x, y)),
     }
+
+    # cold: before each call a copy kernel writes 512 MiB (more than the 256 MB
+    # Infinity Cache), so the stage's inputs come from HBM; median of 10 calls
+    flush_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+
+    def timed_cold(fn, n=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(n):
+            flush_dst.copy_(flush_src)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(ts)[n // 2]
+
+    stage_cold_us = {
+        "route": timed_cold(lambda: B.route(cfg, x, wg, bias, plan, ws)),
+        "dispatch": timed_cold(lambda: B.dispatch(cfg, x, plan, X)),
+        "combine": timed_cold(lambda: B.combine(cfg, Y, plan, x, y)),
+    }
+    del flush_src, flush_dst
 
     # ---- router training terms (load-balancing loss, z-loss): route with the
     # optional losses output, against route without it
@@ -368,6 +403,11 @@ def main():
         "combine": {"us": round(stage_us["combine"], 2), "GB_s": round(gbs(comb_bytes, stage_us["combine"]), 1),
                     "hbm_frac": round(gbs(comb_bytes, stage_us["combine"]) / PEAK_HBM_GBS, 4)},
     }
+    cold_bytes = {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes}
+    stages_cold = {n: {"us": round(v, 2), "GB_s": round(gbs(cold_bytes[n], v), 1),
+                       "hbm_frac": round(gbs(cold_bytes[n], v) / PEAK_HBM_GBS, 4)} for n, v in stage_cold_us.items()}
+    stages_cold["note"] = ("one call after a 512 MiB copy (inputs out of every cache), median of 10; includes the "
+                           "launch latency of an idle GPU")
 
     # ---- CPU baseline: the oracle on the machine's host cores, bounded sample
     cpu = None
@@ -383,6 +423,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -397,6 +438,7 @@ def main():
                                     "dispatch": stages_out["dispatch"]["hbm_frac"],
                                     "combine": stages_out["combine"]["hbm_frac"]},
         "stages": stages_out,
+        "stages_cold": stages_cold,
         "router_training_terms": losses_us,
         "routing_variants": variants,
         "shared_expert": shared_out,
