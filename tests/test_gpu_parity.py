@@ -227,6 +227,10 @@ def _run_edge(gpu, r):
     dict(name="E1", E=1, k=1), dict(name="kE", E=6, k=6), dict(name="k16", E=20, k=16, T=90),
     dict(name="ragged", H=37, F=45), dict(name="H1", H=1, F=3, T=70), dict(name="bigE", E=1024, k=3, T=130, H=64),
     dict(name="tinycf", cf=0.05), dict(name="mincap", cf=0.05, min_capacity=7),
+    # 33..64 experts, a multiple of 4: the router loads the fp32 weights itself
+    # (48: padded expert columns; 36 and T=1: a single, mostly empty token tile)
+    dict(name="E48", E=48, k=2, T=333), dict(name="E36", E=36, k=3, T=1), dict(name="E64H128", E=64, k=1, H=128),
+    dict(name="E44", E=44, k=4, T=257, H=192),
 ])
 def test_edge_shapes(gpu, kw):
     base = recipes.SMALL["5"].scaled(T=200, H=64, F=96, E=16, k=4)

@@ -321,6 +321,28 @@ __device__ __forceinline__ double exact_dot(const uint16_t* __restrict__ xr, con
   return s;
 }
 
+// The same sum over the fp32 weights Wg [H][E] directly (w = hi + mid + lo, so
+// the binary64 result is the same).
+__device__ __forceinline__ double exact_dot_raw(const uint16_t* __restrict__ xr, const float* __restrict__ Wg, int e,
+                                                int H, int E) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int h = 8 * lane; h < H; h += 512) {
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xr + h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t bits = half ? (xv[q] & 0xFFFF0000u) : (xv[q] << 16);
+        s = __builtin_fma((double)__uint_as_float(bits), (double)Wg[(size_t)(h + 2 * q + half) * E + e], s);
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) s += __shfl_xor(s, d, 64);
+  return s;
+}
+
 // Bound on ||x|| from the fp32 sum of squares (each of the <= H additions errs
 // by at most 2^-24 relative) and on the rounding of the square root.
 __device__ __forceinline__ float xnorm_bound(float sq, int H) {
@@ -353,20 +375,25 @@ struct SplitTail {
 // sum_h x^2 per token (fp32), and the blocks of the first token tile write the
 // norms ||w_e|| of their experts.
 // ---------------------------------------------------------------------------
-template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX>
+template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX, bool RAW>
 __global__ void __launch_bounds__(512) router_split_logits_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wp, const float* __restrict__ bias,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wp, const float* __restrict__ Wg,
+    const float* __restrict__ bias,
     const double* __restrict__ wsq, float* __restrict__ logits, float* __restrict__ xsq, double* __restrict__ wn,
     int T, int H, int E, int Ep, int k, int gate_mode, double c1, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_gate, int2* __restrict__ pairs, int4* __restrict__ utok, int* __restrict__ count,
     SplitTail tail) {
   static_assert(TG * EG * KS == 8, "8 waves");
   constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
+  static_assert(!RAW || (FUSE && KS == 1 && BN == 64), "fp32 weights in the stage: one slice of 64 experts");
   constexpr int SR = BM + 3 * BN;  // rows per slice per stage
   constexpr int ROWS = KS * SR;
-  constexpr int NI = ROWS / 8;  // 64-lane load instructions per stage (8 rows each)
+  // 64-lane load instructions per stage: 8 rows of 64 h each; with RAW the
+  // weight block (64 h x 64 experts fp32, 16 KB) takes 16 more
+  constexpr int NIX = BM / 8;
+  constexpr int NI = RAW ? NIX + 16 : ROWS / 8;
   constexpr int L = (NI + 7) / 8;
-  constexpr int STAGE = ROWS * kChunk;  // bf16 elements
+  constexpr int STAGE = RAW ? BM * kChunk + 64 * 64 * 2 : ROWS * kChunk;  // bf16 elements
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -386,10 +413,12 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   double wpre[2] = {0.0, 0.0};
   if constexpr (FUSE) {
     if (bias && tid < BN && e0 + tid < E) bpre = bias[e0 + tid];
+    if constexpr (!RAW) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int hb = tid / BN + q * NG;
-      if (hb < nk) wpre[q] = wsq[(size_t)hb * Ep + e0 + tid % BN];
+      for (int q = 0; q < 2; ++q) {
+        const int hb = tid / BN + q * NG;
+        if (hb < nk) wpre[q] = wsq[(size_t)hb * Ep + e0 + tid % BN];
+      }
     }
   }
 
@@ -399,6 +428,16 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     for (int q = 0; q < L; ++q) {
       int g = q * 8 + w;
       if (g >= NI) g = NI - 1;  // waves without a group of their own repeat the last one
+      if (RAW && g >= NIX) {
+        // weight block: 16-byte slot s of row h holds experts 4 (s ^ 4((h >> 3) & 3)) .. +3,
+        // so the four 8-h groups a fragment read spans fall on different banks
+        const int q2 = (g - NIX) * 64 + lane;
+        const int hr = q2 >> 4;
+        int c4 = ((q2 & 15) ^ (((hr >> 3) & 3) << 2)) * 4;
+        if (e0 + c4 >= E) c4 = 0;  // columns past E: any valid address (never used)
+        __builtin_amdgcn_global_load_lds(Wg + (size_t)(j * kChunk + hr) * E + e0 + c4, st + g * 512, 16, 0, 0);
+        continue;
+      }
       const int p = g * 64 + lane;
       const int r = p >> 3;
       const int c = (p & 7) ^ ((r >> 1) & 7);
@@ -430,6 +469,9 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   float sq[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) sq[i] = 0.0f;
+  float wsum[WN];  // RAW: sum of w^2 over this lane's fragments (waves of token group 0)
+#pragma unroll
+  for (int n = 0; n < WN; ++n) wsum[n] = 0.0f;
 
   int issued = 0;
 #pragma unroll
@@ -442,6 +484,24 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     lds_barrier();
     if (issued < nks) issue(issued % S, issued), ++issued;
     const uint16_t* st = smem + (j % S) * STAGE;
+    // RAW: both k-steps' fp32 weights read up front, so the reads of the second
+    // overlap the splitting and MFMAs of the first
+    float wraw[RAW ? 2 : 1][WN][8];
+    if constexpr (RAW) {
+      const float* wb = reinterpret_cast<const float*>(st + BM * kChunk);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k0 = kk * 32 + 8 * (lane >> 4);
+        const int sw = ((k0 >> 3) & 3) << 2;
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          const int e = (eg * WN + n) * 16 + (lane & 15);
+          const int col = (((e >> 2) ^ sw) << 2) | (e & 3);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wraw[kk][n][i] = wb[(k0 + i) * 64 + col];
+        }
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = kk * 4 + (lane >> 4);
@@ -449,18 +509,54 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
 #pragma unroll
       for (int i = 0; i < MF; ++i)
         a[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(rbase + (tg * MF + i) * 16 + (lane & 15), c));
-#pragma unroll
-      for (int p = 0; p < 3; ++p)
+      if constexpr (RAW) {
+        // the 8 fp32 weights of this lane's fragment (expert e, h = k0 .. k0+7), split
+        // here into bf16 hi + mid + lo by truncation (w = hi + mid + lo exactly)
 #pragma unroll
         for (int n = 0; n < WN; ++n) {
-          const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
-              st + lds_pos(rbase + BM + p * BN + (eg * WN + n) * 16 + (lane & 15), c));
+          u32x4_t ph, pm, pl;
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            uint32_t hb2[2], mb2[2], lb2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float wv = wraw[kk][n][i + u];
+              const float hf = __uint_as_float(__float_as_uint(wv) & 0xFFFF0000u);
+              const float r1 = wv - hf;
+              const float mf = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+              const float r2 = r1 - mf;
+              hb2[u] = __float_as_uint(hf) >> 16;
+              mb2[u] = __float_as_uint(mf) >> 16;
+              lb2[u] = __float_as_uint(r2) >> 16;
+              if (tg == 0) wsum[n] = __builtin_fmaf(wv, wv, wsum[n]);
+            }
+            ph[i / 2] = hb2[0] | (hb2[1] << 16);
+            pm[i / 2] = mb2[0] | (mb2[1] << 16);
+            pl[i / 2] = lb2[0] | (lb2[1] << 16);
+          }
+          const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, ph), bm = __builtin_bit_cast(bf16x8_t, pm),
+                         bl = __builtin_bit_cast(bf16x8_t, pl);
 #pragma unroll
           for (int i = 0; i < MF; ++i) {
-            if (p == 0) acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_hi[i][n], 0, 0, 0);
-            else acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_ml[i][n], 0, 0, 0);
+            acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bh, acc_hi[i][n], 0, 0, 0);
+            acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bm, acc_ml[i][n], 0, 0, 0);
+            acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bl, acc_ml[i][n], 0, 0, 0);
           }
         }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int n = 0; n < WN; ++n) {
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+                st + lds_pos(rbase + BM + p * BN + (eg * WN + n) * 16 + (lane & 15), c));
+#pragma unroll
+            for (int i = 0; i < MF; ++i) {
+              if (p == 0) acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_hi[i][n], 0, 0, 0);
+              else acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_ml[i][n], 0, 0, 0);
+            }
+          }
+      }
       if (eg == 0) {
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
@@ -587,17 +683,27 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     const int tl = tid / G;  // token of this group
     __shared__ float s_wn[BN];  // ||w_e||, rounded up
     double* s_wpart = reinterpret_cast<double*>(s_x + BM);  // [NG][BN] partial sums
-    {
+    if constexpr (RAW) {
+      // the four k groups of a fragment (lanes l, l^16, l^32, l^48) hold one expert's sums
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        float sn = wsum[n];
+        sn += __shfl_xor(sn, 16, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const int e = (eg * WN + n) * 16 + lane;
+        if (tg == 0 && lane < 16) s_wn[e] = e0 + e < E ? xnorm_bound(sn, H) : 0.0f;
+      }
+    } else {
       double sw = wpre[0] + wpre[1];
       for (int hb = tid / BN + 2 * NG; hb < nk; hb += NG) sw += wsq[(size_t)hb * Ep + tid % BN];
       s_wpart[tid] = sw;
-    }
-    __syncthreads();
-    if (tid < BN) {
-      double sw = 0.0;
+      __syncthreads();
+      if (tid < BN) {
+        double sw2 = 0.0;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) sw += s_wpart[g * BN + tid];
-      s_wn[tid] = tid < E ? (float)sqrt(sw * (1.0 + 0x1p-40)) * (1.0f + 0x1p-20f) : 0.0f;
+        for (int g = 0; g < NG; ++g) sw2 += s_wpart[g * BN + tid];
+        s_wn[tid] = tid < E ? (float)sqrt(sw2 * (1.0 + 0x1p-40)) * (1.0f + 0x1p-20f) : 0.0f;
+      }
     }
     __shared__ int s_cnt[2];  // candidate pairs, queued tokens of this workgroup
     if (tid < 2) s_cnt[tid] = 0;
@@ -636,7 +742,8 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     if (ntok > 0) {
       for (int c = w; c < npairs; c += 8) {
         const int2 pr = s_pairs[c];
-        const double sx = exact_dot(x + (size_t)pr.x * H, wp, pr.y, H, Ep);
+        const double sx = RAW ? exact_dot_raw(x + (size_t)pr.x * H, Wg, pr.y, H, E)
+                              : exact_dot(x + (size_t)pr.x * H, wp, pr.y, H, Ep);
         if (lane == 0) {
           const float lv = (float)(sx + (double)s_bias[pr.y]);
           logits[(size_t)pr.x * E + pr.y] = lv;
@@ -880,6 +987,7 @@ int split_router_hs(int H) { return H / kChunk; }
 struct SplitArgs {
   const uint16_t* x;
   const uint16_t* wp;
+  const float* Wg;
   const float* bias;
   float* logits;
   int32_t* topk_idx;
@@ -891,11 +999,11 @@ struct SplitArgs {
   int* fused;      // out: 1 ranks done, 2 loss partials done
 };
 
-template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX>
+template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX, bool RAW = false>
 static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   constexpr int BM = 16 * MF * TG, BN = 16 * WN * EG;
   constexpr int ROWS = KS * (BM + 3 * BN);
-  size_t shm = sizeof(uint16_t) * (size_t)S * ROWS * kChunk;
+  size_t shm = sizeof(uint16_t) * (size_t)S * (RAW ? BM * kChunk + 64 * 64 * 2 : ROWS * kChunk);
   const size_t red = (KS > 1) ? (sizeof(double) * (size_t)(KS - 1) * TG * EG * MF * WN * 4 * 64 +
                                  sizeof(float) * (size_t)(KS - 1) * TG * MF * 64)
                               : 0;
@@ -911,24 +1019,24 @@ static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   *a.fused = kTail ? ((tail.dst_rank ? 1 : 0) | (tail.Ppart ? 2 : 0)) : 0;
   if (red > shm) shm = red;
   if (fz > shm) shm = fz;
-  auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX>;
+  auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX, RAW>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (err != hipSuccess) return err;
   dim3 grid((a.T + BM - 1) / BM, a.Ep / BN);
-  kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
+  kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.Wg, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
                                      a.k, a.gate_mode, a.c1, a.topk_idx, a.topk_gate, a.sc->pairs, a.sc->utok,
                                      a.sc->count, tail);
   return hipGetLastError();
 }
 
 // fused selection: one instantiation per bound on k
-template <int TG, int EG, int KS, int MF, int WN, int S>
+template <int TG, int EG, int KS, int MF, int WN, int S, bool RAW = false>
 static hipError_t launch_split_fused(const SplitArgs& a, hipStream_t st) {
-  if (a.k <= 1) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 1>(a, st);
-  if (a.k <= 2) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 2>(a, st);
-  if (a.k <= 4) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 4>(a, st);
-  if (a.k <= 8) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 8>(a, st);
-  return launch_split_logits<TG, EG, KS, MF, WN, S, true, 16>(a, st);
+  if (a.k <= 1) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 1, RAW>(a, st);
+  if (a.k <= 2) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 2, RAW>(a, st);
+  if (a.k <= 4) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 4, RAW>(a, st);
+  if (a.k <= 8) return launch_split_logits<TG, EG, KS, MF, WN, S, true, 8, RAW>(a, st);
+  return launch_split_logits<TG, EG, KS, MF, WN, S, true, 16, RAW>(a, st);
 }
 
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
@@ -939,9 +1047,15 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   const int Ep = split_router_ep(E), nk = H / kChunk;
   uint16_t* wp = static_cast<uint16_t*>(sc.wp);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  router_split_prep_kernel<<<dim3((Ep + 63) / 64, nk), dim3(256), 0, st>>>(Wg, H, E, Ep, wp, sc.wsq, sc.count);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // 33..64 experts (a multiple of 4, 16-byte aligned Wg): the fused kernel loads
+  // the fp32 weights itself and splits them as it reads its fragments, so no
+  // prep pass; otherwise the pieces are prepared once per call
+  const bool raw = E > 32 && E <= 64 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(Wg) & 15u) == 0;
+  hipError_t err = hipSuccess;
+  if (!raw) {
+    router_split_prep_kernel<<<dim3((Ep + 63) / 64, nk), dim3(256), 0, st>>>(Wg, H, E, Ep, wp, sc.wsq, sc.count);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
   // hi chain: 64 products (+ the running sum), |hi| <= (1 + 2^-7)|w|; mid/lo
   // chain: 128 products, |mid| + |lo| <= 2^-7 |w|; 2^-23 per addition, 1%
@@ -952,7 +1066,7 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
   const SplitTail tail{ep.second_u, ep.dst_rank, ep.hist,  nbits,      (T + 63) / 64,
                        ep.Ppart,    ep.Zpart,    ep.Cpart, ep.score_fn};
-  SplitArgs a{xb, wp, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
+  SplitArgs a{xb, wp, Wg, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
 
   if (E <= 16) {
     // 16 experts per wave; split h across waves when there are few tokens
@@ -962,7 +1076,7 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   } else if (E <= 32) {
     err = launch_split_fused<8, 1, 1, 1, 2, 4>(a, st);
   } else if (E <= 64) {
-    err = launch_split_fused<2, 4, 1, 2, 1, 4>(a, st);
+    err = raw ? launch_split_fused<2, 4, 1, 2, 1, 4, true>(a, st) : launch_split_fused<2, 4, 1, 2, 1, 4>(a, st);
   } else {
     err = (nk % 2) ? launch_split_logits<2, 4, 1, 2, 2, 2, false, 1>(a, st)
                    : launch_split_logits<2, 2, 2, 2, 2, 2, false, 1>(a, st);
