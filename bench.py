@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--core-only", action="store_true",
+                    help="skip the extra measurements (for profiler runs: only the routed layer's launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB (the PMC byte-counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DB", help="print the kernel summary of a rocprofv3 database")
@@ -279,75 +281,81 @@ def main():
         "combine": timed(lambda: B.combine(cfg, Y, plan, x, y)),
     }
 
-    # cold: before each call a copy kernel writes 512 MiB (more than the 256 MB
-    # Infinity Cache), so the stage's inputs come from HBM; median of 10 calls
-    flush_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-    flush_dst = torch.empty_like(flush_src)
+    # Extra measurements (cold stages, training terms, routing variants, shared
+    # expert) are skipped with --core-only, which the profiler runs use so that
+    # every launch they record belongs to the routed layer.
+    stage_cold_us, losses_us, variants, shared_out = None, None, None, None
+    if not args.core_only:
+        # cold: before each call a copy kernel writes 512 MiB (more than the 256 MB
+        # Infinity Cache), so the stage's inputs come from HBM; median of 10 calls
+        flush_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        flush_dst = torch.empty_like(flush_src)
 
-    def timed_cold(fn, n=10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(n):
-            flush_dst.copy_(flush_src)
+        def timed_cold(fn, n=10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ts = []
+            for _ in range(n):
+                flush_dst.copy_(flush_src)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return sorted(ts)[n // 2]
+
+        stage_cold_us = {
+            "route": timed_cold(lambda: B.route(cfg, x, wg, bias, plan, ws)),
+            "dispatch": timed_cold(lambda: B.dispatch(cfg, x, plan, X)),
+            "combine": timed_cold(lambda: B.combine(cfg, Y, plan, x, y)),
+        }
+        del flush_src, flush_dst
+
+        # ---- router training terms (load-balancing loss, z-loss): route with the
+        # optional losses output, against route without it
+        plan_l = dict(plan)
+        plan_l["losses"] = torch.empty(2, dtype=torch.float64, device=dev)
+        losses_us = {"route_us": round(stage_us["route"], 2),
+                     "route_with_losses_us": round(timed(lambda: B.route(cfg, x, wg, bias, plan_l, ws)), 2),
+                     "losses": [float(v) for v in plan_l["losses"].cpu().tolist()]}
+
+        # ---- routing variants: "probs" drop policy and sigmoid scores, route alone
+        def route_time(c):
+            ws_c = B.alloc_workspace(c, dev)
+            plan_c = B.alloc_plan(c, dev)
+            B.route(c, x, wg, bias, plan_c, ws_c)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             e0.record()
-            fn()
+            for _ in range(args.steps):
+                B.route(c, x, wg, bias, plan_c, ws_c)
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        return sorted(ts)[n // 2]
+            return round(e0.elapsed_time(e1) / args.steps * 1e3, 2), int(plan_c["n_dropped"].item())
 
-    stage_cold_us = {
-        "route": timed_cold(lambda: B.route(cfg, x, wg, bias, plan, ws)),
-        "dispatch": timed_cold(lambda: B.dispatch(cfg, x, plan, X)),
-        "combine": timed_cold(lambda: B.combine(cfg, Y, plan, x, y)),
-    }
-    del flush_src, flush_dst
+        # ---- shared expert (one dense FFN of the routed experts' width on every token,
+        # added to the routed output): the layer with it, and its FFN alone
+        cfg_s = B.MoEConfig.from_run(run)
+        cfg_s.shared_F = run.F
+        sws = [up(recipes.gen_shared_weight(run, n, run.F)) if (n != "s3" or run.act == recipes.SWIGLU) else None
+               for n in ("s1", "s3", "s2")]
+        ws_s = B.alloc_workspace(cfg_s, dev)
+        Ys = torch.empty((run.T, run.H), dtype=tdt, device=dev)
+        fwd_s_us = timed(lambda: B.forward_shared(cfg_s, x, wg, bias, w1, w3, w2, *sws, x, y, plan, X, Y, ws_s))
+        shared_ffn_us = timed(lambda: B.shared_expert(cfg_s, x, *sws, Ys, ws_s))
+        shared_flops = 2.0 * run.T * run.H * run.F * run.m
+        shared_out = {"workload": workload + f"+shared-F{run.F}", "ms_per_step": round(fwd_s_us / 1e3, 5),
+                      "tokens_per_s": round(run.T / (fwd_s_us * 1e-6), 1), "shared_ffn_us": round(shared_ffn_us, 2),
+                      "shared_ffn_tflops": round(shared_flops / (shared_ffn_us * 1e-6) / 1e12, 1)}
+        del ws_s, Ys, sws
 
-    # ---- router training terms (load-balancing loss, z-loss): route with the
-    # optional losses output, against route without it
-    plan_l = dict(plan)
-    plan_l["losses"] = torch.empty(2, dtype=torch.float64, device=dev)
-    losses_us = {"route_us": round(stage_us["route"], 2),
-                 "route_with_losses_us": round(timed(lambda: B.route(cfg, x, wg, bias, plan_l, ws)), 2),
-                 "losses": [float(v) for v in plan_l["losses"].cpu().tolist()]}
+        variants = {}
+        for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
+            c = B.MoEConfig.from_run(run)
+            for key, val in kw.items():
+                setattr(c, key, val)
+            us, nd = route_time(c)
+            variants[name] = {"route_us": us, "dropped": nd}
 
-    # ---- routing variants: "probs" drop policy and sigmoid scores, route alone
-    def route_time(c):
-        ws_c = B.alloc_workspace(c, dev)
-        plan_c = B.alloc_plan(c, dev)
-        B.route(c, x, wg, bias, plan_c, ws_c)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            B.route(c, x, wg, bias, plan_c, ws_c)
-        e1.record()
-        torch.cuda.synchronize()
-        return round(e0.elapsed_time(e1) / args.steps * 1e3, 2), int(plan_c["n_dropped"].item())
-
-    # ---- shared expert (one dense FFN of the routed experts' width on every token,
-    # added to the routed output): the layer with it, and its FFN alone
-    cfg_s = B.MoEConfig.from_run(run)
-    cfg_s.shared_F = run.F
-    sws = [up(recipes.gen_shared_weight(run, n, run.F)) if (n != "s3" or run.act == recipes.SWIGLU) else None
-           for n in ("s1", "s3", "s2")]
-    ws_s = B.alloc_workspace(cfg_s, dev)
-    Ys = torch.empty((run.T, run.H), dtype=tdt, device=dev)
-    fwd_s_us = timed(lambda: B.forward_shared(cfg_s, x, wg, bias, w1, w3, w2, *sws, x, y, plan, X, Y, ws_s))
-    shared_ffn_us = timed(lambda: B.shared_expert(cfg_s, x, *sws, Ys, ws_s))
-    shared_flops = 2.0 * run.T * run.H * run.F * run.m
-    shared_out = {"workload": workload + f"+shared-F{run.F}", "ms_per_step": round(fwd_s_us / 1e3, 5),
-                  "tokens_per_s": round(run.T / (fwd_s_us * 1e-6), 1), "shared_ffn_us": round(shared_ffn_us, 2),
-                  "shared_ffn_tflops": round(shared_flops / (shared_ffn_us * 1e-6) / 1e12, 1)}
-    del ws_s, Ys, sws
-
-    variants = {}
-    for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
-        c = B.MoEConfig.from_run(run)
-        for key, val in kw.items():
-            setattr(c, key, val)
-        us, nd = route_time(c)
-        variants[name] = {"route_us": us, "dropped": nd}
     log("[bench] stages (us): " + ", ".join(f"{s}={v:.1f}" for s, v in stage_us.items()))
 
     # ---- algorithmic work per step (from the plan of this batch)
@@ -403,11 +411,14 @@ def main():
         "combine": {"us": round(stage_us["combine"], 2), "GB_s": round(gbs(comb_bytes, stage_us["combine"]), 1),
                     "hbm_frac": round(gbs(comb_bytes, stage_us["combine"]) / PEAK_HBM_GBS, 4)},
     }
-    cold_bytes = {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes}
-    stages_cold = {n: {"us": round(v, 2), "GB_s": round(gbs(cold_bytes[n], v), 1),
-                       "hbm_frac": round(gbs(cold_bytes[n], v) / PEAK_HBM_GBS, 4)} for n, v in stage_cold_us.items()}
-    stages_cold["note"] = ("one call after a 512 MiB copy (inputs out of every cache), median of 10; includes the "
-                           "launch latency of an idle GPU")
+    stages_cold = None
+    if stage_cold_us is not None:
+        cold_bytes = {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes}
+        stages_cold = {n: {"us": round(v, 2), "GB_s": round(gbs(cold_bytes[n], v), 1),
+                           "hbm_frac": round(gbs(cold_bytes[n], v) / PEAK_HBM_GBS, 4)}
+                       for n, v in stage_cold_us.items()}
+        stages_cold["note"] = ("one call after a 512 MiB copy (inputs out of every cache), median of 10; includes "
+                               "the launch latency of an idle GPU")
 
     # ---- CPU baseline: the oracle on the machine's host cores, bounded sample
     cpu = None
