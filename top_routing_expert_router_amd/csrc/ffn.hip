@@ -292,26 +292,23 @@ struct PipeTile {
   int e, row0, rows, n0;
 };
 
-// Row of A that packed row `row0 + r` reads when A is gathered (A = the token
-// rows x, gather = row_token): the 64 / CPR rows one load instruction covers
-// (rb .. rb + RPI - 1, wave-uniform) are looked up with scalar loads and each
-// lane takes its own; rows past the tile's `rows` read the tile's first row.
-template <int CPR>
-__device__ __forceinline__ int gathered_row(const int32_t* __restrict__ gather, int xrows, const PipeTile& t, int rb,
-                                            int lane) {
-  constexpr int RPI = 64 / CPR;
-  const int row0 = __builtin_amdgcn_readfirstlane(t.row0);
-  const int rows = __builtin_amdgcn_readfirstlane(t.rows);
-  const int rbu = __builtin_amdgcn_readfirstlane(rb);
-  int v[RPI];
-#pragma unroll
-  for (int i = 0; i < RPI; ++i) v[i] = gather[row0 + (rbu + i < rows ? rbu + i : 0)];
-  const int sel = lane / CPR;
-  int tok = v[0];
-#pragma unroll
-  for (int i = 1; i < RPI; ++i) tok = sel == i ? v[i] : tok;
-  return tok < 0 ? 0 : (tok < xrows ? tok : xrows - 1);
+// Gathered A (A = the token rows x, gather = row_token): a wave's A loads of a
+// tile cover NA groups of 8 packed rows (group q: rows 8 (q NW + w) .. +7).  One
+// direct-to-LDS load of 4 bytes per lane brings their row_token entries into
+// the wave's slot of an LDS table, issued a tile ahead, so that when the tile
+// starts its entries are there (every stage wait since covers that load);
+// rows past the tile's `rows` take the tile's first row.
+template <int NA, int NW>
+__device__ __forceinline__ void fetch_gather_rows(const int32_t* __restrict__ gather, const PipeTile& t, int w,
+                                                  int lane, int* slot) {
+  static_assert(NA * 8 <= 64, "one load instruction");
+  const int l = lane % (NA * 8);
+  const int r = ((l >> 3) * NW + w) * 8 + (l & 7);
+  const int row = t.row0 + (r < t.rows ? r : 0);
+  __builtin_amdgcn_global_load_lds(gather + row, slot, 4, 0, 0);
 }
+
+__device__ __forceinline__ int clamp_row(int tok, int xrows) { return tok < 0 ? 0 : (tok < xrows ? tok : xrows - 1); }
 
 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
@@ -348,6 +345,9 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
   const int ntn = (N + BN - 1) / BN;
+  constexpr int NA = BM * CPR / (64 * NW);  // this wave's load instructions of A rows per stage
+  __shared__ int s_gidx[2][NW][64];          // gathered row indices, two tiles
+  int gbuf = 0;                              // table of the tile being loaded
 
   {  // tile list: ceil(kept_e / BM) * ntn tiles per expert
     const int per = (E + 64 * NW - 1) / (64 * NW);
@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
       const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       if (r < BM) {
         const int rr = r < t.rows ? r : 0;
-        const int src = gather ? gathered_row<CPR>(gather, xrows, t, blk * 64 / CPR, lane) : t.row0 + rr;
+        const int src = gather ? clamp_row(s_gidx[gbuf][w][q * 8 + lane / CPR], xrows) : t.row0 + rr;
         rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
       } else {
         const int wr = r - BM;
@@ -508,14 +508,28 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
     }
   };
 
+  if (gather) {
+    static_assert(CPR == 8, "8 rows per load instruction");
+    fetch_gather_rows<NA, NW>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
+    wait_vmcnt<0>();
+  }
   set_rows(decode(0));  // rows of the tile of the next stage to load
+  if (gather && my_tiles > 1) fetch_gather_rows<NA, NW>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
   int lt_i = 0, lt_k = 0, issued = 0;
   auto issue_next = [&]() {
     issue(issued % S, lt_k);
     ++issued;
     if (++lt_k == nk) {
       lt_k = 0;
-      if (++lt_i < my_tiles) set_rows(decode(lt_i));
+      if (++lt_i < my_tiles) {
+        if (gather) {
+          gbuf ^= 1;
+          if (nk < S) wait_vmcnt<0>();  // fewer stages per tile than in flight: the table may not be in yet
+        }
+        set_rows(decode(lt_i));
+        if (gather && lt_i + 1 < my_tiles)
+          fetch_gather_rows<NA, NW>(gather, decode(lt_i + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
+      }
     }
   };
 #pragma unroll
@@ -605,6 +619,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
   const int ntn = (N + BN - 1) / BN;
+  __shared__ int s_gidx[2][NW][64];  // gathered row indices, two tiles
+  int gbuf = 0;
   {
     const int per = (E + 64 * NW - 1) / (64 * NW);
     const int e0 = tid * per;
@@ -669,7 +685,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
       const int p = (q * NW + w) * 64 + lane;
       const int r = p / CPR, c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       const int rr = r < t.rows ? r : 0;
-      const int src = gather ? gathered_row<CPR>(gather, xrows, t, (q * NW + w) * 64 / CPR, lane) : t.row0 + rr;
+      const int src = gather ? clamp_row(s_gidx[gbuf][w][q * 8 + lane / CPR], xrows) : t.row0 + rr;
       rowA[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
     }
   };
@@ -687,7 +703,12 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   // load trackers: next stage index, its tile and k-step, per operand
   int a_next = 0, a_tile = 0, a_k = 0;
   int w_next = 0, w_tile = 0, w_k = 0;
+  if (gather) {
+    fetch_gather_rows<LA, NW>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
+    wait_vmcnt<0>();
+  }
   set_rows_a(decode(0));
+  if (gather && my_tiles > 1) fetch_gather_rows<LA, NW>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
   set_rows_w(decode(0));
   auto issue_a = [&]() {
     uint16_t* st = s_a + (a_next & 1) * ASTAGE;
@@ -698,7 +719,14 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
     ++a_next;
     if (++a_k == nk) {
       a_k = 0;
-      if (++a_tile < my_tiles) set_rows_a(decode(a_tile));
+      if (++a_tile < my_tiles) {
+        // the table of this tile came in with a load issued a tile earlier, before
+        // at least one weight group that every step's wait covers
+        gbuf ^= 1;
+        set_rows_a(decode(a_tile));
+        if (gather && a_tile + 1 < my_tiles)
+          fetch_gather_rows<LA, NW>(gather, decode(a_tile + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
+      }
     }
   };
   auto issue_w = [&]() {
