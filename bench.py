@@ -139,10 +139,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the layer captured in a HIP graph instead of eager moe_forward calls")
     ap.add_argument("--core-only", action="store_true",
                     help="skip the extra measurements (for profiler runs: only the routed layer's launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -238,23 +240,58 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---- with --graph the layer's launches are captured once in a HIP graph and a
+    # step is one replay (the same kernels on the same buffers; nothing the
+    # library enqueues is a memset or an allocation).  Default: eager calls.
+    graph = None
+    if args.graph:
+        try:
+            gs = torch.cuda.Stream()
+            gs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gs):
+                step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=gs):
+                step()
+            torch.cuda.synchronize()
+        except Exception as exc:  # capture unavailable: eager steps
+            log(f"[bench] graph capture failed ({exc}); timing eager steps")
+            graph = None
+    run_step = graph.replay if graph is not None else step
+    for _ in range(args.warmup):  # warm-up of the timed form as well (first replays upload the graph)
+        run_step()
+
+    def time_steps(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
     # ---- timed region: K whole-layer steps, back to back on one stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        step()
+        run_step()
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    ms_eager = time_steps(step) if graph is not None else ms_per_step
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step ({'graph replay' if graph else 'eager'})")
 
     # ---- per-step spread: the same K steps with an event between steps (no syncs)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     evs[0].record()
     for i in range(args.steps):
-        step()
+        run_step()
         evs[i + 1].record()
     torch.cuda.synchronize()
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
@@ -435,6 +472,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "ms_per_step_median": round(ms_median, 5),
+        "ms_per_step_eager": round(ms_eager, 5),
+        "launch": "HIP graph replay of moe_forward" if graph is not None else "eager moe_forward calls",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -705,3 +705,51 @@ def test_forward_shared_full_size_sampled(gpu, name):
     yref = oracle.token_outputs(np.arange(len(toks)), x[toks], r.dtype, r.act, sub, cw1, cw3, cw2)
     yref = yref + oracle.shared_expert(x, r.dtype, r.act, *sw, tokens=toks)
     U.assert_close(U.host(y)[toks], yref, r.dtype == recipes.BF16, f"forward+shared full-size run {r.name} sample")
+
+
+def test_forward_graph_replay(gpu):
+    """The whole layer captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) gives the eager result bit for bit."""
+    import torch
+
+    r = recipes.SMALL["2"]
+    d = recipes.gen_all(r)
+    cfg = B.MoEConfig.from_run(r)
+    tdt = torch.bfloat16
+    xd = U.dev(d["x"], gpu)
+    wgt = (U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), U.dev(d["w1"], gpu), None, U.dev(d["w2"], gpu))
+    plan = B.alloc_plan(cfg, gpu)
+    rmax = B.max_rows(cfg)
+    X = torch.empty((rmax, r.H), dtype=tdt, device=gpu)
+    Y = torch.empty_like(X)
+    y = torch.empty((r.T, r.H), dtype=tdt, device=gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    s = torch.cuda.Stream()
+
+    def step():
+        B.forward(cfg, xd, *wgt, xd, y, plan, X, Y, ws, stream=s)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    dst_eager = plan["dst_row"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.zero_()
+        plan["dst_row"].fill_(-7)
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+        assert torch.equal(plan["dst_row"], dst_eager), f"replay {i} plan"
+        with torch.cuda.stream(s):  # eager work between replays
+            step()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+    yref, *_ = oracle.forward(d["x"], r.dtype, d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], r.k, r.gate_mode,
+                              r.act, _cap(r), residual=d["x"])
+    U.assert_close(U.host(y_eager), yref, True, "graph replay forward")
