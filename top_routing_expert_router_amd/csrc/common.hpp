@@ -26,6 +26,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two fp32 values rounded to nearest, ties to even, as bf16 packed into one word
+// (lo in bits 0..15): one hardware conversion for the pair.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+
 // Loads 8 consecutive elements [i, i+8) of a row of `n` elements as fp32,
 // zero-filling past the end.  `vec_ok` promises 16-byte alignment of every
 // vector access (the row base and i are multiples of the vector width).

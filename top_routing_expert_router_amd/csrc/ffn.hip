@@ -20,24 +20,27 @@ namespace moe {
 
 enum { EPI_NONE = 0, EPI_RELU = 1, EPI_GELU = 2, EPI_SWIGLU = 3 };
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
-// (|error| <= 1.5e-7 for all x), with the hardware exp2 and reciprocal.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, ax, 1.0f));
+// GELU x Phi(x) = x/2 + |x|/2 (1 - erfc(|x| / sqrt 2)) with erfc(z) ~ t P(t) e^(-z^2),
+// t = 1 / (1 + p z), from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error| <= 1.5e-7), written in m = x/2 so that the
+// last step is one fma: one reciprocal, one exp2 and 9 further operations;
+// |error| <= 5e-7 over [-12, 12] in fp32.
+__device__ __forceinline__ float gelu_erf(float a) {
+  const float m = 0.5f * a;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(fabsf(m), 0.46328377653272080f, 1.0f));  // z = sqrt 2 |m|
   float p = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
   p = __builtin_fmaf(t, p, 1.421413741f);
   p = __builtin_fmaf(t, p, -0.284496736f);
   p = __builtin_fmaf(t, p, 0.254829592f);
   p *= t;
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(__builtin_fmaf(-p, e, 1.0f), x);
+  const float e = __builtin_amdgcn_exp2f(m * m * -2.8853900817779268f);  // e^(-z^2) = e^(-2 m^2)
+  return __builtin_fmaf(fabsf(m), __builtin_fmaf(-p, e, 1.0f), m);
 }
 
 template <int EPI>
 __device__ __forceinline__ float epilogue(float a, float b) {
   if (EPI == EPI_RELU) return a > 0.0f ? a : 0.0f;
-  if (EPI == EPI_GELU) return 0.5f * a * (1.0f + erf_as7126(a * 0.70710678118654752f));
+  if (EPI == EPI_GELU) return gelu_erf(a);
   if (EPI == EPI_SWIGLU)  // silu(a) * b = a / (1 + e^-a) * b
     return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.4426950408889634f)) * b;
   return a;
@@ -293,17 +296,17 @@ struct PipeTile {
 };
 
 // Gathered A (A = the token rows x, gather = row_token): a wave's A loads of a
-// tile cover NA groups of 8 packed rows (group q: rows 8 (q NW + w) .. +7).  One
+// tile cover NA groups of RPL packed rows (group q: rows RPL (q NW + w) .. +RPL-1).  One
 // direct-to-LDS load of 4 bytes per lane brings their row_token entries into
 // the wave's slot of an LDS table, issued a tile ahead, so that when the tile
 // starts its entries are there (every stage wait since covers that load);
 // rows past the tile's `rows` take the tile's first row.
-template <int NA, int NW>
+template <int NA, int NW, int RPL>
 __device__ __forceinline__ void fetch_gather_rows(const int32_t* __restrict__ gather, const PipeTile& t, int w,
                                                   int lane, int* slot) {
-  static_assert(NA * 8 <= 64, "one load instruction");
-  const int l = lane % (NA * 8);
-  const int r = ((l >> 3) * NW + w) * 8 + (l & 7);
+  static_assert(NA * RPL <= 64, "one load instruction");
+  const int l = lane % (NA * RPL);
+  const int r = ((l / RPL) * NW + w) * RPL + l % RPL;
   const int row = t.row0 + (r < t.rows ? r : 0);
   __builtin_amdgcn_global_load_lds(gather + row, slot, 4, 0, 0);
 }
@@ -312,9 +315,10 @@ __device__ __forceinline__ int clamp_row(int tok, int xrows) { return tok < 0 ? 
 
 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
-// as WGM (token direction) x NW / WGM (weight direction).
+// as WGM (token direction) x NW / WGM (weight direction); at most 256 registers
+// per wave (two waves per SIMD: one workgroup of 8 waves or two of 4 per CU).
 template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
+__global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
                                                                    uint16_t* __restrict__ C,
@@ -325,6 +329,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
   constexpr int CPR = BK / 8;                             // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;                           // rows per 16-byte-per-lane load
   constexpr int RSH = CPR == 8 ? 1 : (CPR == 4 ? 2 : 3);  // rows per 256-byte LDS phase = 1 << RSH
   constexpr int STAGE = ROWS * BK;                        // bf16 elements per stage
   constexpr int L = ROWS * CPR / (64 * NW);         // 16-byte loads per wave per stage
@@ -424,7 +429,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
       const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       if (r < BM) {
         const int rr = r < t.rows ? r : 0;
-        const int src = gather ? clamp_row(s_gidx[gbuf][w][q * 8 + lane / CPR], xrows) : t.row0 + rr;
+        const int src = gather ? clamp_row(s_gidx[gbuf][w][q * RPL + lane / CPR], xrows) : t.row0 + rr;
         rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
       } else {
         const int wr = r - BM;
@@ -499,8 +504,8 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
                 v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
                                : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
               uint2 pk;
-              pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-              pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              pk.x = pack_bf16x2(v[0], v[1]);
+              pk.y = pack_bf16x2(v[2], v[3]);
               *reinterpret_cast<uint2*>(crow + n) = pk;
             }
           }
@@ -509,12 +514,12 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
   };
 
   if (gather) {
-    static_assert(CPR == 8, "8 rows per load instruction");
-    fetch_gather_rows<NA, NW>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
+    fetch_gather_rows<NA, NW, RPL>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
     wait_vmcnt<0>();
   }
   set_rows(decode(0));  // rows of the tile of the next stage to load
-  if (gather && my_tiles > 1) fetch_gather_rows<NA, NW>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
+  if (gather && my_tiles > 1) fetch_gather_rows<NA, NW, RPL>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
+
   int lt_i = 0, lt_k = 0, issued = 0;
   auto issue_next = [&]() {
     issue(issued % S, lt_k);
@@ -528,7 +533,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_pipe_kernel(const uin
         }
         set_rows(decode(lt_i));
         if (gather && lt_i + 1 < my_tiles)
-          fetch_gather_rows<NA, NW>(gather, decode(lt_i + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
+          fetch_gather_rows<NA, NW, RPL>(gather, decode(lt_i + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
       }
     }
   };
@@ -704,11 +709,11 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   int a_next = 0, a_tile = 0, a_k = 0;
   int w_next = 0, w_tile = 0, w_k = 0;
   if (gather) {
-    fetch_gather_rows<LA, NW>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
+    fetch_gather_rows<LA, NW, 8>(gather, decode(0), w, lane, &s_gidx[0][w][0]);
     wait_vmcnt<0>();
   }
   set_rows_a(decode(0));
-  if (gather && my_tiles > 1) fetch_gather_rows<LA, NW>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
+  if (gather && my_tiles > 1) fetch_gather_rows<LA, NW, 8>(gather, decode(1), w, lane, &s_gidx[1][w][0]);
   set_rows_w(decode(0));
   auto issue_a = [&]() {
     uint16_t* st = s_a + (a_next & 1) * ASTAGE;
@@ -725,7 +730,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
         gbuf ^= 1;
         set_rows_a(decode(a_tile));
         if (gather && a_tile + 1 < my_tiles)
-          fetch_gather_rows<LA, NW>(gather, decode(a_tile + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
+          fetch_gather_rows<LA, NW, 8>(gather, decode(a_tile + 1), w, lane, &s_gidx[gbuf ^ 1][w][0]);
       }
     }
   };
@@ -795,8 +800,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
                 v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
                                : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
               uint2 pk;
-              pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-              pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+              pk.x = pack_bf16x2(v[0], v[1]);
+              pk.y = pack_bf16x2(v[2], v[3]);
               *reinterpret_cast<uint2*>(crow + n) = pk;
             }
           }
@@ -880,7 +885,8 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
   if (tiles <= 0) return hipSuccess;
-  const int grid = (int)(tiles < cus ? tiles : cus);
+  const int64_t slots = (int64_t)cus * (8 / NW);  // resident workgroups
+  const int grid = (int)(tiles < slots ? tiles : slots);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
   hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
