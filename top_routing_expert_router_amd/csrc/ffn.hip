@@ -295,6 +295,12 @@ struct PipeTile {
   int e, row0, rows, n0;
 };
 
+// Cache policy of a direct-to-LDS load: 0, or non-temporal (kLoadNT) for
+// weight rows that no other tile reads (NTW: every expert fits one m-tile), so
+// that the streamed weights do not push the token rows and the hidden
+// activations, which other tiles and the next GEMM read again, out of L2.
+constexpr int kLoadNT = 2;
+
 // Gathered A (A = the token rows x, gather = row_token): a wave's A loads of a
 // tile cover NA groups of RPL packed rows (group q: rows RPL (q NW + w) .. +RPL-1).  One
 // direct-to-LDS load of 4 bytes per lane brings their row_token entries into
@@ -317,7 +323,7 @@ __device__ __forceinline__ int clamp_row(int tok, int xrows) { return tok < 0 ? 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
 // as WGM (token direction) x NW / WGM (weight direction); at most 256 registers
 // per wave (two waves per SIMD: one workgroup of 8 waves or two of 4 per CU).
-template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW, bool NTW>
 __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
@@ -444,9 +450,11 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
     uint16_t* st = smem + buf * STAGE;
     const int k0 = kstep * BK;
 #pragma unroll
-    for (int q = 0; q < L; ++q)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rowp[q]) + k0, st + (q * NW + w) * 512, 16, 0,
-                                       0);
+    for (int q = 0; q < L; ++q) {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(rowp[q]) + k0;
+      if (NTW && q >= NA) __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, kLoadNT);
+      else __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, 0);
+    }
   };
 
   f32x16_t acc[NF][MF];
@@ -593,7 +601,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
 // (shared by the tiles of one expert, mostly L2 hits) one step.  BK = 64, 8
 // waves.
 // ---------------------------------------------------------------------------
-template <int BM, int WR, int SW, int WGM, int EPI>
+template <int BM, int WR, int SW, int WGM, int EPI, bool NTW>
 __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
@@ -737,9 +745,11 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   auto issue_w = [&]() {
     uint16_t* st = s_w + (w_next % SW) * WSTAGE;
 #pragma unroll
-    for (int q = 0; q < LW; ++q)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(rowW[q]) + w_k * BK,
-                                       st + (q * NW + w) * 512, 16, 0, 0);
+    for (int q = 0; q < LW; ++q) {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(rowW[q]) + w_k * BK;
+      if (NTW) __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, kLoadNT);
+      else __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, 0);
+    }
     ++w_next;
     if (++w_k == nk) {
       w_k = 0;
@@ -858,7 +868,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   }
 }
 
-template <int BM, int WR, int SW, int WGM, int EPI>
+template <int BM, int WR, int SW, int WGM, int EPI, bool NTW>
 static hipError_t launch_ring(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
                               hipStream_t st) {
@@ -868,16 +878,16 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   if (tiles <= 0) return hipSuccess;
   const int grid = (int)(tiles < cus ? tiles : cus);
   const size_t shm = sizeof(uint16_t) * ((size_t)2 * BM + (size_t)SW * WR) * 64 + sizeof(int) * 2 * (size_t)(E + 1);
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI>,
+  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (err != hipSuccess) return err;
-  grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI><<<dim3(grid), dim3(512), shm, st>>>(
+  grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW><<<dim3(grid), dim3(512), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
       static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
 }
 
-template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW = 8>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
                               hipStream_t st) {
@@ -888,10 +898,10 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   const int64_t slots = (int64_t)cus * (8 / NW);  // resident workgroups
   const int grid = (int)(tiles < slots ? tiles : slots);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW>,
+  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (err != hipSuccess) return err;
-  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
+  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
       static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
   return hipGetLastError();
@@ -927,8 +937,8 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
 
 template <int EPI>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
-                             const int32_t* offsets, int E, int N, int K, int64_t R_max, hipStream_t st,
-                             const int32_t* gather = nullptr, int xrows = 0) {
+                             const int32_t* offsets, int E, int N, int K, int64_t R_max, int64_t rows_cap,
+                             hipStream_t st, const int32_t* gather = nullptr, int xrows = 0) {
   if (vec && bf16 && K % 64 == 0) {
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -948,10 +958,18 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       };
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
-          return launch_ring<256, 192, 3, 4, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
-      return launch_pipe<256, 256, 64, 2, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
+          return rows_cap <= 256
+                     ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
+                     : launch_ring<256, 192, 3, 4, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
+                                                              st);
+      return rows_cap <= 256
+                 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
+                 : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
+                                                               st);
     }
-    return launch_pipe<128, 256, 64, 3, 2, EPI>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
+    return rows_cap <= 128
+               ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
+               : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
   }
   if (gather) return hipErrorInvalidValue;  // only the tiled kernels read gathered rows
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
@@ -963,19 +981,23 @@ bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 
 
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st, const int32_t* gather, int xrows) {
+                             int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather, int xrows) {
   if (R_max == 0) return hipSuccess;
   if (gather && !expert_ffn_gathers(bf16, vec, H)) return hipErrorInvalidValue;
   hipError_t err;
   switch (act) {
-    case 0: err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st, gather, xrows); break;
-    case 1: err = launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, st, gather, xrows); break;
+    case 0:
+      err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
+      break;
+    case 1:
+      err = launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
+      break;
     default:
-      err = launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, st, gather, xrows);
+      err = launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
       break;
   }
   if (err != hipSuccess) return err;
-  return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, st);
+  return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, rows_cap, st);
 }
 
 }  // namespace moe

@@ -73,9 +73,12 @@ hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T
 // and packed row r of the first GEMM reads x[gather[r]] (the dispatch folded
 // into the GEMM's loads).
 bool expert_ffn_gathers(bool bf16, bool vec, int H);
+// rows_cap: most rows any one expert can hold (the capacity, or R_max when
+// nothing caps it); at most one m-tile per expert lets the weight loads stream.
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, hipStream_t st, const int32_t* gather = nullptr, int xrows = 0);
+                             int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather = nullptr,
+                             int xrows = 0);
 // shared (optional): the shared expert's output [T][H], added after the routed terms.
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
                           int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st,

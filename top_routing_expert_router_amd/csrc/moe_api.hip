@@ -52,6 +52,13 @@ int effective_capacity(const moe_config* c) {
   return (int)C;
 }
 
+// Most rows one expert can hold: the capacity, or every kept row when no
+// capacity limits (the expert FFN streams weight rows that one tile covers).
+int64_t expert_rows_cap(const moe_config* c, int64_t R_max) {
+  const int C = effective_capacity(c);
+  return C == INT32_MAX || (int64_t)C > R_max ? R_max : (int64_t)C;
+}
+
 struct Layout {
   int nb, Q;
   bool split;  // split-bf16 router buffers present
@@ -270,7 +277,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* X, const moe_plan* pl
   const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(X) && aligned16(Y) && aligned16(W1) &&
                    aligned16(W3) && aligned16(W2) && aligned16(h);
   hipError_t e = moe::launch_expert_ffn(X, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec, R_max,
-                                        static_cast<hipStream_t>(stream));
+                                        expert_rows_cap(c, R_max), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert_ffn");
 }
 
@@ -306,7 +313,8 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
                    aligned16(W3) && aligned16(W2) && aligned16(h);
   if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
     hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
-                                          R_max, static_cast<hipStream_t>(stream), plan->row_token, c->T);
+                                          R_max, expert_rows_cap(c, R_max), static_cast<hipStream_t>(stream),
+                                          plan->row_token, c->T);
     if (e != hipSuccess) return hip_fail(e, "expert_ffn");
   } else {
     if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
@@ -334,7 +342,8 @@ moe_status moe_shared_expert(const moe_config* c, const void* x, const void* Ws1
   // one expert holding every token: rows [0, T)
   hipError_t e = moe::launch_dense_offsets(off, c->T, st);
   if (e == hipSuccess)
-    e = moe::launch_expert_ffn(x, Ws1, Ws3, Ws2, hs, Ys, off, 1, c->H, c->shared_F, c->act, bf16, vec, c->T, st);
+    e = moe::launch_expert_ffn(x, Ws1, Ws3, Ws2, hs, Ys, off, 1, c->H, c->shared_F, c->act, bf16, vec, c->T, c->T,
+                               st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "shared_expert");
 }
 
@@ -371,7 +380,8 @@ moe_status moe_forward_shared(const moe_config* c, const void* x, const float* W
                    aligned16(W3) && aligned16(W2) && aligned16(h);
   if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
     hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
-                                          R_max, static_cast<hipStream_t>(stream), plan->row_token, c->T);
+                                          R_max, expert_rows_cap(c, R_max), static_cast<hipStream_t>(stream),
+                                          plan->row_token, c->T);
     if (e != hipSuccess) return hip_fail(e, "expert_ffn");
   } else {
     if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
