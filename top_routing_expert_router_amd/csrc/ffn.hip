@@ -503,19 +503,26 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
 #pragma unroll
         for (int f = 0; f < HF; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-            if (n < N) {
+          for (int g = 0; g < 4; g += 2) {
+            uint32_t pk[2][2];  // [group g, g + 1][packed column pair]
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
               float v[4];
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj)
-                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
-                               : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
-              uint2 pk;
-              pk.x = pack_bf16x2(v[0], v[1]);
-              pk.y = pack_bf16x2(v[2], v[3]);
-              *reinterpret_cast<uint2*>(crow + n) = pk;
+                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * (g + h) + jj], acc[HF + f][i][4 * (g + h) + jj])
+                               : epilogue<EPI>(acc[f][i][4 * (g + h) + jj], 0.0f);
+              pk[h][0] = pack_bf16x2(v[0], v[1]);
+              pk[h][1] = pack_bf16x2(v[2], v[3]);
             }
+            // lanes l and l + 32 hold the two column halves of the 8-column
+            // groups of one row: after swapping lanes 32..63 of group g's
+            // words with lanes 0..31 of group g + 1's, lane l holds all of
+            // group g and lane l + 32 all of group g + 1 (16-byte stores)
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
+            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
           }
       }
     }
@@ -801,19 +808,26 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
 #pragma unroll
         for (int f = 0; f < HF; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * g + 4 * (lane >> 5);
-            if (n < N) {
+          for (int g = 0; g < 4; g += 2) {
+            uint32_t pk[2][2];  // [group g, g + 1][packed column pair]
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
               float v[4];
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj)
-                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * g + jj], acc[HF + f][i][4 * g + jj])
-                               : epilogue<EPI>(acc[f][i][4 * g + jj], 0.0f);
-              uint2 pk;
-              pk.x = pack_bf16x2(v[0], v[1]);
-              pk.y = pack_bf16x2(v[2], v[3]);
-              *reinterpret_cast<uint2*>(crow + n) = pk;
+                v[jj] = kGated ? epilogue<EPI>(acc[f][i][4 * (g + h) + jj], acc[HF + f][i][4 * (g + h) + jj])
+                               : epilogue<EPI>(acc[f][i][4 * (g + h) + jj], 0.0f);
+              pk[h][0] = pack_bf16x2(v[0], v[1]);
+              pk[h][1] = pack_bf16x2(v[2], v[3]);
             }
+            // lanes l and l + 32 hold the two column halves of the 8-column
+            // groups of one row: after swapping lanes 32..63 of group g's
+            // words with lanes 0..31 of group g + 1's, lane l holds all of
+            // group g and lane l + 32 all of group g + 1 (16-byte stores)
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+            const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
+            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
           }
       }
     }
