@@ -136,6 +136,13 @@ def summarize_pmc(fetch_db, write_db, workload, cmd):
         tot += fb + wb
         print(f"kernel: {n[:90]}  read_bytes_per_launch: {fb:.4g}  write_bytes_per_launch: {wb:.4g}")
     print(f"hbm_bytes_per_step_expert_stage: {tot:.6g}")
+    print("# the other kernels of the same runs (route, slot assignment, combine), bytes per launch")
+    for n in sorted(set(f) | set(w)):
+        if EXPERT_KERNEL in n or "copy" in n.lower() or "elementwise" in n.lower():
+            continue
+        fb = sum(f.get(n, [0])) / max(len(f.get(n, [1])), 1) * 1024 * sf
+        wb = sum(w.get(n, [0])) / max(len(w.get(n, [1])), 1) * 1024 * sw
+        print(f"other_kernel: {n[:90]}  read_bytes_per_launch: {fb:.4g}  write_bytes_per_launch: {wb:.4g}")
 
 
 def main():
