@@ -231,6 +231,10 @@ def _run_edge(gpu, r):
     # (48: padded expert columns; 36 and T=1: a single, mostly empty token tile)
     dict(name="E48", E=48, k=2, T=333), dict(name="E36", E=36, k=3, T=1), dict(name="E64H128", E=64, k=1, H=128),
     dict(name="E44", E=44, k=4, T=257, H=192),
+    # tiled GEMMs whose output width is 8 mod 16: the last 8-column group of a
+    # row is stored by the lower half-wave only (F=72 for the first GEMM, H=72
+    # for the second)
+    dict(name="F72", H=128, F=72, T=300), dict(name="H72", H=72, F=128, T=300),
 ])
 def test_edge_shapes(gpu, kw):
     base = recipes.SMALL["5"].scaled(T=200, H=64, F=96, E=16, k=4)
