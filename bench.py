@@ -69,7 +69,27 @@ def read_traffic(workload):
 
 
 EXPERT_KERNEL = "grouped_gemm"
+EPI_COMBINE1 = 4  # epilogue argument of the second GEMM that also does the top-1 combine
 COPY_BYTES = 256 << 20
+
+
+def _gemm_epilogue(name):
+    """Epilogue template argument of a tiled grouped-GEMM kernel name, else None."""
+    import re
+
+    m = re.search(r"grouped_gemm_(pipe|ring)_kernel<([^>]*)>", name)
+    if not m:
+        return None
+    args = [a.strip() for a in m.group(2).split(",")]
+    try:
+        return int(args[5] if m.group(1) == "pipe" else args[4])
+    except (IndexError, ValueError):
+        return None
+
+
+def _stage_kernel(name):
+    """A launch of the expert-FFN stage (the forward's combine-fused second GEMM is not)."""
+    return EXPERT_KERNEL in name and _gemm_epilogue(name) != EPI_COMBINE1
 
 
 def _kernel_rows(db_path):
@@ -129,16 +149,17 @@ def summarize_pmc(fetch_db, write_db, workload, cmd):
     print(f"write_scale_from_copy: {sw:.4f}   # copy writes {COPY_BYTES} B; WRITE_SIZE read {cw} KiB")
     tot = 0.0
     for n in sorted(set(f) | set(w)):
-        if EXPERT_KERNEL not in n:
+        if not _stage_kernel(n):
             continue
         fb = sum(f.get(n, [0])) / max(len(f.get(n, [1])), 1) * 1024 * sf
         wb = sum(w.get(n, [0])) / max(len(w.get(n, [1])), 1) * 1024 * sw
         tot += fb + wb
         print(f"kernel: {n[:90]}  read_bytes_per_launch: {fb:.4g}  write_bytes_per_launch: {wb:.4g}")
     print(f"hbm_bytes_per_step_expert_stage: {tot:.6g}")
-    print("# the other kernels of the same runs (route, slot assignment, combine), bytes per launch")
+    print("# the other kernels of the same runs (route, slot assignment, combine, the forward's second GEMM\n"
+          "# with the top-1 combine folded in), bytes per launch")
     for n in sorted(set(f) | set(w)):
-        if EXPERT_KERNEL in n or "copy" in n.lower() or "elementwise" in n.lower():
+        if _stage_kernel(n) or "copy" in n.lower() or "elementwise" in n.lower():
             continue
         fb = sum(f.get(n, [0])) / max(len(f.get(n, [1])), 1) * 1024 * sf
         wb = sum(w.get(n, [0])) / max(len(w.get(n, [1])), 1) * 1024 * sw

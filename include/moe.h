@@ -223,7 +223,10 @@ moe_status moe_combine(const moe_config *cfg, const void *Y, const moe_plan *pla
 /* The whole layer on `stream`: moe_route, moe_dispatch, moe_expert_ffn,
  * moe_combine.  Where the expert GEMMs run on the tiled bf16 path (bf16, H % 64
  * == 0, 16-byte aligned buffers), the first GEMM reads the token rows of x
- * through plan->row_token itself and the dispatch copy is not made.  X and Y:
+ * through plan->row_token itself and the dispatch copy is not made; with
+ * k == 1 there (and F % 64 == 0, 16-byte aligned residual and y) the second GEMM
+ * also does the combine, writing y directly with the arithmetic of moe_combine
+ * (bit-identical to the separate calls), and Y is not written.  X and Y:
  * device [R_max][H] dtype scratch; their contents afterwards are unspecified. */
 moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, const float *bias, const void *W1,
                        const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,

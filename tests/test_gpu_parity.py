@@ -196,6 +196,45 @@ def test_forward_full_size_sampled(gpu, name):
     U.assert_close(U.host(y)[toks], yref, r.dtype == recipes.BF16, f"forward full-size run {r.name} sample")
 
 
+@pytest.mark.parametrize("shape", [
+    # top-1, bf16, H % 64 == 0, F % 64 == 0: the second GEMM writes y itself;
+    # one shape per tiled kernel it can run in (128-row pipe, 256-row pipe,
+    # split-ring), with drops (cf < 1) so that the dropped-token pass matters
+    dict(name="pipe128", T=2048, H=256, E=16, F=512, cf=1.0),
+    dict(name="pipe256", T=4096, H=256, E=8, F=256, cf=0.5),
+    dict(name="ring", T=16384, H=768, E=8, F=256, cf=0.5),
+])
+@pytest.mark.parametrize("residual", [False, True])
+def test_forward_top1_fused_equals_stages(gpu, shape, residual):
+    """moe_forward (combine folded into the second GEMM) against the stage entry
+    points route -> dispatch -> expert_ffn -> combine: bit-identical y."""
+    import torch
+
+    kw = dict(shape)
+    r = recipes.RUNS["2"].scaled(name="top1-" + kw.pop("name"), **kw)
+    d = recipes.gen_all(r)
+    gplan, y = _gpu_forward(r, gpu, d, residual=residual)
+    cfg = B.MoEConfig.from_run(r)
+    xd = U.dev(d["x"], gpu)
+    w = (U.dev(d["w1"], gpu), None, U.dev(d["w2"], gpu))
+    plan = B.alloc_plan(cfg, gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    rmax = B.max_rows(cfg)
+    X = torch.zeros((rmax, r.H), dtype=torch.bfloat16, device=gpu)
+    Y = torch.zeros_like(X)
+    ys = torch.empty((r.T, r.H), dtype=torch.bfloat16, device=gpu)
+    B.route(cfg, xd, U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), plan, ws)
+    B.dispatch(cfg, xd, plan, X)
+    B.expert_ffn(cfg, X, plan, *w, Y, ws)
+    B.combine(cfg, Y, plan, xd if residual else None, ys)
+    torch.cuda.synchronize()
+    nd = int(U.host(plan["n_dropped"])[0])
+    print(f"[parity] top-1 fused {r.name} residual={residual}: dropped {nd} of {r.T}", flush=True)
+    assert nd > 0 or r.cf >= 1.0
+    assert np.array_equal(U.host(plan["dst_row"]), U.host(gplan["dst_row"]))
+    assert np.array_equal(U.host(y).view(np.uint16), U.host(ys).view(np.uint16))
+
+
 def test_determinism(gpu):
     r = recipes.SMALL["3a"]
     d = recipes.gen_all(r)

@@ -18,7 +18,7 @@
 
 namespace moe {
 
-enum { EPI_NONE = 0, EPI_RELU = 1, EPI_GELU = 2, EPI_SWIGLU = 3 };
+enum { EPI_NONE = 0, EPI_RELU = 1, EPI_GELU = 2, EPI_SWIGLU = 3, EPI_COMBINE1 = 4 };
 
 // GELU x Phi(x) = x/2 + |x|/2 (1 - erfc(|x| / sqrt 2)) with
 // erfc(z) ~ (a1 t + ... + an t^n) e^(-z^2), t = 1 / (1 + p z), from Abramowitz &
@@ -309,6 +309,35 @@ struct PipeTile {
   int e, row0, rows, n0;
 };
 
+// Top-1 combine of 8 output columns: o holds the bf16 expert outputs (as the
+// second GEMM would store them), r the bf16 residual; fp32 fma, one rounding.
+__device__ __forceinline__ u32x4_t combine1_8(u32x4_t o, u32x4_t r, float g) {
+  u32x4_t out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = __builtin_fmaf(g, __uint_as_float(o[j] << 16), __uint_as_float(r[j] << 16));
+    const float hi = __builtin_fmaf(g, __uint_as_float(o[j] & 0xffff0000u), __uint_as_float(r[j] & 0xffff0000u));
+    out[j] = pack_bf16x2(lo, hi);
+  }
+  return out;
+}
+
+// Top-1 combine, tokens that no packed row holds: y[t] = res[t] (or 0).  Part
+// `part` of `parts`, nthr threads, 16 bytes per thread-iteration.
+__device__ __forceinline__ void combine1_dropped(const Combine1& cmb, uint16_t* __restrict__ y, int H, int rmax,
+                                                 int part, int parts, int tid, int nthr) {
+  const int nch = H / 8;
+  const int64_t total = (int64_t)cmb.T * nch;
+  for (int64_t i = (int64_t)part * nthr + tid; i < total; i += (int64_t)parts * nthr) {
+    const int t = (int)(i / nch);
+    const int c = (int)(i - (int64_t)t * nch) * 8;
+    const int d = cmb.dst_row[t];
+    if (d >= 0 && d < rmax) continue;
+    const u32x4_t v = cmb.res ? *reinterpret_cast<const u32x4_t*>(cmb.res + (size_t)t * H + c) : u32x4_t{0, 0, 0, 0};
+    *reinterpret_cast<u32x4_t*>(y + (size_t)t * H + c) = v;
+  }
+}
+
 // Cache policy of a direct-to-LDS load: 0, or non-temporal (kLoadNT) for
 // weight rows that no other tile reads (NTW: every expert fits one m-tile), so
 // that the streamed weights do not push the token rows and the hidden
@@ -344,7 +373,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows) {
+                                                                   const int32_t* __restrict__ gather, int xrows, Combine1 cmb) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -407,7 +436,10 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   const int my_tiles = total_tiles > slot ? (total_tiles - 1 - slot) / G + 1 : 0;
   const int nk = K / BK;
   const int total_steps = my_tiles * nk;
-  if (total_steps == 0) return;
+  if (total_steps == 0) {
+    if constexpr (EPI == EPI_COMBINE1) combine1_dropped(cmb, C, N, rmax, slot, G, tid, 64 * NW);
+    return;
+  }
 
   auto decode = [&](int i) {  // i-th tile of this workgroup
     const int g = slot + i * G;
@@ -512,8 +544,28 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int m = wm * (MF * 32) + i * 32 + (lane & 31);
-      if (m < t.rows) {
-        uint16_t* crow = C + (size_t)(t.row0 + m) * N;
+      int crow_i = t.row0 + m;  // output row: the packed row, or its token (top-1 combine)
+      bool ok = m < t.rows;
+      float gt = 0.0f;
+      if constexpr (EPI == EPI_COMBINE1) {
+        const int tok = ok ? cmb.row_token[crow_i] : -1;
+        ok = tok >= 0 && tok < cmb.T;
+        crow_i = ok ? tok : 0;
+        gt = cmb.gate[crow_i];
+      }
+      if (ok) {
+        uint16_t* crow = C + (size_t)crow_i * N;
+        u32x4_t rv[HF][2];  // top-1 combine: this lane's residual groups of the row, loaded first
+        if constexpr (EPI == EPI_COMBINE1) {
+#pragma unroll
+          for (int f = 0; f < HF; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; g += 2) {
+              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
+              rv[f][g / 2] = (cmb.res && n < N) ? *reinterpret_cast<const u32x4_t*>(cmb.res + (size_t)crow_i * N + n)
+                                                : u32x4_t{0, 0, 0, 0};
+            }
+        }
 #pragma unroll
         for (int f = 0; f < HF; ++f)
 #pragma unroll
@@ -536,7 +588,9 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
             const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
             const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
-            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+            u32x4_t o = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+            if constexpr (EPI == EPI_COMBINE1) o = combine1_8(o, rv[f][g / 2], gt);
+            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = o;
           }
       }
     }
@@ -610,6 +664,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
       if (j + 1 < total_steps) ct = decode((j + 1) / nk);
     }
   }
+  if constexpr (EPI == EPI_COMBINE1) combine1_dropped(cmb, C, N, rmax, slot, G, tid, 64 * NW);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,7 +684,7 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows) {
+                                                                   const int32_t* __restrict__ gather, int xrows, Combine1 cmb) {
   constexpr int NW = 8, BK = 64, CPR = 8, RSH = 1;
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;
@@ -685,7 +740,10 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
   const int my_tiles = total_tiles > slot ? (total_tiles - 1 - slot) / G + 1 : 0;
   const int nk = K / BK;
   const int total_steps = my_tiles * nk;
-  if (total_steps == 0) return;
+  if (total_steps == 0) {
+    if constexpr (EPI == EPI_COMBINE1) combine1_dropped(cmb, C, N, rmax, slot, G, tid, 64 * NW);
+    return;
+  }
 
   auto decode = [&](int i) {
     const int g = slot + i * G;
@@ -817,8 +875,28 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
       const int m = wm * (MF * 32) + i * 32 + (lane & 31);
-      if (m < t.rows) {
-        uint16_t* crow = C + (size_t)(t.row0 + m) * N;
+      int crow_i = t.row0 + m;  // output row: the packed row, or its token (top-1 combine)
+      bool ok = m < t.rows;
+      float gt = 0.0f;
+      if constexpr (EPI == EPI_COMBINE1) {
+        const int tok = ok ? cmb.row_token[crow_i] : -1;
+        ok = tok >= 0 && tok < cmb.T;
+        crow_i = ok ? tok : 0;
+        gt = cmb.gate[crow_i];
+      }
+      if (ok) {
+        uint16_t* crow = C + (size_t)crow_i * N;
+        u32x4_t rv[HF][2];  // top-1 combine: this lane's residual groups of the row, loaded first
+        if constexpr (EPI == EPI_COMBINE1) {
+#pragma unroll
+          for (int f = 0; f < HF; ++f)
+#pragma unroll
+            for (int g = 0; g < 4; g += 2) {
+              const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
+              rv[f][g / 2] = (cmb.res && n < N) ? *reinterpret_cast<const u32x4_t*>(cmb.res + (size_t)crow_i * N + n)
+                                                : u32x4_t{0, 0, 0, 0};
+            }
+        }
 #pragma unroll
         for (int f = 0; f < HF; ++f)
 #pragma unroll
@@ -841,7 +919,9 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
             const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
             const int n = t.n0 + wn * (HF * 32) + f * 32 + 8 * (g + (lane >> 5));
-            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+            u32x4_t o = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+            if constexpr (EPI == EPI_COMBINE1) o = combine1_8(o, rv[f][g / 2], gt);
+            if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = o;
           }
       }
     }
@@ -894,12 +974,13 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
       if (j + 1 < total_steps) ct = decode((j + 1) / nk);
     }
   }
+  if constexpr (EPI == EPI_COMBINE1) combine1_dropped(cmb, C, N, rmax, slot, G, tid, 64 * NW);
 }
 
 template <int BM, int WR, int SW, int WGM, int EPI, bool NTW>
 static hipError_t launch_ring(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              hipStream_t st) {
+                              const Combine1& cmb, hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -911,14 +992,14 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW><<<dim3(grid), dim3(512), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb);
   return hipGetLastError();
 }
 
 template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              hipStream_t st) {
+                              const Combine1& cmb, hipStream_t st) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -931,7 +1012,7 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb);
   return hipGetLastError();
 }
 
@@ -966,7 +1047,8 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
 template <int EPI>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
                              const int32_t* offsets, int E, int N, int K, int64_t R_max, int64_t rows_cap,
-                             hipStream_t st, const int32_t* gather = nullptr, int xrows = 0) {
+                             hipStream_t st, const int32_t* gather = nullptr, int xrows = 0,
+                             const Combine1& cmb = Combine1{}) {
   if (vec && bf16 && K % 64 == 0) {
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -987,31 +1069,35 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
           return rows_cap <= 256
-                     ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
+                     ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
                      : launch_ring<256, 192, 3, 4, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
-                                                              st);
+                                                              cmb, st);
       return rows_cap <= 256
-                 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
+                 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
                  : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
-                                                               st);
+                                                               cmb, st);
     }
     return rows_cap <= 128
-               ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st)
-               : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, st);
+               ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
+               : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st);
   }
-  if (gather) return hipErrorInvalidValue;  // only the tiled kernels read gathered rows
+  // only the tiled kernels read gathered rows or combine
+  if (gather || EPI == EPI_COMBINE1) return hipErrorInvalidValue;
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
 }
 
 bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 64 == 0; }
+bool expert_ffn_combines(bool bf16, bool vec, int H, int F) { return bf16 && vec && H % 8 == 0 && F % 64 == 0; }
 
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
-                             int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather, int xrows) {
-  if (R_max == 0) return hipSuccess;
+                             int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather, int xrows,
+                             const Combine1* cmb) {
+  if (R_max == 0) return cmb ? hipErrorInvalidValue : hipSuccess;  // the combine needs a launch to run in
   if (gather && !expert_ffn_gathers(bf16, vec, H)) return hipErrorInvalidValue;
+  if (cmb && !expert_ffn_combines(bf16, vec, H, F)) return hipErrorInvalidValue;
   hipError_t err;
   switch (act) {
     case 0:
@@ -1025,6 +1111,9 @@ hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, cons
       break;
   }
   if (err != hipSuccess) return err;
+  if (cmb)
+    return launch_one<EPI_COMBINE1>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, rows_cap, st, nullptr, 0,
+                                    *cmb);
   return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, rows_cap, st);
 }
 

@@ -73,12 +73,27 @@ hipError_t launch_dispatch(const void* x, const int32_t* dst_row, void* X, int T
 // and packed row r of the first GEMM reads x[gather[r]] (the dispatch folded
 // into the GEMM's loads).
 bool expert_ffn_gathers(bool bf16, bool vec, int H);
+// Top-1 combine folded into the second GEMM (one choice per token, so packed
+// row r is the only term of token row_token[r]): y[t] = fma(gate[t], Y, res[t])
+// with Y rounded to bf16 first, as the combine would read it, then rounded once;
+// tokens with dst_row[t] outside [0, R_max) get y[t] = res[t] (0 without one).
+struct Combine1 {
+  const int32_t* row_token;  // [R_max]
+  const int32_t* dst_row;    // [T]
+  const float* gate;         // [T]
+  const uint16_t* res;       // [T][H] bf16 or null
+  int T;
+};
 // rows_cap: most rows any one expert can hold (the capacity, or R_max when
 // nothing caps it); at most one m-tile per expert lets the weight loads stream.
+// cmb (optional, bf16 tiled path only, see expert_ffn_combines): Y is then the
+// layer output y [T][H] instead of the expert rows.
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
                              int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather = nullptr,
-                             int xrows = 0);
+                             int xrows = 0, const Combine1* cmb = nullptr);
+// whether launch_expert_ffn can take cmb for these shapes
+bool expert_ffn_combines(bool bf16, bool vec, int H, int F);
 // shared (optional): the shared expert's output [T][H], added after the routed terms.
 hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* gate, const void* residual, void* y,
                           int T, int H, int k, int rmax, bool bf16, bool vec_ok, hipStream_t st,

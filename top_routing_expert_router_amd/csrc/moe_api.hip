@@ -312,10 +312,17 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
   const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(x) && aligned16(Y) && aligned16(W1) &&
                    aligned16(W3) && aligned16(W2) && aligned16(h);
   if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
-    hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, Y, plan->offsets, c->E, c->H, c->F, c->act, bf16, vec,
-                                          R_max, expert_rows_cap(c, R_max), static_cast<hipStream_t>(stream),
-                                          plan->row_token, c->T);
+    // Top-1 on the same path: the second GEMM writes y itself (Y unused).
+    const bool fuse = c->k == 1 && moe::expert_ffn_combines(bf16, vec, c->H, c->F) && aligned16(residual) &&
+                      aligned16(y);
+    const moe::Combine1 cmb{plan->row_token, plan->dst_row, plan->topk_gate,
+                            static_cast<const uint16_t*>(residual), c->T};
+    hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, fuse ? y : Y, plan->offsets, c->E, c->H, c->F, c->act,
+                                          bf16, vec, R_max, expert_rows_cap(c, R_max),
+                                          static_cast<hipStream_t>(stream), plan->row_token, c->T,
+                                          fuse ? &cmb : nullptr);
     if (e != hipSuccess) return hip_fail(e, "expert_ffn");
+    if (fuse) return MOE_OK;
   } else {
     if ((s = moe_dispatch(c, x, plan, X, stream)) != MOE_OK) return s;
     if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
