@@ -227,7 +227,10 @@ moe_status moe_combine(const moe_config *cfg, const void *Y, const moe_plan *pla
  * k == 1 there (and F % 64 == 0, 16-byte aligned residual and y) the second GEMM
  * also does the combine, writing y directly with the arithmetic of moe_combine
  * (bit-identical to the separate calls), and Y is not written.  X and Y:
- * device [R_max][H] dtype scratch; their contents afterwards are unspecified. */
+ * device [R_max][H] dtype scratch; their contents afterwards are unspecified.
+ * y may be the same buffer as residual and x (the layer applied in place): x is
+ * read by launches that precede every write of y, and each element of y is
+ * written by the thread that read its residual. */
 moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, const float *bias, const void *W1,
                        const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,
                        void *X, void *Y, void *ws, size_t ws_bytes, void *stream);

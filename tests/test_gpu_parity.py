@@ -235,6 +235,28 @@ def test_forward_top1_fused_equals_stages(gpu, shape, residual):
     assert np.array_equal(U.host(y).view(np.uint16), U.host(ys).view(np.uint16))
 
 
+@pytest.mark.parametrize("name", ["2", "3a"])
+def test_forward_in_place(gpu, name):
+    """y, the residual and x as one buffer (top-1 with the combine in the second
+    GEMM, and top-4 with the separate combine): the same y as with three buffers."""
+    import torch
+
+    r = recipes.SMALL[name]
+    d = recipes.gen_all(r)
+    _, y = _gpu_forward(r, gpu, d, residual=True)
+    cfg = B.MoEConfig.from_run(r)
+    rmax = B.max_rows(cfg)
+    xd = U.dev(d["x"], gpu)
+    plan = B.alloc_plan(cfg, gpu)
+    X = torch.empty((max(rmax, 1), r.H), dtype=xd.dtype, device=gpu)
+    Y = torch.empty_like(X)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.forward(cfg, xd, U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), U.dev(d["w1"], gpu), U.dev(d["w3"], gpu),
+              U.dev(d["w2"], gpu), xd, xd, plan, X, Y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(U.host(xd), U.host(y))
+
+
 def test_determinism(gpu):
     r = recipes.SMALL["3a"]
     d = recipes.gen_all(r)

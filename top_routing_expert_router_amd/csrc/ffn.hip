@@ -373,7 +373,8 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows, Combine1 cmb) {
+                                                                   const int32_t* __restrict__ gather, int xrows,
+                                                                   Combine1 cmb) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -684,7 +685,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
                                                                    uint16_t* __restrict__ C,
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
-                                                                   const int32_t* __restrict__ gather, int xrows, Combine1 cmb) {
+                                                                   const int32_t* __restrict__ gather, int xrows,
+                                                                   Combine1 cmb) {
   constexpr int NW = 8, BK = 64, CPR = 8, RSH = 1;
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;
@@ -1068,18 +1070,19 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
       };
       if constexpr (!kGated)
         if (fill(192) > fill(256) + 0.05)
-          return rows_cap <= 256
-                     ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
-                     : launch_ring<256, 192, 3, 4, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
-                                                              cmb, st);
-      return rows_cap <= 256
-                 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
-                 : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows,
-                                                               cmb, st);
+          return rows_cap <= 256 ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                           gather, xrows, cmb, st)
+                                 : launch_ring<256, 192, 3, 4, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                            gather, xrows, cmb, st);
+      return rows_cap <= 256 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                          gather, xrows, cmb, st)
+                             : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                           gather, xrows, cmb, st);
     }
-    return rows_cap <= 128
-               ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st)
-               : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st);
+    return rows_cap <= 128 ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                        gather, xrows, cmb, st)
+                           : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                         gather, xrows, cmb, st);
   }
   // only the tiled kernels read gathered rows or combine
   if (gather || EPI == EPI_COMBINE1) return hipErrorInvalidValue;
