@@ -479,6 +479,9 @@ def main():
         "combine": {"us": round(stage_us["combine"], 2), "GB_s": round(gbs(comb_bytes, stage_us["combine"]), 1),
                     "hbm_frac": round(gbs(comb_bytes, stage_us["combine"]) / PEAK_HBM_GBS, 4)},
     }
+    if k == 1 and bf16 and H % 64 == 0 and F % 64 == 0:
+        stages_out["combine"]["note"] = ("the stage entry point; moe_forward folds the top-1 combine into the second "
+                                         "GEMM's epilogue on this shape")
     stages_cold = None
     if stage_cold_us is not None:
         cold_bytes = {"route": route_bytes, "dispatch": disp_bytes, "combine": comb_bytes}
