@@ -166,6 +166,45 @@ def summarize_pmc(fetch_db, write_db, workload, cmd):
         print(f"other_kernel: {n[:90]}  read_bytes_per_launch: {fb:.4g}  write_bytes_per_launch: {wb:.4g}")
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(db_path, workload, cmd, cus=256):
+    """Matrix-core work of the grouped-GEMM launches from a rocprofv3 --pmc run of MFMA_COUNTERS.
+    Each counter arrives as one row per hardware instance of a dispatch: the SQ counters are
+    summed over the instances, GRBM_GUI_ACTIVE (the dispatch's active cycles, per instance)
+    taken at its largest.  SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 bf16 flops; the busy
+    share is SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x CUs x 4 SIMDs.  Averages per launch."""
+    import sqlite3
+
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select dispatch_id, name, counter_name, counter_value, duration from pmc_events").fetchall()
+    disp = {}
+    for d, n, c, v, dur in rows:
+        if EXPERT_KERNEL not in n:
+            continue
+        e = disp.setdefault(d, {"name": n, "dur": dur, "c": {}})
+        if c == "GRBM_GUI_ACTIVE":
+            e["c"][c] = max(e["c"].get(c, 0.0), v)
+        else:
+            e["c"][c] = e["c"].get(c, 0.0) + v
+    per = {}
+    for e in disp.values():
+        per.setdefault(e["name"], []).append(e)
+    print(f"# rocprofv3 PMC summary: matrix-core work of the grouped-GEMM launches\n# command: {cmd}")
+    print(f"workload: {workload}")
+    print(f"ffn_hip_sha256_16: {src_hash()}")
+    for n in sorted(per):
+        es = per[n]
+        avg = lambda c: sum(e["c"].get(c, 0.0) for e in es) / len(es)
+        flops = avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        gui = avg("GRBM_GUI_ACTIVE")
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (gui * cus * 4) if gui else float("nan")
+        dur_us = sum(e["dur"] for e in es) / len(es) / 1e3
+        print(f"kernel: {n[:90]}  launches: {len(es)}  mfma_flops_per_launch: {flops:.4g}  "
+              f"mfma_busy_frac: {busy:.4f}  gui_active_cycles: {gui:.4g}  us_under_counters: {dur_us:.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +222,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DB", help="print the kernel summary of a rocprofv3 database")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print expert-FFN HBM bytes from FETCH_SIZE / WRITE_SIZE rocprofv3 databases")
+    ap.add_argument("--summarize-mfma", metavar="DB",
+                    help="print the grouped-GEMM matrix-core counters of a rocprofv3 --pmc database")
     ap.add_argument("--cmd", default="", help="command line to record in a summary")
     args = ap.parse_args()
     if args.summarize_trace:
@@ -190,6 +231,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, WORKLOADS[args.config], args.cmd)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, WORKLOADS[args.config], args.cmd)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: the expert-parallel path across GPUs is designed, not built",
