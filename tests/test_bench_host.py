@@ -1,0 +1,75 @@
+"""Host logic of bench.py's profiler summaries, on synthetic rocprofv3 databases (no GPU).
+
+The summaries turn per-instance counter rows into per-launch figures: the
+grouped-GEMM kernels are told apart by their epilogue template argument (the
+forward's combine-fused second GEMM is not part of the expert-FFN stage), byte
+counters are scaled by what they read for a copy of known size, and the
+matrix-core counters are summed over the instances of each dispatch.
+"""
+import sqlite3
+
+import pytest
+
+import bench
+
+RING = "void moe::grouped_gemm_ring_kernel<256, 192, 3, 4, {epi}, true>(unsigned short const*, int)"
+PIPE = "void moe::grouped_gemm_pipe_kernel<256, 256, 64, 2, 2, {epi}, 8, true>(unsigned short const*, int)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _db(path, rows):
+    """rows: (dispatch_id, kernel name, counter, value, duration ns)."""
+    db = sqlite3.connect(path)
+    db.execute("create table pmc_events (dispatch_id integer, name text, counter_name text, counter_value real, "
+               "duration integer)")
+    db.executemany("insert into pmc_events values (?, ?, ?, ?, ?)", rows)
+    db.commit()
+    db.close()
+    return str(path)
+
+
+def test_gemm_epilogue_parsing():
+    assert bench._gemm_epilogue(RING.format(epi=4)) == 4
+    assert bench._gemm_epilogue(RING.format(epi=0)) == 0
+    assert bench._gemm_epilogue(PIPE.format(epi=2)) == 2
+    assert bench._gemm_epilogue("void moe::combine_kernel<true>(void const*)") is None
+    assert bench._stage_kernel(PIPE.format(epi=2)) and bench._stage_kernel(RING.format(epi=0))
+    assert not bench._stage_kernel(RING.format(epi=bench.EPI_COMBINE1))
+    assert not bench._stage_kernel("void moe::combine_kernel<true>(void const*)")
+
+
+def test_summarize_mfma_sums_instances_per_dispatch(tmp_path, capsys):
+    rows = []
+    # two launches of one kernel, 32 counter instances each; GRBM_GUI_ACTIVE per instance
+    for d in (1, 2):
+        for inst in range(32):
+            rows.append((d, RING.format(epi=0), "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0 * d, 5000))
+            rows.append((d, RING.format(epi=0), "SQ_VALU_MFMA_BUSY_CYCLES", 100.0, 5000))
+            rows.append((d, RING.format(epi=0), "GRBM_GUI_ACTIVE", 900.0 + inst, 5000))
+    rows.append((3, "moe::slot_scan_kernel(int*)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 7.0, 100))
+    bench.summarize_mfma(_db(tmp_path / "m.db", rows), "w", "cmd", cus=2)
+    out = capsys.readouterr().out
+    line = [l for l in out.splitlines() if l.startswith("kernel:")]
+    assert len(line) == 1  # only the grouped GEMM
+    f = dict(kv.split(": ") for kv in line[0].split("  ")[1:])
+    assert int(f["launches"]) == 2
+    assert float(f["mfma_flops_per_launch"]) == pytest.approx(1.5 * 32 * 1000 * 512, rel=1e-3)
+    # busy: 32 * 100 cycles over (largest GUI-active instance 931) x 2 CUs x 4 SIMDs
+    assert float(f["mfma_busy_frac"]) == pytest.approx(3200 / (931 * 2 * 4), rel=1e-3)
+    assert float(f["us_under_counters"]) == pytest.approx(5.0)
+
+
+def test_summarize_pmc_scales_by_the_copy(tmp_path, capsys):
+    kib = bench.COPY_BYTES / 1024
+    # FETCH_SIZE reads half of the copy's bytes (factor 2), WRITE_SIZE all of them (factor 1)
+    f_rows = [(1, COPY, "FETCH_SIZE", kib / 2, 10), (2, PIPE.format(epi=2), "FETCH_SIZE", 1000.0, 10),
+              (3, RING.format(epi=0), "FETCH_SIZE", 2000.0, 10), (4, RING.format(epi=4), "FETCH_SIZE", 5000.0, 10)]
+    w_rows = [(1, COPY, "WRITE_SIZE", kib, 10), (2, PIPE.format(epi=2), "WRITE_SIZE", 300.0, 10),
+              (3, RING.format(epi=0), "WRITE_SIZE", 100.0, 10), (4, RING.format(epi=4), "WRITE_SIZE", 100.0, 10)]
+    bench.summarize_pmc(_db(tmp_path / "f.db", f_rows), _db(tmp_path / "w.db", w_rows), "w", "cmd")
+    out = capsys.readouterr().out
+    total = [l for l in out.splitlines() if l.startswith("hbm_bytes_per_step_expert_stage:")]
+    # stage = GEMM1 + the stage's GEMM2 (epilogue 0); the fused launch (epilogue 4) is listed apart
+    want = (1000.0 * 2 + 300.0 + 2000.0 * 2 + 100.0) * 1024
+    assert float(total[0].split(":")[1]) == pytest.approx(want, rel=1e-4)
+    assert any(l.startswith("other_kernel:") and ", 4, true>" in l for l in out.splitlines())
