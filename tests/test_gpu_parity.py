@@ -203,6 +203,8 @@ def test_forward_full_size_sampled(gpu, name):
     dict(name="pipe128", T=2048, H=256, E=16, F=512, cf=1.0),
     dict(name="pipe256", T=4096, H=256, E=8, F=256, cf=0.5),
     dict(name="ring", T=16384, H=768, E=8, F=256, cf=0.5),
+    # the Switch workload itself (the benchmark's configuration)
+    dict(name="switch", T=16384, H=768, E=64, F=3072, cf=1.0),
 ])
 @pytest.mark.parametrize("residual", [False, True])
 def test_forward_top1_fused_equals_stages(gpu, shape, residual):
