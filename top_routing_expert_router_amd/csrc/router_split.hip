@@ -1084,7 +1084,9 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   if (err != hipSuccess) return err;
 
   const int je = (E + 63) / 64;
-  const dim3 cgrid((T + 3) / 4), rgrid(T < 256 ? T : 256);
+  // refine: one block per queued token, grid-strided; four blocks per CU keep
+  // enough tokens in flight when many are undecided (k = 8 of 256 experts)
+  const dim3 cgrid((T + 3) / 4), rgrid(T < 1024 ? T : 1024);
   const bool fused_tile = E <= 64;
 #define MOE_CR(J, K)                                                                                               \
   do {                                                                                                             \
