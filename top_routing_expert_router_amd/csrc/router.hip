@@ -317,26 +317,37 @@ __global__ void __launch_bounds__(64) router_select_kernel(const float* __restri
 }
 
 // Ranks and block histogram from a finished topk_idx (the split router writes
-// the choices itself; this is the rank part of the kernel above).
-template <int KMAX>
+// the choices itself): the rank part of the kernel above, with one wave per
+// (64-token block, choice r) since the choices are ranked independently.
 __global__ void __launch_bounds__(64) router_rank_kernel(const int32_t* __restrict__ topk_idx,
                                                          const float* __restrict__ topk_gate,
                                                          const float* __restrict__ second_u, int T, int E, int k,
                                                          int nbits, int nb, int32_t* __restrict__ dst_rank,
                                                          int32_t* __restrict__ hist) {
   extern __shared__ int s_cnt[];  // [E + 1]
-  const int t = blockIdx.x * 64 + threadIdx.x;
+  const int lane = threadIdx.x, blk = blockIdx.x, r = blockIdx.y;
+  const int t = blk * 64 + lane;
   const bool valid = t < T;
-  int ti[KMAX];
-  bool absent[KMAX];
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    ti[r] = (valid && r < k) ? topk_idx[(size_t)t * k + r] : 0;
-    absent[r] = false;
+  const bool absent = r == 1 && second_u && valid &&
+                      !second_choice_taken(second_u[t], topk_gate[(size_t)t * k], topk_gate[(size_t)t * k + 1]);
+  const int my_e = absent ? E : (valid ? topk_idx[(size_t)t * k + r] : 0);
+  for (int e = lane; e <= E; e += 64) s_cnt[e] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (my_e >> b) & 1;
+    const uint64_t mb = __ballot(bit);
+    same &= bit ? mb : ~mb;
   }
-  if (KMAX >= 2 && second_u && valid)
-    absent[1] = !second_choice_taken(second_u[t], topk_gate[(size_t)t * k], topk_gate[(size_t)t * k + 1]);
-  block_ranks<KMAX>(ti, absent, valid, k, E, nbits, nb, t, dst_rank, hist, s_cnt);
+  if (valid) {
+    const int rank = __popcll(same & lt_mask);
+    dst_rank[(size_t)t * k + r] = absent ? kAbsentChoice : rank;
+    if (rank == 0) s_cnt[my_e] = __popcll(same);
+  }
+  __syncthreads();
+  const int Q = k * nb;
+  for (int e = lane; e < E; e += 64) hist[(size_t)e * Q + r * nb + blk] = s_cnt[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -394,17 +405,9 @@ hipError_t launch_router_rank(const int32_t* topk_idx, const float* topk_gate, c
   if (T == 0) return hipSuccess;
   int nbits = 0;
   while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
-  dim3 grid(nb), block(64);
+  dim3 grid(nb, k), block(64);
   size_t shm = sizeof(int) * (size_t)(E + 1);
-#define MOE_RANK(KM)                                                                                          \
-  router_rank_kernel<KM><<<grid, block, shm, st>>>(topk_idx, topk_gate, second_u, T, E, k, nbits, nb, dst_rank, \
-                                                   hist)
-  if (k <= 1) MOE_RANK(1);
-  else if (k <= 2) MOE_RANK(2);
-  else if (k <= 4) MOE_RANK(4);
-  else if (k <= 8) MOE_RANK(8);
-  else MOE_RANK(16);
-#undef MOE_RANK
+  router_rank_kernel<<<grid, block, shm, st>>>(topk_idx, topk_gate, second_u, T, E, k, nbits, nb, dst_rank, hist);
   return hipGetLastError();
 }
 
