@@ -42,9 +42,10 @@ __global__ void __launch_bounds__(256) slot_scan_kernel(int32_t* __restrict__ hi
   }
 }
 
-// K2b: one wave per block of 64 tokens.  Every workgroup derives offsets (the
-// exclusive prefix sum of kept) in LDS; workgroup 0 also publishes offsets[0..E]
-// and n_dropped.  Then each lane resolves its token's k assignments.
+// K2b: one wave per (block of 64 tokens, choice r): the assignments are
+// resolved independently.  Every workgroup derives offsets (the exclusive
+// prefix sum of kept) in LDS; workgroup (0, 0) also publishes offsets[0..E] and
+// n_dropped.  Then each lane resolves its token's choice r.
 __global__ void __launch_bounds__(64) slot_finalize_kernel(const int32_t* __restrict__ base, int Q, int nb, int T,
                                                            int E, int k, int C, const int32_t* __restrict__ topk_idx,
                                                            const int32_t* __restrict__ kept,
@@ -73,28 +74,26 @@ __global__ void __launch_bounds__(64) slot_finalize_kernel(const int32_t* __rest
   const int R = __shfl(inc, 63, 64);
   if (lane == 0) s_off[E] = R;
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int e = lane; e <= E; e += 64) offsets[e] = s_off[e];
     if (lane == 0) *n_dropped = T * k - R;
   }
-  const int blk = blockIdx.x;
+  const int blk = blockIdx.x, r = blockIdx.y;
   const int t = blk * 64 + lane;
   if (t >= T) return;
-  for (int r = 0; r < k; ++r) {
-    const size_t i = (size_t)t * k + r;
-    if (dst_row[i] == kAbsentChoice) {
-      dst_row[i] = -1;
-      continue;
-    }
-    const int e = topk_idx[i];
-    const int slot = base[(size_t)e * Q + r * nb + blk] + dst_row[i];
-    const int d = s_off[e] + slot;
-    if (slot < C && d < rmax) {  // d < R <= rmax for any plan this kernel derives
-      dst_row[i] = d;
-      row_token[d] = t;
-    } else {
-      dst_row[i] = -1;
-    }
+  const size_t i = (size_t)t * k + r;
+  if (dst_row[i] == kAbsentChoice) {
+    dst_row[i] = -1;
+    return;
+  }
+  const int e = topk_idx[i];
+  const int slot = base[(size_t)e * Q + r * nb + blk] + dst_row[i];
+  const int d = s_off[e] + slot;
+  if (slot < C && d < rmax) {  // d < R <= rmax for any plan this kernel derives
+    dst_row[i] = d;
+    row_token[d] = t;
+  } else {
+    dst_row[i] = -1;
   }
 }
 
@@ -106,8 +105,8 @@ hipError_t launch_slot_scan(int32_t* hist, int Q, int E, int C, int32_t* demand,
 hipError_t launch_slot_finalize(const int32_t* base, int Q, int nb, int T, int E, int k, int C,
                                 const int32_t* topk_idx, const int32_t* kept, int32_t* dst_row, int32_t* row_token,
                                 int32_t* offsets, int32_t* n_dropped, int rmax, hipStream_t st) {
-  const int grid = nb > 0 ? nb : 1;
-  slot_finalize_kernel<<<dim3(grid), dim3(64), sizeof(int) * (size_t)(E + 1), st>>>(
+  const dim3 grid(nb > 0 ? nb : 1, k);
+  slot_finalize_kernel<<<grid, dim3(64), sizeof(int) * (size_t)(E + 1), st>>>(
       base, Q, nb, T, E, k, C, topk_idx, kept, dst_row, row_token, offsets, n_dropped, rmax);
   return hipGetLastError();
 }
