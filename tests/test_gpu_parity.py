@@ -38,7 +38,16 @@ def _gpu_route(r, gpu, x, wg, bias):
     return cfg, plan
 
 
+def _exact_path(r):
+    """The runs whose router computes every logit and gate as defined (fp32 activations, or H
+    not a multiple of 64): logits and gates are then bit-identical to the oracle's."""
+    return r.dtype == recipes.F32 or r.H % 64 != 0
+
+
 def _check_route(r, gplan, oplan):
+    if _exact_path(r):
+        _check_exact_route(r, gplan, oplan, f"run {r.name}")
+        return
     gl = U.host(gplan["logits"])
     nd = int((gl != oplan["logits"]).sum())
     _, rel = U.err_stats(gl.astype(np.float64), oplan["logits"].astype(np.float64))
@@ -551,47 +560,24 @@ def test_sigmoid_scoring_forward(gpu):
     U.assert_close(U.host(y), yref, True, "sigmoid forward")
 
 
-def _check_probs_plan(r, gplan, oplan, tol=2e-6):
-    """The kept sets must be the oracle's except for assignments whose oracle gate is within
-    `tol` (relative) of its expert's cut-off; whatever the GPU kept must be a valid "probs"
-    choice under the GPU's own gates; packing exact for what was kept."""
-    T, k = r.T, r.k
-    gi, gg, gd = (U.host(gplan[n]).reshape(T, k) for n in ("topk_idx", "topk_gate", "dst_row"))
-    assert np.array_equal(gi, oplan["topk_idx"])
-    for n in ("demand", "kept"):
-        assert np.array_equal(U.host(gplan[n]), oplan[n]), n
-    off = U.host(gplan["offsets"])
-    assert np.array_equal(off, oplan["offsets"])
-    rt = U.host(gplan["row_token"])
-    og, od = oplan["topk_gate"], oplan["dst_row"]
-    differing = 0
-    for e in range(r.E):
-        qs = [(rr * T + t, t, rr) for rr in range(k) for t in range(T) if gi[t, rr] == e]
-        gk = [(q, t, rr) for q, t, rr in qs if gd[t, rr] >= 0]
-        gdrop = [(q, t, rr) for q, t, rr in qs if gd[t, rr] < 0]
-        if gdrop and gk:  # valid under the GPU's own gates
-            lo = min((gg[t, rr], -q) for q, t, rr in gk)
-            hi = max((gg[t, rr], -q) for q, t, rr in gdrop)
-            assert lo > hi, (e, lo, hi)
-        rows = [gd[t, rr] for q, t, rr in sorted(gk)]
-        assert rows == list(range(off[e], off[e] + len(gk))), e
-        for q, t, rr in gk:
-            assert rt[gd[t, rr]] == t
-        okept = {(t, rr) for q, t, rr in qs if od[t, rr] >= 0}
-        diff = okept ^ {(t, rr) for q, t, rr in gk}
-        if diff:
-            cut = sorted((og[t, rr] for q, t, rr in qs), reverse=True)[int(oplan["kept"][e]) - 1]
-            for t, rr in diff:
-                assert abs(og[t, rr] - cut) <= tol * cut, (e, t, rr, og[t, rr], cut)
-            differing += len(diff)
-    print(f"[probs] run {r.name}: {differing} assignments differ from the oracle inside the gate tolerance",
-          flush=True)
-    gates_rel = np.abs(gg.astype(np.float64) - og) / np.maximum(og, 1e-30)
-    assert gates_rel.max() <= U.GATE_REL
+def _check_exact_route(r, gplan, oplan, what):
+    """Exact path (every logit and gate computed as defined): logits and gates bit-identical
+    to the oracle's, the plan bit-exact."""
+    gl = U.host(gplan["logits"])
+    assert np.array_equal(gl.view(np.uint32), oplan["logits"].view(np.uint32)), \
+        f"{what}: {int((gl != oplan['logits']).sum())} logits not bit-identical"
+    gg = U.host(gplan["topk_gate"]).reshape(oplan["topk_gate"].shape)
+    assert np.array_equal(gg.view(np.uint32), oplan["topk_gate"].view(np.uint32)), \
+        f"{what}: {int((gg != oplan['topk_gate']).sum())} gates not bit-identical"
+    U.assert_plan_equal(gplan, oplan, what)
+    print(f"[exact] {what}: logits, gates and plan bit-identical; R={oplan['R']} "
+          f"dropped={int(oplan['n_dropped'][0])}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["1", "2", "3a", "3b", "3c", "full-3c"])
+@pytest.mark.parametrize("name", ["1", "2", "3a", "3b", "3c", "full-3a", "full-3c", "full-2"])
 def test_probs_drop_policy(gpu, name):
+    """"probs" policy: the gate values decide which assignments are kept, so the plan must
+    equal the oracle's bit for bit, with gates bit-identical."""
     r = recipes.RUNS[name[5:]] if name.startswith("full-") else recipes.SMALL[name]
     x = recipes.gen_x(r)
     wg, bias = recipes.gen_router(r)
@@ -600,7 +586,7 @@ def test_probs_drop_policy(gpu, name):
     gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
     oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), drop_policy=oracle.DROP_PROBS)
     assert oplan["n_dropped"][0] > 0
-    _check_probs_plan(r, gplan, oplan)
+    _check_exact_route(r, gplan, oplan, f"probs run {r.name}")
 
 
 def test_probs_drop_policy_ties_and_dropless(gpu):
@@ -614,7 +600,7 @@ def test_probs_drop_policy_ties_and_dropless(gpu):
     cfg.drop_policy = 1
     gplan = _gpu_route_cfg(cfg, gpu, x, wg, bias)
     oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), drop_policy=oracle.DROP_PROBS)
-    U.assert_plan_equal(gplan, oplan, "probs ties")
+    _check_exact_route(r, gplan, oplan, "probs ties")
     rd = r.scaled(name="probs-dropless", dropless=1)
     cfg = B.MoEConfig.from_run(rd)
     cfg.drop_policy = 1
@@ -622,40 +608,72 @@ def test_probs_drop_policy_ties_and_dropless(gpu):
     U.assert_plan_equal(gplan, _oracle_route(rd, x, wg, bias), "probs dropless")
 
 
-def _second_u(r, x, wg, bias, seed):
-    """Seeded uniforms for GShard's second choice, moved out of the band where the fp32 gates
-    of the two sides (which may differ in the last bit) could decide differently."""
-    u = np.random.default_rng(seed).random(r.T).astype(np.float32)
-    g = _oracle_route(r, x, wg, bias)["topk_gate"].astype(np.float64)
-    s = g[:, 0] + g[:, 1]
-    near = np.abs(u * s - 2 * g[:, 1]) <= 1e-5 * s
-    u[near] = np.minimum(u[near] + 1e-3, 0.999).astype(np.float32)
-    return u
+def _second_u(r, seed):
+    """Seeded uniforms in [0, 1) for GShard's second choice, as drawn (no adjustment)."""
+    return np.random.default_rng(seed).random(r.T).astype(np.float32)
 
 
-@pytest.mark.parametrize("name", ["4", "3a-k2", "2-k2", "1-k2"])
-def test_gshard_random_second_choice(gpu, name):
-    base = {"4": recipes.SMALL["4"], "3a-k2": recipes.SMALL["3a"].scaled(name="3a-k2", k=2),
-            "2-k2": recipes.SMALL["2"].scaled(name="2-k2", k=2, gate_mode=recipes.SOFTMAX_TOPK_RENORM),
-            "1-k2": recipes.RUNS["1"].scaled(name="1-k2", k=2, T=500)}[name]
-    r = base
-    x = recipes.gen_x(r)
-    wg, bias = recipes.gen_router(r)
-    u = _second_u(r, x, wg, bias, 21)
+def _gpu_route_gshard(r, gpu, x, wg, bias, u):
+    import torch
+
     cfg = B.MoEConfig.from_run(r)
     cfg.second_policy = 1
     plan = B.alloc_plan(cfg, gpu, logits=True)
     plan["second_u"] = U.dev(u, gpu)
     ws = B.alloc_workspace(cfg, gpu)
-    import torch
-
     B.route(cfg, U.dev(x, gpu), U.dev(wg, gpu), U.dev(bias, gpu), plan, ws)
     torch.cuda.synchronize()
+    return plan
+
+
+_GSHARD = {
+    "4": lambda: recipes.SMALL["4"],
+    "3a-k2": lambda: recipes.SMALL["3a"].scaled(name="3a-k2", k=2),
+    "2-k2": lambda: recipes.SMALL["2"].scaled(name="2-k2", k=2, gate_mode=recipes.SOFTMAX_TOPK_RENORM),
+    "1-k2": lambda: recipes.RUNS["1"].scaled(name="1-k2", k=2, T=500),
+    # more than 64 experts (one token's experts span several lanes' registers)
+    "E96-k2": lambda: recipes.SMALL["5"].scaled(name="E96-k2", E=96, k=2, T=1000),
+    # few experts, H a multiple of 256 and fewer than 16384 tokens (32-token tiles of the split router)
+    "E12-k2-T4000": lambda: recipes.SMALL["3a"].scaled(name="E12-k2-T4000", k=2, T=4000, H=512),
+    # full-size Mixtral-like routing with capacity
+    "full-4-cap": lambda: recipes.RUNS["4"].scaled(name="full-4-cap", dropless=0, cf=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(_GSHARD))
+def test_gshard_random_second_choice(gpu, name):
+    r = _GSHARD[name]()
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    u = _second_u(r, 21)
+    plan = _gpu_route_gshard(r, gpu, x, wg, bias, u)
     oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), second_u=u)
     absent = int((oplan["dst_row"][:, 1] < 0).sum())
     print(f"[gshard] run {r.name}: {absent} of {r.T} second choices not taken", flush=True)
     assert 0 < absent < r.T
-    _check_route(r, plan, oplan)
+    _check_exact_route(r, plan, oplan, f"gshard run {r.name}")
+
+
+@pytest.mark.parametrize("name", ["3a-k2", "2-k2", "E96-k2"])
+def test_gshard_uniforms_on_the_threshold(gpu, name):
+    """Uniforms placed on GShard's threshold 2 g2 / (g1 + g2) computed from the oracle's gates
+    (the fp32 value nearest to it, and its two neighbours): the decision then rests on the
+    last bits of the gates, and the GPU must take the oracle's on every token."""
+    r = _GSHARD[name]()
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    og = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r))["topk_gate"].astype(np.float64)
+    thr = 2.0 * og[:, 1] / (og[:, 0] + og[:, 1])
+    u0 = thr.astype(np.float32)
+    shift = np.arange(r.T) % 3  # 0: nearest, 1: one ulp below, 2: one ulp above
+    u = np.where(shift == 1, np.nextafter(u0, np.float32(0)), np.where(shift == 2, np.nextafter(u0, np.float32(1)), u0))
+    u = np.minimum(u, np.float32(np.nextafter(np.float32(1), np.float32(0)))).astype(np.float32)
+    plan = _gpu_route_gshard(r, gpu, x, wg, bias, u)
+    oplan = oracle.route(x, r.dtype, wg, bias, r.k, r.gate_mode, _cap(r), second_u=u)
+    absent = (oplan["dst_row"][:, 1] < 0)
+    print(f"[gshard-threshold] run {r.name}: {int(absent.sum())} of {r.T} second choices not taken", flush=True)
+    assert 0 < absent.sum() < r.T
+    _check_exact_route(r, plan, oplan, f"gshard threshold run {r.name}")
 
 
 def test_gshard_random_second_choice_forward(gpu):
@@ -663,7 +681,7 @@ def test_gshard_random_second_choice_forward(gpu):
 
     r = recipes.SMALL["4"].scaled(name="gshard-fwd", dropless=0, cf=1.0)
     d = recipes.gen_all(r)
-    u = _second_u(r, d["x"], d["wg"], d["bias"], 5)
+    u = _second_u(r, 5)
     yref, oplan, _, _ = oracle.forward(d["x"], r.dtype, d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], r.k,
                                        r.gate_mode, r.act, _cap(r), second_u=u)
     cfg = B.MoEConfig.from_run(r)
@@ -678,7 +696,7 @@ def test_gshard_random_second_choice_forward(gpu):
     B.forward(cfg, U.dev(d["x"], gpu), U.dev(d["wg"], gpu), U.dev(d["bias"], gpu), U.dev(d["w1"], gpu),
               U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), None, y, plan, X, Y, ws)
     torch.cuda.synchronize()
-    _check_route(r, plan, oplan)
+    _check_exact_route(r, plan, oplan, "gshard forward")
     U.assert_close(U.host(y), yref, True, "gshard forward")
 
 

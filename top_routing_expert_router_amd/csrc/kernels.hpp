@@ -14,8 +14,10 @@ constexpr int kSigmoidFlag = 16;
 // choice not taken); the finalize steps turn it into -1.
 constexpr int32_t kAbsentChoice = INT32_MIN;
 
-hipError_t launch_router_logits(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
-                                int H, int E, bool vec_ok, hipStream_t st);
+// Logits in their defining order (binary64 sums over h ascending, rounded once
+// to fp32: the exact values), any shape.
+hipError_t launch_router_exact(const void* x, bool bf16, const float* Wg, const float* bias, float* logits, int T,
+                               int H, int E, bool vec_ok, hipStream_t st);
 // Split-bf16 router (bf16 x, H % 64 == 0, 16-byte aligned x): logits with a
 // certified radius, choices and gates per token, exact recomputation of the
 // undecided tokens.
@@ -35,7 +37,6 @@ int split_router_hs(int H);
 // partials of launch_router_losses.  *fused reports what was done (1: ranks,
 // 2: loss partials); the caller launches the rest.
 struct SplitEpilogue {
-  const float* second_u;
   int32_t* dst_rank;
   int32_t* hist;
   double* Ppart;
@@ -46,8 +47,10 @@ struct SplitEpilogue {
 hipError_t launch_router_split(const void* x, const float* Wg, const float* bias, float* logits, int T, int H, int E,
                                int k, int gate_mode, int32_t* topk_idx, float* topk_gate, const SplitScratch& sc,
                                const SplitEpilogue& ep, int* fused, hipStream_t st);
-hipError_t launch_router_rank(const int32_t* topk_idx, const float* topk_gate, const float* second_u, int T, int E,
-                              int k, int nb, int32_t* dst_rank, int32_t* hist, hipStream_t st);
+hipError_t launch_router_rank(const int32_t* topk_idx, int T, int E, int k, int nb, int32_t* dst_rank, int32_t* hist,
+                              hipStream_t st);
+// Choices, gates (binary64, rounded once), ranks and block histograms from
+// exact logits; second_u (k = 2, or null): GShard's random second choice.
 hipError_t launch_router_select(const float* logits, int T, int E, int k, int gate_mode, const float* second_u,
                                 int nb, int32_t* topk_idx, float* topk_gate, int32_t* dst_rank, int32_t* hist,
                                 hipStream_t st);

@@ -67,7 +67,7 @@ struct Layout {
 };
 
 // The split-bf16 router runs for bf16 activations with H a multiple of 64 and a
-// 16-byte aligned x; otherwise the binary64 router does.
+// 16-byte aligned x; otherwise the exact router does.
 bool split_router_shape(const moe_config* c) { return c->dtype == MOE_BF16 && c->H % 64 == 0; }
 
 Layout layout_of(const moe_config* c) {
@@ -199,7 +199,12 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
   const int gm = c->gate_mode | (c->score_fn == MOE_SCORE_SIGMOID ? moe::kSigmoidFlag : 0);
   hipError_t e;
   int fused = 0;  // work the split router's epilogue took over (1: ranks, 2: loss partials)
-  if (L.split && aligned16(x)) {
+  // Where gate values decide the plan (the "probs" policy under a limiting
+  // capacity, GShard's random second choice) every logit and gate is computed
+  // exactly as defined (exact path); elsewhere the split-bf16 router certifies
+  // the choices where its shape allows.
+  const bool gate_decides = c->second_policy == MOE_SECOND_RANDOM || (c->drop_policy == MOE_DROP_PROBS && C != INT32_MAX);
+  if (L.split && aligned16(x) && !gate_decides) {
     moe::SplitScratch sc;
     sc.wp = w + L.wp;
     sc.wsq = reinterpret_cast<double*>(w + L.wsq);
@@ -208,8 +213,7 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     sc.pairs = reinterpret_cast<int2*>(w + L.pairs);
     sc.utok = reinterpret_cast<int4*>(w + L.utok);
     sc.count = reinterpret_cast<int*>(w + L.count);
-    const moe::SplitEpilogue ep{su,
-                                plan->dst_row,
+    const moe::SplitEpilogue ep{plan->dst_row,
                                 hist,
                                 plan->losses ? reinterpret_cast<double*>(w + L.lp) : nullptr,
                                 reinterpret_cast<double*>(w + L.lz),
@@ -218,13 +222,13 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     if ((e = moe::launch_router_split(x, Wg, bias, logits, c->T, c->H, c->E, c->k, gm, plan->topk_idx,
                                       plan->topk_gate, sc, ep, &fused, st)) != hipSuccess)
       return hip_fail(e, "router_split");
-    if (!(fused & 1) && (e = moe::launch_router_rank(plan->topk_idx, plan->topk_gate, su, c->T, c->E, c->k, L.nb,
-                                                     plan->dst_row, hist, st)) != hipSuccess)
+    if (!(fused & 1) &&
+        (e = moe::launch_router_rank(plan->topk_idx, c->T, c->E, c->k, L.nb, plan->dst_row, hist, st)) != hipSuccess)
       return hip_fail(e, "router_rank");
   } else {
-    if ((e = moe::launch_router_logits(x, bf16, Wg, bias, logits, c->T, c->H, c->E, c->H % 8 == 0 && aligned16(x),
-                                       st)) != hipSuccess)
-      return hip_fail(e, "router_logits");
+    if ((e = moe::launch_router_exact(x, bf16, Wg, bias, logits, c->T, c->H, c->E, aligned16(x) && c->H % 4 == 0, st)) !=
+        hipSuccess)
+      return hip_fail(e, "router_exact");
     if ((e = moe::launch_router_select(logits, c->T, c->E, c->k, gm, su, L.nb, plan->topk_idx,
                                        plan->topk_gate, plan->dst_row, hist, st)) != hipSuccess)
       return hip_fail(e, "router_select");

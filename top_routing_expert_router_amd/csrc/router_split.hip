@@ -353,10 +353,9 @@ __device__ __forceinline__ float xnorm_bound(float sq, int H) {
 // is a whole number of 64-token blocks: the ranks and per-block expert counts
 // (dst_rank non-null) and the per-block loss partials (Ppart non-null).
 struct SplitTail {
-  const float* second_u;  // GShard second-choice draws (k = 2), or null
   int32_t* dst_rank;      // [T][k] rank among the block's tokens with the same choice
   int32_t* hist;          // [E][k][nb] choices per expert, choice and block
-  int nbits, nb;          // bits of an expert id 0..E; 64-token blocks
+  int nbits, nb;          // bits of an expert id 0..E-1; 64-token blocks
   double* Ppart;          // [E][nb] sum over the block of P(e | t)
   double* Zpart;          // [nb] sum over the block of logsumexp^2
   int32_t* Cpart;         // [E][nb] first choices per expert
@@ -770,37 +769,29 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
       constexpr int RB = BM / 64 > 0 ? BM / 64 : 1;  // 64-token blocks of this workgroup
       const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
       if (tail.dst_rank && w < RB && (blockIdx.x * RB + w) * 64 < T) {
-        // ranks: position among the block's earlier tokens with the same choice
-        // (expert E marks an absent GShard second choice); counts per expert
+        // ranks: position among the block's earlier tokens with the same choice;
+        // counts per expert
         const int b = blockIdx.x * RB + w, tr = b * 64 + lane;
         const bool valid = tr < T;
         const int Q = k * tail.nb;
         const uint64_t vmask = __ballot(valid);
         int ti[KMAX];
-        bool absent[KMAX];
 #pragma unroll
-        for (int r = 0; r < KMAX; ++r) {
-          ti[r] = (valid && r < k) ? s_idx[(w * 64 + lane) * k + r] : 0;
-          absent[r] = false;
-        }
-        if (KMAX >= 2 && tail.second_u && valid)
-          absent[1] = !second_choice_taken(tail.second_u[tr], s_gt[(w * 64 + lane) * k],
-                                           s_gt[(w * 64 + lane) * k + 1]);
-        int* cnt_e = s_rc + w * 65;  // this wave's counts, expert E: absent
+        for (int r = 0; r < KMAX; ++r) ti[r] = (valid && r < k) ? s_idx[(w * 64 + lane) * k + r] : 0;
+        int* cnt_e = s_rc + w * 65;  // this wave's counts
 #pragma unroll
         for (int r = 0; r < KMAX; ++r) {
           if (r >= k) break;
-          const int my_e = absent[r] ? E : ti[r];
+          const int my_e = ti[r];
           uint64_t same = vmask;
           for (int bit = 0; bit < tail.nbits; ++bit) {
             const uint64_t mb = __ballot((my_e >> bit) & 1);
             same &= ((my_e >> bit) & 1) ? mb : ~mb;
           }
-          if (valid) tail.dst_rank[(size_t)tr * k + r] = absent[r] ? kAbsentChoice : __popcll(same & lt);
+          if (valid) tail.dst_rank[(size_t)tr * k + r] = __popcll(same & lt);
           // the first lane of each choice group writes the group's size (the
           // wave's LDS operations complete in order)
           cnt_e[lane] = 0;
-          if (lane == 0) cnt_e[64] = 0;
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
           __builtin_amdgcn_wave_barrier();
           if (valid && (same & lt) == 0) cnt_e[my_e] = __popcll(same);
@@ -1063,9 +1054,8 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   // 4 H 2^-53 relative to sum|x*w|.
   const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
   int nbits = 0;
-  while ((1 << nbits) < E + 1) ++nbits;  // expert ids 0 .. E (E: an absent choice)
-  const SplitTail tail{ep.second_u, ep.dst_rank, ep.hist,  nbits,      (T + 63) / 64,
-                       ep.Ppart,    ep.Zpart,    ep.Cpart, ep.score_fn};
+  while ((1 << nbits) < E) ++nbits;  // expert ids 0 .. E-1
+  const SplitTail tail{ep.dst_rank, ep.hist, nbits, (T + 63) / 64, ep.Ppart, ep.Zpart, ep.Cpart, ep.score_fn};
   SplitArgs a{xb, wp, Wg, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
 
   if (E <= 16) {
