@@ -2,8 +2,10 @@
 
 One step = one moe_forward (route -> slot assignment -> dispatch -> expert FFN ->
 combine) over one batch of seeded synthetic tokens already resident in HBM.
-Default workload: the Switch-style top-1 layer (T=16384, H=768, E=64, k=1,
-F=3072, GELU, cf=1.0 with drop, bf16 activations/weights, fp32 router).
+Default workload: the DeepSeek-R1-shaped routed experts on one GPU holding all
+of them (T=4096, H=7168, E=256, k=8, SwiGLU 7168->2048->7168, dropless,
+softmax then top-8 renormalised, router bias N(0,1), bf16 activations and
+weights, fp32 router): the largest workload that fits one GPU.
 
 Prints one JSON line: the layer's tokens/s, per-stage times, the roofline of
 the expert FFN (algorithmic bytes over its launch time against 8 TB/s, with
@@ -210,7 +212,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="2", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="5", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true",
@@ -266,14 +268,10 @@ def main():
     t0 = time.time()
     x_h = recipes.gen_x(run)
     wg_h, bias_h = recipes.gen_router(run)
-    keep_host = run.E * run.m * run.H * run.F * eb <= (4 << 30)  # host copies for the CPU baseline
-    host_w = {}
-
     def upload(which):
         out_f, in_f = (run.F, run.H) if which in ("w1", "w3") else (run.H, run.F)
         w = torch.empty((run.E, out_f, in_f), dtype=tdt, device=dev)
         per = max(1, (1 << 26) // (out_f * in_f))
-        parts = []
         for e0 in range(0, run.E, per):
             es = list(range(e0, min(run.E, e0 + per)))
             p = recipes.gen_expert_weight(run, which, experts=es)
@@ -281,10 +279,6 @@ def main():
             hb = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16) if blk.dtype == np.uint16 \
                 else torch.from_numpy(blk)
             w[e0:e0 + len(es)].copy_(hb)
-            if keep_host:
-                parts.append(blk)
-        if keep_host:
-            host_w[which] = np.concatenate(parts)
         return w
 
     x = up(x_h)
@@ -396,31 +390,43 @@ def main():
     # Extra measurements (cold stages, training terms, routing variants, shared
     # expert) are skipped with --core-only, which the profiler runs use so that
     # every launch they record belongs to the routed layer.
-    stage_cold_us, losses_us, variants, shared_out = None, None, None, None
+    stage_cold_us, losses_us, variants, shared_out, cold_sets = None, None, None, None, None
     if not args.core_only:
-        # cold: before each call a copy kernel writes 512 MiB (more than the 256 MB
-        # Infinity Cache), so the stage's inputs come from HBM; median of 10 calls
-        flush_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-        flush_dst = torch.empty_like(flush_src)
-
-        def timed_cold(fn, n=10):
+        # cold: the stage runs back to back over rotating copies of its buffers, as many
+        # sets as make 1 GiB of traffic per rotation (four times the 256 MB Infinity
+        # Cache), so every call reads inputs that have left every cache while the GPU
+        # stays busy (no idle-launch gap in the timed region)
+        def timed_rotating(make_set, call, bytes_per_call):
+            nsets = max(2, -(-(1 << 30) // max(int(bytes_per_call), 1)))
+            sets = [make_set() for _ in range(nsets)]
+            torch.cuda.synchronize()
+            for st in sets:  # touch every set once
+                call(*st)
+            reps = max(2, args.steps // nsets + 1)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ts = []
-            for _ in range(n):
-                flush_dst.copy_(flush_src)
-                e0.record()
-                fn()
-                e1.record()
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            return sorted(ts)[n // 2]
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                for st in sets:
+                    call(*st)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / (reps * nsets) * 1e3
+            del sets
+            return us, nsets
 
-        stage_cold_us = {
-            "route": timed_cold(lambda: B.route(cfg, x, wg, bias, plan, ws)),
-            "dispatch": timed_cold(lambda: B.dispatch(cfg, x, plan, X)),
-            "combine": timed_cold(lambda: B.combine(cfg, Y, plan, x, y)),
-        }
-        del flush_src, flush_dst
+        kept_now = plan["kept"].cpu().numpy()
+        R_now = int(kept_now.sum())
+        xb = run.T * run.H * eb
+        cold_disp, ns_d = timed_rotating(lambda: (x.clone(), torch.empty_like(X)),
+                                         lambda xs, Xs: B.dispatch(cfg, xs, plan, Xs), xb + R_now * run.H * eb)
+        cold_comb, ns_c = timed_rotating(lambda: (Y.clone(), x.clone(), torch.empty_like(y)),
+                                         lambda Ys, rs, ys: B.combine(cfg, Ys, plan, rs, ys),
+                                         R_now * run.H * eb + 2 * xb)
+        cold_route, ns_r = timed_rotating(lambda: (x.clone(),), lambda xs: B.route(cfg, xs, wg, bias, plan, ws),
+                                          xb)
+        stage_cold_us = {"route": cold_route, "dispatch": cold_disp, "combine": cold_comb}
+        cold_sets = {"route": ns_r, "dispatch": ns_d, "combine": ns_c}
 
         # ---- router training terms (load-balancing loss, z-loss): route with the
         # optional losses output, against route without it
@@ -532,13 +538,14 @@ def main():
         stages_cold = {n: {"us": round(v, 2), "GB_s": round(gbs(cold_bytes[n], v), 1),
                            "hbm_frac": round(gbs(cold_bytes[n], v) / PEAK_HBM_GBS, 4)}
                        for n, v in stage_cold_us.items()}
-        stages_cold["note"] = ("one call after a 512 MiB copy (inputs out of every cache), median of 10; includes "
-                               "the launch latency of an idle GPU")
+        stages_cold["note"] = ("back-to-back calls rotating over copies of the stage's buffers, "
+                               f"{cold_sets} sets per rotation (>= 1 GiB of traffic, 4x the 256 MB Infinity "
+                               "Cache): inputs come from HBM, no idle gaps")
 
     # ---- CPU baseline: the oracle on the machine's host cores, bounded sample
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(run, x_h, wg_h, bias_h, host_w, args.cpu_seconds) if keep_host else None
+        cpu = cpu_baseline(run, x_h, wg_h, bias_h, args.cpu_seconds)
 
     value = T / (ms_per_step * 1e-3)
     out = {
@@ -576,33 +583,50 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(run, x_h, wg_h, bias_h, host_w, target_s):
-    """Oracle tokens/s: routing over the whole batch (capacity needs every token),
-    the expert FFN + combine on a sample of tokens, scaled to the batch."""
+def cpu_baseline(run, x_h, wg_h, bias_h, target_s):
+    """Oracle tokens/s on the host cores: routing of the whole batch (capacity needs every
+    token), the expert FFN of every row of a seeded sample of experts (only their weights
+    are generated on the host), scaled to all kept rows, and the combine of every token."""
     import numpy as np
 
     import oracle
+    from top_routing_expert_router_amd.synth import recipes
 
     C = None if run.dropless else oracle.capacity(run.T, run.k, run.E, run.cf, run.min_capacity)
     t0 = time.perf_counter()
     plan = oracle.route(x_h, run.dtype, wg_h, bias_h, run.k, run.gate_mode, C)
     t_route = time.perf_counter() - t0
-    n = 64
-    rng = np.random.default_rng(0)
-    while True:
-        toks = np.sort(rng.choice(run.T, size=min(n, run.T), replace=False))
-        t1 = time.perf_counter()
-        oracle.token_outputs(toks, x_h, run.dtype, run.act, plan, host_w["w1"], host_w.get("w3"), host_w["w2"],
-                             residual=x_h)
-        t_s = time.perf_counter() - t1
-        if t_s >= 0.3 * target_s or n >= run.T:
-            break
-        n = min(run.T, int(n * max(2.0, 0.5 * target_s / max(t_s, 1e-3))))
-    per_tok = t_route / run.T + t_s / len(toks)
+    off, R = plan["offsets"], plan["R"]
+    rows_of = np.diff(off)
+    order = np.random.default_rng(run.run_id).permutation(np.nonzero(rows_of > 0)[0])
+    # about target_s of FFN work at a first guess of 4 GFLOP/s per thread, at least one expert
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": round(1.0 / per_tok, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"routing of all {run.T} tokens ({t_route:.2f}s) + expert FFN and combine of {len(toks)} "
-                      f"sampled tokens ({t_s:.2f}s), fp64 C oracle with OpenMP"}
+    flop_row = 2.0 * run.H * run.F * run.m
+    budget = max(1, int(target_s * 4e9 * threads / flop_row))
+    chosen, m = [], 0
+    for e in order:
+        if chosen and m + rows_of[e] > budget:
+            break
+        chosen.append(int(e))
+        m += int(rows_of[e])
+    Y = np.zeros((max(R, 1), run.H), np.float64)
+    ws = {n: recipes.gen_expert_weight(run, n, experts=chosen) for n in (("w1", "w3", "w2") if run.m == 3 else
+                                                                          ("w1", "w2"))}
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in chosen])
+    ex = np.concatenate([np.full(rows_of[e], i, np.int32) for i, e in enumerate(chosen)])
+    xin = x_h[plan["row_token"][rows]]
+    cw = {n: np.stack([ws[n][e] for e in chosen]) for n in ws}
+    t1 = time.perf_counter()
+    Y[rows] = oracle.expert_rows(xin, ex, run.dtype, run.act, cw["w1"], cw.get("w3"), cw["w2"])
+    t_ffn = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    oracle.combine(Y[:max(R, 1)], plan, run.dtype, residual=x_h)
+    t_comb = time.perf_counter() - t2
+    total = t_route + t_ffn * (R / max(m, 1)) + t_comb
+    return {"value": round(run.T / total, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"routing of all {run.T} tokens ({t_route:.2f}s); expert FFN of all {m} rows of {len(chosen)} "
+                      f"seeded-random non-empty experts ({t_ffn:.2f}s), scaled to the {R} kept rows; combine of all "
+                      f"{run.T} tokens ({t_comb:.2f}s); binary64 C oracle with OpenMP"}
 
 
 if __name__ == "__main__":

@@ -104,3 +104,56 @@ def upload_expert_weight(run, which, device, keep=()):
             if e in keep:
                 kept[e] = part[e]
     return w, kept
+
+
+def tile_boundary_tokens(oplan, T, seed, tile=128, extra=256):
+    """Tokens whose packed rows are the first and last row of every `tile`-row m-tile of
+    every non-empty expert (so each non-empty expert and each tile edge of the 128- and
+    256-row grouped-GEMM tiles is covered), plus `extra` random tokens, 0 and T-1."""
+    off, rt = oplan["offsets"], oplan["row_token"]
+    rows = set()
+    for e in range(off.size - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        for m0 in range(lo, hi, tile):
+            rows.add(m0)
+            rows.add(min(m0 + tile - 1, hi - 1))
+    toks = {int(rt[r]) for r in rows} | {0, T - 1}
+    rng = np.random.default_rng(seed)
+    toks |= set(rng.choice(T, size=min(extra, T), replace=False).tolist())
+    return np.array(sorted(toks), np.int64)
+
+
+def upload_weights_with_reference(run, device, x, oplan, toks, chunk=16):
+    """Uploads every expert weight (generated `chunk` experts at a time) and, chunk by
+    chunk, has the oracle compute the expert outputs of the kept assignments of the
+    sampled tokens `toks` whose expert is in the chunk.  Returns the device weights
+    (w1, w3, w2) and the oracle's output rows of those tokens (combine of the per-row
+    expert outputs, binary64)."""
+    import torch
+
+    import oracle
+
+    tdt = torch.bfloat16 if run.dtype == recipes.BF16 else torch.float32
+    gated = run.act == recipes.SWIGLU
+    w = {n: torch.empty((run.E,) + ((run.F, run.H) if n != "w2" else (run.H, run.F)), dtype=tdt, device=device)
+         for n in (("w1", "w3", "w2") if gated else ("w1", "w2"))}
+    sub_idx = oplan["topk_idx"][toks]
+    sub_dst = oplan["dst_row"][toks]
+    pair_of = np.full(sub_dst.shape, -1, np.int32)  # row of Ysub for each kept (token, choice)
+    kept = np.argwhere(sub_dst >= 0)
+    pair_of[kept[:, 0], kept[:, 1]] = np.arange(len(kept), dtype=np.int32)
+    Ysub = np.zeros((max(len(kept), 1), run.H), np.float64)
+    for e0 in range(0, run.E, chunk):
+        es = list(range(e0, min(run.E, e0 + chunk)))
+        parts = {n: recipes.gen_expert_weight(run, n, experts=es) for n in w}
+        for n, part in parts.items():
+            w[n][e0:e0 + len(es)].copy_(dev(np.stack([part[e] for e in es]), "cpu"))
+        sel = [j for j, (i, c) in enumerate(kept) if e0 <= sub_idx[i, c] < e0 + len(es)]
+        if sel:
+            rows = np.stack([x[toks[kept[j][0]]] for j in sel])
+            ex = np.array([sub_idx[kept[j][0], kept[j][1]] - e0 for j in sel], np.int32)
+            cw = {n: np.stack([parts[n][e] for e in es]) for n in parts}
+            Ysub[sel] = oracle.expert_rows(rows, ex, run.dtype, run.act, cw["w1"], cw.get("w3"), cw["w2"])
+    sub = {"topk_idx": sub_idx, "topk_gate": oplan["topk_gate"][toks], "dst_row": pair_of}
+    yref = oracle.combine(Ysub, sub, run.dtype)
+    return (w["w1"], w.get("w3"), w["w2"]), yref

@@ -73,3 +73,17 @@ def test_summarize_pmc_scales_by_the_copy(tmp_path, capsys):
     want = (1000.0 * 2 + 300.0 + 2000.0 * 2 + 100.0) * 1024
     assert float(total[0].split(":")[1]) == pytest.approx(want, rel=1e-4)
     assert any(l.startswith("other_kernel:") and ", 4, true>" in l for l in out.splitlines())
+
+
+def test_cpu_baseline_samples_whole_experts():
+    """The CPU baseline routes every token, runs the oracle's FFN on every row of a sample of
+    experts (generating only their weights) and scales to all kept rows."""
+    from top_routing_expert_router_amd.synth import recipes
+
+    r = recipes.SMALL["5"]
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    out = bench.cpu_baseline(r, x, wg, bias, 0.05)
+    assert out["kind"] == "oracle" and out["unit"] == "tokens/s" and out["cores"] >= 1
+    assert out["value"] > 0
+    assert f"routing of all {r.T} tokens" in out["sample"] and "seeded-random non-empty experts" in out["sample"]
