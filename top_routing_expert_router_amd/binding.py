@@ -18,7 +18,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ("moe_validate", "moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_status_str",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_shared_expert", "moe_combine_shared", "moe_forward_shared")
+           "moe_shared_expert", "moe_combine_shared", "moe_forward_shared", "moe_route_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -100,6 +100,8 @@ def lib():
         L.moe_last_error.argtypes = []
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [cfgp, vp, vp, vp, planp, vp, sz, vp]
+        L.moe_route_noalloc.restype = ctypes.c_int
+        L.moe_route_noalloc.argtypes = [cfgp, vp, vp, vp, planp, vp]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [cfgp, vp, planp, vp, vp]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -196,6 +198,14 @@ def route(cfg, x, wg, bias, plan, ws, stream=None):
     st = lib().moe_route(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(bias), ctypes.byref(p), _ptr(ws),
                          ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "moe_route")
+
+
+def route_noalloc(cfg, x, wg, bias, plan, stream=None):
+    """moe_route on the library's static scratch (no workspace argument, nothing allocated)."""
+    c, p = cfg.c(), _plan_struct(plan)
+    st = lib().moe_route_noalloc(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(bias), ctypes.byref(p), _stream(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_route_noalloc", lib().moe_last_error().decode())
 
 
 def dispatch(cfg, x, plan, X, stream=None):

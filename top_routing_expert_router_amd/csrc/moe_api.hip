@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 #include "moe.h"
 
@@ -126,6 +128,37 @@ moe_status check_plan(const moe_config* c, const moe_plan* p) {
   return MOE_OK;
 }
 
+// Argument checks shared by the two route entry points (workspace checked apart).
+moe_status check_route_args(const moe_config* c, const void* x, const float* Wg, const moe_plan* plan);
+moe_status route_body(const moe_config* c, const void* x, const float* Wg, const float* bias, const moe_plan* plan,
+                      void* ws, void* stream);
+
+// Route scratch of moe_route_noalloc: one array per device (each GPU that runs
+// the library holds its own copy until the process ends), shared by every call
+// on that device.  Host code uses only the device address taken from the symbol
+// (per device, once), never the array's name.
+constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,14 +215,49 @@ const char* moe_last_error(void) { return g_last_error; }
 
 moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const float* bias, const moe_plan* plan,
                      void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = check_route_args(c, x, Wg, plan);
+  if (s != MOE_OK) return s;
+  if (!ws || ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
+  return route_body(c, x, Wg, bias, plan, ws, stream);
+}
+
+moe_status moe_route_noalloc(const moe_config* c, const void* x, const float* Wg, const float* bias,
+                             const moe_plan* plan, void* stream) {
+  moe_status s = check_route_args(c, x, Wg, plan);
+  if (s != MOE_OK) return s;
+  const size_t need = layout_of(c).route_end;
+  if (need > kStaticScratchBytes) {
+    snprintf(g_last_error, sizeof g_last_error,
+             "moe_route_noalloc: this configuration needs %zu bytes of route scratch, more than the %zu of the "
+             "static scratch",
+             need, kStaticScratchBytes);
+    return MOE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_noalloc: static scratch address");
+  return route_body(c, x, Wg, bias, plan, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status check_route_args(const moe_config* c, const void* x, const float* Wg, const moe_plan* plan) {
   moe_status s = moe_validate(c);
   if (s != MOE_OK) return s;
   if ((s = check_plan(c, plan)) != MOE_OK) return s;
   if ((c->T > 0 && !x) || !Wg) return MOE_ERR_INVALID_ARG;
   if (c->second_policy == MOE_SECOND_RANDOM && c->T > 0 && !plan->second_u) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// Route into the workspace `ws` (at least layout_of(c).route_end bytes; checked by
+// the caller together with the arguments).
+moe_status route_body(const moe_config* c, const void* x, const float* Wg, const float* bias, const moe_plan* plan,
+                      void* ws, void* stream) {
   const float* su = c->second_policy == MOE_SECOND_RANDOM ? plan->second_u : nullptr;
   const Layout L = layout_of(c);
-  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(w + L.hist);
@@ -255,6 +323,10 @@ moe_status moe_route(const moe_config* c, const void* x, const float* Wg, const 
     return hip_fail(e, "router_losses");
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 moe_status moe_dispatch(const moe_config* c, const void* x, const moe_plan* plan, void* X, void* stream) {
   moe_status s = moe_validate(c);
