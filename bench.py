@@ -70,6 +70,9 @@ def read_traffic(workload):
         return None
 
 
+# workloads measured briefly next to the main one (layer time and expert-FFN roofline)
+EXTRA_WORKLOADS = ("2", "4")
+
 EXPERT_KERNEL = "grouped_gemm"
 EPI_COMBINE1 = 4  # epilogue argument of the second GEMM that also does the top-1 combine
 COPY_BYTES = 256 << 20
@@ -217,6 +220,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the layer captured in a HIP graph instead of eager moe_forward calls")
+    ap.add_argument("--no-extra", action="store_true", help="skip the brief runs of the other workloads")
     ap.add_argument("--core-only", action="store_true",
                     help="skip the extra measurements (for profiler runs: only the routed layer's launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -580,7 +584,77 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if not args.core_only and not args.no_extra:
+        out["extra_workloads"] = {n: extra_workload(n, 20, 10) for n in EXTRA_WORKLOADS if n != args.config}
+        log("[bench] extra workloads: " + ", ".join(f"{n}={v['ms_per_step']:.3f} ms" for n, v in
+                                                     out["extra_workloads"].items()))
     print(json.dumps(out), flush=True)
+
+
+def extra_workload(name, steps, warmup):
+    """The same whole-layer measurement, briefer, on another workload: layer time, tokens/s,
+    the expert-FFN stage (two launches) and its roofline fraction."""
+    import numpy as np
+    import torch
+
+    from top_routing_expert_router_amd import binding as B
+    from top_routing_expert_router_amd.synth import recipes
+
+    run = recipes.RUNS[name]
+    dev = torch.device("cuda:0")
+    cfg = B.MoEConfig.from_run(run)
+    bf16 = run.dtype == recipes.BF16
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    eb = run.elem_bytes
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x = up(recipes.gen_x(run))
+    wg, bias = (up(t) for t in recipes.gen_router(run))
+    ws_ = {n: up(recipes.gen_expert_weight(run, n)) if (n != "w3" or run.act == recipes.SWIGLU) else None
+           for n in ("w1", "w3", "w2")}
+    plan = B.alloc_plan(cfg, dev)
+    rmax = B.max_rows(cfg)
+    X = torch.empty((max(rmax, 1), run.H), dtype=tdt, device=dev)
+    Y = torch.empty_like(X)
+    y = torch.empty((run.T, run.H), dtype=tdt, device=dev)
+    ws = B.alloc_workspace(cfg, dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    layer_us = timed(lambda: B.forward(cfg, x, wg, bias, ws_["w1"], ws_["w3"], ws_["w2"], x, y, plan, X, Y, ws))
+    B.dispatch(cfg, x, plan, X)  # the forward reads x through row_token and leaves X unwritten
+    ffn_us = timed(lambda: B.expert_ffn(cfg, X, plan, ws_["w1"], ws_["w3"], ws_["w2"], Y, ws))
+    kept = plan["kept"].cpu().numpy()
+    R = int(kept.sum())
+    flops = 2.0 * R * run.H * run.F * run.m
+    byts = int((kept > 0).sum()) * run.m * run.H * run.F * eb + 2.0 * R * run.H * eb
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    t_mfma, t_hbm = flops / (peak * 1e12) * 1e6, byts / (PEAK_HBM_GBS * 1e9) * 1e6
+    out = {"workload": WORKLOADS[name], "ms_per_step": round(layer_us / 1e3, 5),
+           "tokens_per_s": round(run.T / (layer_us * 1e-6), 1), "expert_ffn_us": round(ffn_us, 2),
+           "expert_ffn_tflops": round(flops / (ffn_us * 1e-6) / 1e12, 1),
+           "expert_ffn_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                                   "frac": round(max(t_mfma, t_hbm) / ffn_us, 4)}}
+    del ws_, X, Y, y, ws, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(run, x_h, wg_h, bias_h, target_s):

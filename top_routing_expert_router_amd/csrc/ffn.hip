@@ -989,8 +989,8 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   if (tiles <= 0) return hipSuccess;
   const int grid = (int)(tiles < cus ? tiles : cus);
   const size_t shm = sizeof(uint16_t) * ((size_t)2 * BM + (size_t)SW * WR) * 64 + sizeof(int) * 2 * (size_t)(E + 1);
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  constexpr int kMaxShm = sizeof(uint16_t) * (2 * BM + SW * WR) * 64 + sizeof(int) * 2 * (1024 + 1);  // E <= 1024
+  hipError_t err = lds_limit_once<grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW>>(kMaxShm);
   if (err != hipSuccess) return err;
   grouped_gemm_ring_kernel<BM, WR, SW, WGM, EPI, NTW><<<dim3(grid), dim3(512), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
@@ -1009,8 +1009,8 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   const int64_t slots = (int64_t)cus * (8 / NW);  // resident workgroups
   const int grid = (int)(tiles < slots ? tiles : slots);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  constexpr int kMaxShm = sizeof(uint16_t) * S * (BM + WR) * BK + sizeof(int) * 2 * (1024 + 1);  // E <= 1024
+  hipError_t err = lds_limit_once<grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW>>(kMaxShm);
   if (err != hipSuccess) return err;
   grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
@@ -1026,8 +1026,7 @@ static hipError_t launch_bf16(const void* A, const void* B, const void* B2, void
   const int64_t grid = mtiles * ntn;
   if (grid <= 0) return hipSuccess;
   const size_t shm = sizeof(uint16_t) * (size_t)GB_TILE * 2 * (1 + (EPI == EPI_SWIGLU ? 2 : 1));
-  hipError_t err = hipFuncSetAttribute((const void*)grouped_gemm_bf16_kernel<EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  hipError_t err = lds_limit_once<grouped_gemm_bf16_kernel<EPI>>((int)shm);
   if (err != hipSuccess) return err;
   grouped_gemm_bf16_kernel<EPI><<<dim3((unsigned)grid), dim3(256), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
@@ -1052,10 +1051,9 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
                              hipStream_t st, const int32_t* gather = nullptr, int xrows = 0,
                              const Combine1& cmb = Combine1{}) {
   if (vec && bf16 && K % 64 == 0) {
-    int dev = 0, cus = 0;
-    hipError_t err = hipGetDevice(&dev);
+    int cus = 0;
+    hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
     // Experts with more than 128 rows on average take 256-row tiles: 256 x 256
     // (two stages of 512 rows), or, where 192 weight rows per tile fill the
     // CUs more evenly in whole waves of tiles, 256 x 192 with split rings (two
@@ -1089,6 +1087,21 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
+}
+
+hipError_t device_cus(int* cus) {
+  static int cached[kMaxDevices] = {};  // 0: not queried yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_ACQUIRE);
+  if (v == 0) {
+    if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELEASE);
+  }
+  *cus = v;
+  return hipSuccess;
 }
 
 bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 64 == 0; }

@@ -6,6 +6,28 @@
 
 namespace moe {
 
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int* cus);
+
+// Raises kernel Kern's dynamic LDS limit to `bytes` (the most any of its
+// launches uses) once per device; the attribute persists for the process, so
+// launches carry no attribute call.
+constexpr int kMaxDevices = 64;
+template <auto Kern>
+hipError_t lds_limit_once(int bytes) {
+  static unsigned long long done = 0;  // bit d: set on device d
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (__atomic_load_n(&done, __ATOMIC_ACQUIRE) >> dev & 1ull) return hipSuccess;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               bytes)) != hipSuccess)
+    return e;
+  __atomic_fetch_or(&done, 1ull << dev, __ATOMIC_ACQ_REL);
+  return hipSuccess;
+}
+
 // Added to a moe_gate_mode passed to the router launchers: sigmoid scores
 // instead of softmax (the choices are the same; the gates differ).
 constexpr int kSigmoidFlag = 16;

@@ -140,15 +140,14 @@ moe_status route_body(const moe_config* c, const void* x, const float* Wg, const
 constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
 __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
+void* g_scratch_ptr[moe::kMaxDevices] = {};
 
 hipError_t static_scratch(void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= moe::kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;

@@ -1011,7 +1011,7 @@ static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   if (red > shm) shm = red;
   if (fz > shm) shm = fz;
   auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX, RAW>;
-  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  hipError_t err = lds_limit_once<router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX, RAW>>((int)shm);
   if (err != hipSuccess) return err;
   dim3 grid((a.T + BM - 1) / BM, a.Ep / BN);
   kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.Wg, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
