@@ -338,6 +338,13 @@ __device__ __forceinline__ void combine1_dropped(const Combine1& cmb, uint16_t* 
   }
 }
 
+// A row of zeros (zero-initialised at load, never written) that the token-row
+// loads of a tile's padding rows read instead of a real row: their products
+// are discarded either way, and zero operands cost the matrix cores less
+// power, which the clock of a power-limited GEMM turns into speed.
+constexpr int kZeroRowElems = 32768;
+__device__ __align__(16) uint16_t g_zero_row[kZeroRowElems];
+
 // Cache policy of a direct-to-LDS load: 0, or non-temporal (kLoadNT) for
 // weight rows that no other tile reads (NTW: every expert fits one m-tile), so
 // that the streamed weights do not push the token rows and the hidden
@@ -483,7 +490,8 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
       if (r < BM) {
         const int rr = r < t.rows ? r : 0;
         const int src = gather ? clamp_row(s_gidx[gbuf][w][q * RPL + lane / CPR], xrows) : t.row0 + rr;
-        rowp[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
+        rowp[q] = (r >= t.rows && K <= kZeroRowElems) ? reinterpret_cast<uintptr_t>(g_zero_row + c * 8)
+                                                      : reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
       } else {
         const int wr = r - BM;
         const uint16_t* base = (kGated && wr >= WR / 2) ? W2 : W;
@@ -780,7 +788,8 @@ __global__ void __launch_bounds__(512, 1) grouped_gemm_ring_kernel(const uint16_
       const int r = p / CPR, c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
       const int rr = r < t.rows ? r : 0;
       const int src = gather ? clamp_row(s_gidx[gbuf][w][q * 8 + lane / CPR], xrows) : t.row0 + rr;
-      rowA[q] = reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
+      rowA[q] = (r >= t.rows && K <= kZeroRowElems) ? reinterpret_cast<uintptr_t>(g_zero_row + c * 8)
+                                                    : reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
     }
   };
   auto set_rows_w = [&](const PipeTile& t) {
