@@ -409,14 +409,14 @@ def test_expert_ffn_large_tiles(gpu, act, F, H):
 
 def _radius(x, wg, bias, v):
     """Certified radius of an approximate logit (bf16 x, H % 64 == 0): c1 ||x|| ||w_e|| + c2 |v| + c3 |b_e|,
-    with c1 = 1.01 (65 (1 + 2^-7) + 129 2^-7) 2^-23 + 4 H 2^-53 (per 64-wide h chunk, an fp32 chain of the
-    64 exact products with the leading bf16 piece and one of the 128 with the two trailing pieces),
-    c2 = 2^-24 + 2^-44 and c3 = H 2^-52."""
+    with c1 = 1.01 ((65 (1 + 2^-7) + 129 2^-7) 2^-23 + (1 + 2^-6) 2^-24) + 4 H 2^-53 (per 64-wide h chunk,
+    an fp32 chain of the 64 exact products with the leading bf16 piece and one of the 128 with the two
+    trailing pieces, the two chain sums added in fp32), c2 = 2^-24 + 2^-44 and c3 = H 2^-52."""
     H = x.shape[1]
     xf = U.as_f64(x)
     xn = np.sqrt((xf * xf).sum(1))
     wn = np.sqrt((wg.astype(np.float64) ** 2).sum(0))
-    c1 = 1.01 * (65 * (1 + 2.0 ** -7) + 129 * 2.0 ** -7) * 2.0 ** -23 + 4 * H * 2.0 ** -53
+    c1 = 1.01 * ((65 * (1 + 2.0 ** -7) + 129 * 2.0 ** -7) * 2.0 ** -23 + (1 + 2.0 ** -6) * 2.0 ** -24) + 4 * H * 2.0 ** -53
     b = np.zeros(wg.shape[1]) if bias is None else np.abs(bias.astype(np.float64))
     return c1 * xn[:, None] * wn[None, :] + (2.0 ** -24 + 2.0 ** -44) * np.abs(v) + H * 2.0 ** -52 * b[None, :]
 

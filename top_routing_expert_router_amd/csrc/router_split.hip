@@ -12,11 +12,13 @@
 //              expert-major [3][Ep][H]; partial sums of w^2 per 64 h.
 //  2. approx:  v = fl32(bias + sum over 64-wide h chunks of two fp32 MFMA
 //              chains, one over the 64 exact products x*hi and one over the
-//              128 products x*mid, x*lo; chain sums added in binary64).  A sum
-//              of n terms whose every addition errs by at most 2^-23 of the
-//              running magnitude (round-to-nearest or truncation alike) is off
-//              by at most ~n 2^-23 sum|terms|; |hi| <= (1 + 2^-8)|w| and
-//              |mid| + |lo| <= 2^-7 |w|; Cauchy-Schwarz gives sum|x*w| <=
+//              128 products x*mid, x*lo; per chunk the two chain sums are
+//              added in fp32, and the chunk sums in binary64).  A sum of n
+//              terms whose every addition errs by at most 2^-23 of the running
+//              magnitude (round-to-nearest or truncation alike) is off by at
+//              most ~n 2^-23 sum|terms|; |hi| <= (1 + 2^-8)|w| and |mid| + |lo|
+//              <= 2^-7 |w|; the fp32 addition of the two chain sums errs by at
+//              most 2^-24 of their magnitude; Cauchy-Schwarz gives sum|x*w| <=
 //              ||x|| ||w_e||.  Hence
 //                |v - l_exact| <= rho = c1 ||x|| ||w_e|| + c2 |v| + c3 |bias|.
 //  3. certify: per token (one wave), the top k by (v desc, index asc) and its
@@ -42,6 +44,7 @@ namespace moe {
 namespace {
 
 constexpr int kChunk = 64;  // h per pipeline stage and per fp32 accumulation chain
+constexpr f32x4_t kZero4 = {0.f, 0.f, 0.f, 0.f};
 
 __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   hi = f32_to_bf16_bits(w);
@@ -343,10 +346,12 @@ __device__ __forceinline__ double exact_dot_raw(const uint16_t* __restrict__ xr,
   return s;
 }
 
-// Bound on ||x|| from the fp32 sum of squares (each of the <= H additions errs
-// by at most 2^-24 relative) and on the rounding of the square root.
+// Bound on ||x|| from an fp32 sum of squares of bf16 values, in any order
+// (each of the <= 2H roundings errs by at most 2^-23 relative, or by at most
+// 2^-126 absolute where the matrix cores flush a tiny product or partial sum
+// to zero), and on the rounding of the square root.
 __device__ __forceinline__ float xnorm_bound(float sq, int H) {
-  return sqrtf(sq * (1.0f + (float)H * 0x1p-22f + 0x1p-20f)) * (1.0f + 0x1p-20f);
+  return sqrtf((sq + (float)(2 * H) * 0x1p-126f) * (1.0f + (float)H * 0x1p-22f + 0x1p-20f)) * (1.0f + 0x1p-20f);
 }
 
 // Work the fused epilogue takes over from later kernels when its token tile
@@ -465,9 +470,12 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc64[i][n][j] = 0.0;
     }
-  float sq[MF];
+  // sum_h x^2 of the wave's token rows (waves of expert group 0): the diagonal
+  // of x x^T, accumulated on the matrix cores from the x fragments themselves
+  f32x4_t acc_sq[MF];
 #pragma unroll
-  for (int i = 0; i < MF; ++i) sq[i] = 0.0f;
+  for (int i = 0; i < MF; ++i) acc_sq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float sq[MF];
   float wsum[WN];  // RAW: sum of w^2 over this lane's fragments (waves of token group 0)
 #pragma unroll
   for (int n = 0; n < WN; ++n) wsum[n] = 0.0f;
@@ -537,8 +545,9 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
                          bl = __builtin_bit_cast(bf16x8_t, pl);
 #pragma unroll
           for (int i = 0; i < MF; ++i) {
-            acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bh, acc_hi[i][n], 0, 0, 0);
-            acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bm, acc_ml[i][n], 0, 0, 0);
+            // each stage's chains start from a zero C operand (no clearing)
+            acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bh, kk == 0 ? kZero4 : acc_hi[i][n], 0, 0, 0);
+            acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bm, kk == 0 ? kZero4 : acc_ml[i][n], 0, 0, 0);
             acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bl, acc_ml[i][n], 0, 0, 0);
           }
         }
@@ -551,43 +560,37 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
                 st + lds_pos(rbase + BM + p * BN + (eg * WN + n) * 16 + (lane & 15), c));
 #pragma unroll
             for (int i = 0; i < MF; ++i) {
-              if (p == 0) acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_hi[i][n], 0, 0, 0);
-              else acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc_ml[i][n], 0, 0, 0);
+              // each stage's chains start from a zero C operand (no clearing)
+              if (p == 0)
+                acc_hi[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, kk == 0 ? kZero4 : acc_hi[i][n], 0, 0, 0);
+              else
+                acc_ml[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    a[i], b, kk == 0 && p == 1 ? kZero4 : acc_ml[i][n], 0, 0, 0);
             }
           }
       }
       if (eg == 0) {
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          const u32x4_t u = __builtin_bit_cast(u32x4_t, a[i]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float lo = __uint_as_float(u[q] << 16), hi = __uint_as_float(u[q] & 0xFFFF0000u);
-            sq[i] = __builtin_fmaf(lo, lo, sq[i]);
-            sq[i] = __builtin_fmaf(hi, hi, sq[i]);
-          }
-        }
+        for (int i = 0; i < MF; ++i) acc_sq[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], a[i], acc_sq[i], 0, 0, 0);
       }
     }
+    // the two chain sums are added in fp32 (one more rounding, at most 2^-24
+    // of their magnitude), then into the binary64 accumulators
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
-      for (int n = 0; n < WN; ++n) {
+      for (int n = 0; n < WN; ++n)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          acc64[i][n][jj] += (double)acc_hi[i][n][jj];
-          acc64[i][n][jj] += (double)acc_ml[i][n][jj];
-        }
-        acc_hi[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc_ml[i][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+        for (int jj = 0; jj < 4; ++jj) acc64[i][n][jj] += (double)(acc_hi[i][n][jj] + acc_ml[i][n][jj]);
   }
 
-  // row sums of x^2: lanes l, l^16, l^32, l^48 hold the four k groups of row l%16
+  // row sums of x^2 to every lane l of row l%16: entry (t, t) of the 16 x 16
+  // block is element t%4 of lane 16 (t/4) + t
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
-    sq[i] += __shfl_xor(sq[i], 16, 64);
-    sq[i] += __shfl_xor(sq[i], 32, 64);
+    const int t = lane & 15, q = lane & 3;
+    const float d = q == 0 ? acc_sq[i][0] : q == 1 ? acc_sq[i][1] : q == 2 ? acc_sq[i][2] : acc_sq[i][3];
+    sq[i] = __shfl(d, 16 * (t >> 2) + t, 64);
   }
 
   // slices > 0 hand their partial sums to slice 0 through LDS
@@ -1049,10 +1052,12 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   }
 
   // hi chain: 64 products (+ the running sum), |hi| <= (1 + 2^-7)|w|; mid/lo
-  // chain: 128 products, |mid| + |lo| <= 2^-7 |w|; 2^-23 per addition, 1%
+  // chain: 128 products, |mid| + |lo| <= 2^-7 |w|; 2^-23 per addition; the
+  // fp32 sum of the two chains, 2^-24 of at most (1 + 2^-6) sum|x*w|; 1%
   // slack; binary64 sums (here and in the exact definition) add at most
   // 4 H 2^-53 relative to sum|x*w|.
-  const double c1 = 1.01 * (65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + 4.0 * (double)H * 0x1p-53;
+  const double c1 = 1.01 * ((65.0 * (1.0 + 0x1p-7) + 129.0 * 0x1p-7) * 0x1p-23 + (1.0 + 0x1p-6) * 0x1p-24) +
+                    4.0 * (double)H * 0x1p-53;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;  // expert ids 0 .. E-1
   const SplitTail tail{ep.dst_rank, ep.hist, nbits, (T + 63) / 64, ep.Ppart, ep.Zpart, ep.Cpart, ep.score_fn};
