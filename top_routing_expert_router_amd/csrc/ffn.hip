@@ -381,7 +381,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
                                                                    const int32_t* __restrict__ gather, int xrows,
-                                                                   Combine1 cmb) {
+                                                                   Combine1 cmb, int rlo, int rhi) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -411,13 +411,18 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   __shared__ int s_gidx[2][NW][64];          // gathered row indices, two tiles
   int gbuf = 0;                              // table of the tile being loaded
 
-  {  // tile list: ceil(kept_e / BM) * ntn tiles per expert
+  {  // tile list: ceil(kept_e / BM) * ntn tiles per expert whose row count
+     // lies in (rlo, rhi] (the other experts belong to another launch)
     const int per = (E + 64 * NW - 1) / (64 * NW);
     const int e0 = tid * per;
+    auto tiles_of = [&](int e) {
+      const int rows = offsets[e + 1] - offsets[e];
+      return rows > rlo && rows <= rhi ? (rows + BM - 1) / BM * ntn : 0;
+    };
     int cnt = 0;
     for (int j = 0; j < per; ++j) {
       const int e = e0 + j;
-      if (e < E) cnt += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+      if (e < E) cnt += tiles_of(e);
     }
     int total;
     int run = block_exclusive_scan(cnt, s_scan, &total);
@@ -426,7 +431,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
       if (e < E) {
         s_ts[e] = run;
         s_off[e] = offsets[e];
-        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * ntn;
+        run += tiles_of(e);
       }
     }
     if (tid == 0) {
@@ -1007,10 +1012,11 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
   return hipGetLastError();
 }
 
+// rlo, rhi: only the experts with rlo < rows <= rhi
 template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              const Combine1& cmb, hipStream_t st) {
+                              const Combine1& cmb, hipStream_t st, int rlo = -1, int rhi = INT32_MAX) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -1023,7 +1029,7 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   if (err != hipSuccess) return err;
   grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb, rlo, rhi);
   return hipGetLastError();
 }
 
@@ -1085,6 +1091,21 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
                                                                           gather, xrows, cmb, st)
                              : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
                                                                            gather, xrows, cmb, st);
+    }
+    // With experts of more than 128 rows possible, those take 256 x 256 tiles
+    // (a CU's loads per stage carry twice the MFMA work) in a launch of their
+    // own after the 128 x 256 tiles of the others.  (The top-1 combine epilogue
+    // also handles the dropped tokens once per launch: kept in one launch.)
+    if constexpr (EPI != EPI_COMBINE1) {
+      if (rows_cap > 128) {
+        hipError_t e1 = launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather,
+                                                                   xrows, cmb, st, -1, 128);
+        if (e1 != hipSuccess) return e1;
+        return rows_cap <= 256 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                            gather, xrows, cmb, st, 128)
+                               : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max,
+                                                                             cus, gather, xrows, cmb, st, 128);
+      }
     }
     return rows_cap <= 128 ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
                                                                         gather, xrows, cmb, st)
