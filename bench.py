@@ -52,8 +52,8 @@ def src_hash():
 
 
 def read_traffic(workload):
-    """HBM bytes per expert-stage launch pair from the committed rocprofv3 PMC summary,
-    if it was taken on the current expert-FFN source; else None."""
+    """HBM bytes per step of the expert-FFN stage (all its grouped-GEMM launches) from the
+    committed rocprofv3 PMC summary, if it was taken on the current expert-FFN source; else None."""
     path = os.path.join(ROOT, "profiles", f"expert_ffn_pmc_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -593,7 +593,7 @@ def main():
 
 def extra_workload(name, steps, warmup):
     """The same whole-layer measurement, briefer, on another workload: layer time, tokens/s,
-    the expert-FFN stage (two launches) and its roofline fraction."""
+    the expert-FFN stage (its grouped-GEMM launches) and its roofline fraction."""
     import numpy as np
     import torch
 
