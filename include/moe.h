@@ -273,6 +273,44 @@ moe_status moe_forward_shared(const moe_config *cfg, const void *x, const float 
                               const void *Ws2, const void *residual, void *y, const moe_plan *plan, void *X, void *Y,
                               void *ws, size_t ws_bytes, void *stream);
 
+/* ---- backward ([EP] layer walk-through run backwards; its all-to-all paragraph:
+ * the combine's backward has the dispatch's shape and the dispatch's backward the
+ * combine's; router section: the load-balancing term reaches the router only
+ * through P_e, the z-loss acts on the logits).  The gradient of
+ *   L = sum_{t,h} dy[t][h] * y[t][h]  (+ the router training terms when plan->losses != NULL)
+ * where y is the routed layer's output (moe_forward without the shared expert),
+ * with the routing decision held fixed: the choices, drops and GShard draws of
+ * `plan` are constants, roundings are taken as the identity, and a dropped or
+ * absent choice gets no gradient from y while still entering the Jacobian of the
+ * other gates.  The residual's gradient is dy itself and is not written.  The
+ * hidden activations and expert outputs are recomputed from x (no forward
+ * buffers are needed). */
+typedef struct {
+  float *dx;    /* [T][H]    dL/dx (expert and router paths), fp32, required            */
+  float *dWg;   /* [H][E]    dL/dWg, fp32, required                                     */
+  float *dbias; /* [E]       dL/dbias, fp32, or NULL                                    */
+  float *dW1;   /* [E][F][H] fp32, required                                             */
+  float *dW3;   /* [E][F][H] fp32, required iff SwiGLU (else ignored)                   */
+  float *dW2;   /* [E][H][F] fp32, required                                             */
+  float *dg;    /* [T][k]    dL/dtopk_gate, fp32, or NULL (0 for dropped choices)        */
+} moe_grads;
+
+/* Device workspace bytes moe_backward needs (0 when the configuration is invalid). */
+size_t moe_backward_workspace_bytes(const moe_config *cfg);
+
+/* x: device [T][H] dtype (the forward's input).  Wg: device [H][E] fp32.  W1, W3,
+ * W2: the expert weights (W3 iff SwiGLU).  plan: the routing moe_route made for x
+ * (topk_idx, topk_gate, dst_row, demand, offsets, row_token) with plan->logits
+ * written; plan->losses != NULL adds the gradients of the training terms of cfg
+ * (aux_mode, aux_coeff, z_coeff, score_fn).  dy: device [T][H] dtype.  Every
+ * sum is accumulated in fp32 in a fixed order (binary64 inside the per-token
+ * gate Jacobian), so results are deterministic.  ws: device, >=
+ * moe_backward_workspace_bytes.  The shared expert is not part of this
+ * gradient. */
+moe_status moe_backward(const moe_config *cfg, const void *x, const float *Wg, const void *W1, const void *W3,
+                        const void *W2, const moe_plan *plan, const void *dy, const moe_grads *grads, void *ws,
+                        size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 
 EXPORTS = ("moe_validate", "moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_status_str",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_shared_expert", "moe_combine_shared", "moe_forward_shared", "moe_route_noalloc")
+           "moe_shared_expert", "moe_combine_shared", "moe_forward_shared", "moe_route_noalloc",
+           "moe_backward_workspace_bytes", "moe_backward")
 
 
 class MoEError(RuntimeError):
@@ -39,6 +40,10 @@ class _Config(ctypes.Structure):
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_gate", "dst_row", "demand", "kept", "offsets",
                                                "row_token", "n_dropped", "logits", "losses", "second_u")]
+
+
+class _Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dg")]
 
 
 @dataclass
@@ -116,6 +121,10 @@ def lib():
         L.moe_combine_shared.argtypes = [cfgp, vp, planp, vp, vp, vp, vp]
         L.moe_forward_shared.restype = ctypes.c_int
         L.moe_forward_shared.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, planp, vp, vp, vp, sz, vp]
+        L.moe_backward_workspace_bytes.restype = sz
+        L.moe_backward_workspace_bytes.argtypes = [cfgp]
+        L.moe_backward.restype = ctypes.c_int
+        L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, planp, vp, ctypes.POINTER(_Grads), vp, sz, vp]
         _lib = L
     return _lib
 
@@ -253,3 +262,34 @@ def forward_shared(cfg, x, wg, bias, w1, w3, w2, ws1, ws3, ws2, residual, y, pla
                                   _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(residual), _ptr(y), ctypes.byref(p), _ptr(X),
                                   _ptr(Y), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "moe_forward_shared")
+
+
+def backward_workspace_bytes(cfg: MoEConfig):
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(cfg.c())))
+
+
+def alloc_grads(cfg: MoEConfig, device, bias=True, dg=False):
+    """fp32 device tensors for the gradients moe_backward writes."""
+    import torch
+
+    f32 = torch.float32
+    g = dict(dx=torch.empty((cfg.T, cfg.H), dtype=f32, device=device),
+             dWg=torch.empty((cfg.H, cfg.E), dtype=f32, device=device),
+             dW1=torch.empty((cfg.E, cfg.F, cfg.H), dtype=f32, device=device),
+             dW2=torch.empty((cfg.E, cfg.H, cfg.F), dtype=f32, device=device))
+    if cfg.act == SWIGLU:
+        g["dW3"] = torch.empty((cfg.E, cfg.F, cfg.H), dtype=f32, device=device)
+    if bias:
+        g["dbias"] = torch.empty(cfg.E, dtype=f32, device=device)
+    if dg:
+        g["dg"] = torch.empty((cfg.T, cfg.k), dtype=f32, device=device)
+    return g
+
+
+def backward(cfg, x, wg, w1, w3, w2, plan, dy, grads, ws, stream=None):
+    """moe_backward: grads is a dict of device tensors (see alloc_grads)."""
+    c, p = cfg.c(), _plan_struct(plan)
+    gs = _Grads(*[_ptr(grads.get(n)) for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dg")])
+    st = lib().moe_backward(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), ctypes.byref(p),
+                            _ptr(dy), ctypes.byref(gs), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(st, "moe_backward")

@@ -1,0 +1,570 @@
+// Backward of the MoE layer: the gradient of L = sum(dy * y) (+ the router
+// training terms) in x, the router weights and bias, and the expert weights,
+// with the routing decision held fixed.
+//
+// The chain is the layer walk-through of the "Expert-parallel MoE training"
+// explainer run backwards, and its all-to-all paragraph gives the two
+// transposes: the combine's backward has the dispatch's shape (each kept
+// choice's row receives g * dy of its token) and the dispatch's backward the
+// combine's (each token sums the input gradients of its kept rows).  The same
+// explainer's router section: the load-balancing term reaches the router only
+// through P_e (f_e comes from the top-k selection), the z-loss acts on the
+// logits.  Roundings are taken as the identity; a dropped or absent choice
+// gets no gradient from the output but still enters the other gates' Jacobian.
+//
+// The forward's hidden activations and expert outputs are recomputed from x
+// and the plan (activation checkpointing): u = x W1^T (and v = x W3^T), z =
+// act(u) (or silu(u) * v), Y = z W2^T.  Then
+//   dY = g * dy (kept rows), dg = <Y, dy>;
+//   dz = dY W2;  du = dz * act'(u)  (SwiGLU: du = dz v silu'(u), dv = dz silu(u));
+//   dX = du W1 (+ dv W3);  dx = sum of the token's kept rows of dX;
+//   dW2_e = dY_e^T z_e;  dW1_e = du_e^T X_e;  dW3_e = dv_e^T X_e;
+//   dl = gate Jacobian^T dg (+ training terms);  dWg = x^T dl;  dbias = sum_t dl;
+//   dx += dl Wg^T.
+// Every product here is a tiled fp32-accumulate GEMM with arbitrary strides,
+// over groups of rows (one per expert: ragged M) or of reduction indices
+// (ragged K), so that no operand needs a transposed copy; the order of every
+// sum is fixed, so results are deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+// ---------------------------------------------------------------------------
+// C (+)= A B per group g (blockIdx.z), fp32 accumulation in k order:
+//   A(m, k) = A[row(m) * sam + k * sak],  B(k, n) = B[krow(k) * sbk + n * sbn],
+//   C(m, n) = C[m * scm + n * scn]  (+ the group's offsets a_g, b_g, c_g).
+// ragged 0: group g owns the rows offs[g] .. offs[g+1]-1 (global row indices for
+// A and C; A's row goes through `gather` when given); ragged 1: group g owns the
+// reduction indices offs[g] .. offs[g+1]-1 (B's row goes through `gather`).  An
+// empty reduction writes zeros (or leaves C unchanged when accumulating).
+// ---------------------------------------------------------------------------
+template <typename TA, typename TB>
+__global__ void __launch_bounds__(256) gemm_generic_kernel(GemmArgs p) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4], Bs[BK][BN + 4];
+  const int g = blockIdx.z;
+  int64_t m_lo = 0, k_lo = 0;
+  int m_n = p.M, k_n = p.K;
+  if (p.offs) {
+    const int lo = p.offs[g], hi = p.offs[g + 1];
+    if (p.ragged == 0) {
+      m_lo = lo;
+      m_n = hi - lo;
+    } else {
+      k_lo = lo;
+      k_n = hi - lo;
+    }
+  }
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= m_n || n0 >= p.N) return;
+  const TA* A = static_cast<const TA*>(p.A) + (int64_t)g * p.a_g;
+  const TB* B = static_cast<const TB*>(p.B) + (int64_t)g * p.b_g;
+  float* C = p.C + (int64_t)g * p.c_g;
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < k_n; k0 += BK) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      const int mm = e % BM, kk = e / BM;
+      const int m = m0 + mm, k = k0 + kk;
+      float v = 0.0f;
+      if (m < m_n && k < k_n) {
+        int64_t row = m_lo + m;
+        if (p.ragged == 0 && p.gather) row = p.gather[row];
+        v = ld(A, row * p.sam + (k_lo + k) * p.sak);
+      }
+      As[kk][mm] = v;
+      const int nn = e % BN;
+      const int n = n0 + nn;
+      float w = 0.0f;
+      if (n < p.N && k < k_n) {
+        int64_t kr = k_lo + k;
+        if (p.ragged == 1 && p.gather) kr = p.gather[kr];
+        w = ld(B, kr * p.sbk + n * p.sbn);
+      }
+      Bs[kk][nn] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < m_n && n < p.N) {
+        float* c = C + (m_lo + m) * p.scm + (int64_t)n * p.scn;
+        *c = p.accumulate ? *c + acc[i][j] : acc[i][j];
+      }
+    }
+}
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+
+__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+
+// d/du of the exact-erf GELU: Phi(u) + u phi(u)
+__device__ __forceinline__ float gelu_grad_f(float u) {
+  return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
+}
+
+// z = act(u), or silu(u) * v; rows of the kept range only (R read on the device)
+__global__ void act_fwd_kernel(const float* __restrict__ u, const float* __restrict__ v, float* __restrict__ z,
+                               const int32_t* __restrict__ offsets, int E, int F, int act) {
+  const int64_t n = (int64_t)offsets[E] * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float a = u[i];
+    z[i] = act == 2 ? silu_f(a) * v[i] : (act == 0 ? (a > 0.0f ? a : 0.0f) : gelu_f(a));
+  }
+}
+
+// du = dz * act'(u); SwiGLU: du = dz * v * silu'(u), dv = dz * silu(u)
+__global__ void act_bwd_kernel(const float* __restrict__ dz, const float* __restrict__ u, const float* __restrict__ v,
+                               float* __restrict__ du, float* __restrict__ dv, const int32_t* __restrict__ offsets,
+                               int E, int F, int act) {
+  const int64_t n = (int64_t)offsets[E] * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float a = u[i], d = dz[i];
+    if (act == 2) {
+      const float s = 1.0f / (1.0f + __expf(-a));
+      du[i] = d * v[i] * (s * (1.0f + a * (1.0f - s)));
+      dv[i] = d * (a * s);
+    } else {
+      du[i] = d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a));
+    }
+  }
+}
+
+// Block sum of one float per thread (256 threads), in a fixed order.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Combine backward, one block per token: dY[dst_row] = g * dy[t] for each kept
+// choice, dg[t][r] = <Y[dst_row], dy[t]> (0 for a dropped or absent choice).
+template <typename TD, typename TY>
+__global__ void __launch_bounds__(256) combine_bwd_kernel(const TD* __restrict__ dy, const TY* __restrict__ Y,
+                                                          const float* __restrict__ gate,
+                                                          const int32_t* __restrict__ dst, float* __restrict__ dY,
+                                                          float* __restrict__ dg, int H, int k) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  for (int r = 0; r < k; ++r) {
+    const int row = dst[(int64_t)t * k + r];
+    if (row < 0) {
+      if (threadIdx.x == 0) dg[(int64_t)t * k + r] = 0.0f;
+      continue;
+    }
+    const float g = gate[(int64_t)t * k + r];
+    float part = 0.0f;
+    for (int h = threadIdx.x; h < H; h += 256) {
+      const float d = ld(dy, (int64_t)t * H + h);
+      part = __builtin_fmaf(ld(Y, (int64_t)row * H + h), d, part);
+      dY[(int64_t)row * H + h] = g * d;
+    }
+    const float s = block_sum256(part, red);
+    if (threadIdx.x == 0) dg[(int64_t)t * k + r] = s;
+  }
+}
+
+// Dispatch backward: dx[t] = sum over r ascending of the kept rows of dX.
+__global__ void __launch_bounds__(256) gather_sum_kernel(const float* __restrict__ dX, const int32_t* __restrict__ dst,
+                                                         float* __restrict__ dx, int H, int k) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float acc = 0.0f;
+    for (int r = 0; r < k; ++r) {
+      const int row = dst[(int64_t)t * k + r];
+      if (row >= 0) acc += dX[(int64_t)row * H + h];
+    }
+    dx[(int64_t)t * H + h] = acc;
+  }
+}
+
+// f_e of the load-balancing term: demand / (T k) (every choice) or the first
+// choices / T; one block.
+__global__ void __launch_bounds__(1024) aux_f_kernel(const int32_t* __restrict__ demand,
+                                                     const int32_t* __restrict__ topk_idx, int T, int E, int k,
+                                                     int aux_mode, double* __restrict__ f) {
+  __shared__ int cnt[1024];
+  for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  if (aux_mode == 1)
+    for (int t = threadIdx.x; t < T; t += 1024) {
+      const int e = topk_idx[(int64_t)t * k];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024)
+    f[e] = aux_mode == 1 ? (double)cnt[e] / (double)T : (double)demand[e] / ((double)T * (double)k);
+}
+
+// dL/dlogits of one token (one wave), binary64 sums: the gate Jacobian applied
+// to dg, plus the load-balancing term through P_e and the z-loss when asked.
+constexpr int kMaxJE = 16;  // E <= 1024 = 64 lanes x 16
+__global__ void __launch_bounds__(64) gate_bwd_kernel(const float* __restrict__ logits, const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ dg, const double* __restrict__ f,
+                                                      float* __restrict__ dl, int T, int E, int k, int gate_mode,
+                                                      int score_fn, double aux_coeff, double z_coeff) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float* l = logits + (int64_t)t * E;
+  const int je = (E + 63) / 64;
+  double lv[kMaxJE], acc[kMaxJE];
+  double m = -INFINITY;
+  for (int j = 0; j < je; ++j) {
+    const int e = lane + 64 * j;
+    lv[j] = e < E ? (double)l[e] : -INFINITY;
+    acc[j] = 0.0;
+    m = lv[j] > m ? lv[j] : m;
+  }
+  for (int d = 32; d > 0; d >>= 1) {
+    const double o = __shfl_xor(m, d, 64);
+    m = o > m ? o : m;
+  }
+  double den = 0.0;
+  for (int j = 0; j < je; ++j) den += lane + 64 * j < E ? exp(lv[j] - m) : 0.0;
+  for (int d = 32; d > 0; d >>= 1) den += __shfl_xor(den, d, 64);
+  auto p_of = [&](double x) { return exp(x - m) / den; };
+  // the chosen experts' logits and upstream gradients (every lane holds all k)
+  double lc[16], dgc[16];
+  int ic[16];
+  for (int r = 0; r < k; ++r) {
+    ic[r] = idx[(int64_t)t * k + r];
+    lc[r] = (double)l[ic[r]];
+    dgc[r] = (double)dg[(int64_t)t * k + r];
+  }
+  auto add_at = [&](int e, double v) {
+    if ((e & 63) == lane) acc[e >> 6] += v;
+  };
+  if (score_fn == 1 && gate_mode != 2) {  // sigmoid scores
+    double s[16], S = 0.0, sgd = 0.0;
+    for (int r = 0; r < k; ++r) {
+      s[r] = 1.0 / (1.0 + exp(-lc[r]));
+      S += s[r];
+    }
+    for (int r = 0; r < k; ++r) sgd += s[r] / S * dgc[r];
+    for (int r = 0; r < k; ++r) {
+      const double dsc = gate_mode == 0 ? dgc[r] : (dgc[r] - sgd) / S;
+      add_at(ic[r], dsc * s[r] * (1.0 - s[r]));
+    }
+  } else if (gate_mode == 0) {  // softmax over all E, the chosen p
+    double sgd = 0.0;
+    for (int r = 0; r < k; ++r) sgd += p_of(lc[r]) * dgc[r];
+    for (int j = 0; j < je; ++j)
+      if (lane + 64 * j < E) acc[j] -= p_of(lv[j]) * sgd;
+    for (int r = 0; r < k; ++r) add_at(ic[r], p_of(lc[r]) * dgc[r]);
+  } else {  // renormalised or softmax over the chosen: softmax over the chosen logits
+    double mc = lc[0], dc = 0.0, sgd = 0.0;
+    for (int r = 1; r < k; ++r) mc = lc[r] > mc ? lc[r] : mc;
+    for (int r = 0; r < k; ++r) dc += exp(lc[r] - mc);
+    for (int r = 0; r < k; ++r) sgd += exp(lc[r] - mc) / dc * dgc[r];
+    for (int r = 0; r < k; ++r) add_at(ic[r], exp(lc[r] - mc) / dc * (dgc[r] - sgd));
+  }
+  if (f && aux_coeff != 0.0) {
+    const double scale = aux_coeff * (double)E / (double)T;  // dL/dq_e(t) = scale * f_e
+    if (score_fn == 1) {
+      double S = 0.0, cs = 0.0;
+      for (int j = 0; j < je; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+          const double s = 1.0 / (1.0 + exp(-lv[j]));
+          S += s;
+          cs += scale * f[e] * s;
+        }
+      }
+      for (int d = 32; d > 0; d >>= 1) {
+        S += __shfl_xor(S, d, 64);
+        cs += __shfl_xor(cs, d, 64);
+      }
+      for (int j = 0; j < je; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+          const double s = 1.0 / (1.0 + exp(-lv[j]));
+          acc[j] += s * (1.0 - s) / S * (scale * f[e] - cs / S);
+        }
+      }
+    } else {
+      double cp = 0.0;
+      for (int j = 0; j < je; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) cp += scale * f[e] * p_of(lv[j]);
+      }
+      for (int d = 32; d > 0; d >>= 1) cp += __shfl_xor(cp, d, 64);
+      for (int j = 0; j < je; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) acc[j] += p_of(lv[j]) * (scale * f[e] - cp);
+      }
+    }
+  }
+  if (z_coeff != 0.0) {
+    const double lse = m + log(den);
+    for (int j = 0; j < je; ++j)
+      if (lane + 64 * j < E) acc[j] += z_coeff * 2.0 / (double)T * lse * p_of(lv[j]);
+  }
+  for (int j = 0; j < je; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) dl[(int64_t)t * E + e] = (float)acc[j];
+  }
+}
+
+// dbias[e] = sum over t of dl[t][e]: 64 experts per block, four token phases
+// summed in a fixed order.
+__global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ dl, float* __restrict__ out, int T,
+                                                     int E) {
+  __shared__ float part[4][64];
+  const int el = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  float s = 0.0f;
+  if (e < E)
+    for (int t = ph; t < T; t += 4) s += dl[(int64_t)t * E + e];
+  part[ph][el] = s;
+  __syncthreads();
+  if (ph == 0 && e < E) out[e] = (part[0][el] + part[1][el]) + (part[2][el] + part[3][el]);
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+int grid_1d(int64_t n, int bs) {
+  const int64_t b = (n + bs - 1) / bs;
+  return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+}  // namespace
+
+template <typename TA, typename TB>
+hipError_t launch_gemm_generic(const GemmArgs& p, int groups, int max_m, hipStream_t st) {
+  if (groups <= 0 || max_m <= 0 || p.N <= 0) return hipSuccess;
+  dim3 grid((p.N + 63) / 64, (max_m + 63) / 64, groups);
+  gemm_generic_kernel<TA, TB><<<grid, dim3(256), 0, st>>>(p);
+  return hipGetLastError();
+}
+
+static hipError_t gemm(bool a_bf16, bool b_bf16, const GemmArgs& p, int groups, int max_m, hipStream_t st) {
+  if (a_bf16 && b_bf16) return launch_gemm_generic<uint16_t, uint16_t>(p, groups, max_m, st);
+  if (a_bf16) return launch_gemm_generic<uint16_t, float>(p, groups, max_m, st);
+  if (b_bf16) return launch_gemm_generic<float, uint16_t>(p, groups, max_m, st);
+  return launch_gemm_generic<float, float>(p, groups, max_m, st);
+}
+
+size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t RF = al(sizeof(float) * (size_t)R_max * (size_t)F), RH = al(sizeof(float) * (size_t)R_max * (size_t)H);
+  // u, v, z, dz, du, dv [R][F]; Y, dY, dX [R][H]; dl [T][E]; f [E]; dg [T][k]
+  return 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E) + al(sizeof(double) * (size_t)E) +
+         al(sizeof(float) * (size_t)T * (size_t)k) + 256;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
+  const int T = a.T, H = a.H, E = a.E, k = a.k, F = a.F;
+  const int64_t R_max = a.R_max;
+  const bool bf = a.bf16;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  char* w = static_cast<char*>(a.ws);
+  const size_t RF = al(sizeof(float) * (size_t)R_max * (size_t)F), RH = al(sizeof(float) * (size_t)R_max * (size_t)H);
+  float* u = reinterpret_cast<float*>(w);
+  float* v = reinterpret_cast<float*>(w + RF);
+  float* z = reinterpret_cast<float*>(w + 2 * RF);
+  float* dz = reinterpret_cast<float*>(w + 3 * RF);
+  float* du = reinterpret_cast<float*>(w + 4 * RF);
+  float* dv = reinterpret_cast<float*>(w + 5 * RF);
+  float* Y = reinterpret_cast<float*>(w + 6 * RF);
+  float* dY = reinterpret_cast<float*>(w + 6 * RF + RH);
+  float* dX = reinterpret_cast<float*>(w + 6 * RF + 2 * RH);
+  float* dl = reinterpret_cast<float*>(w + 6 * RF + 3 * RH);
+  double* f = reinterpret_cast<double*>(w + 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E));
+  float* dgw = reinterpret_cast<float*>(w + 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E) +
+                                        al(sizeof(double) * (size_t)E));
+  const bool gated = a.act == 2;
+  hipError_t err = hipSuccess;
+#define MOE_BW(call)                                \
+  do {                                              \
+    if ((err = (call)) != hipSuccess) return err;   \
+  } while (0)
+
+  if (T == 0) {  // no tokens: every gradient is zero
+    auto zero = [&](float* q, int64_t n) {
+      if (q && n > 0) zero_f32_kernel<<<grid_1d(n, 256), 256, 0, st>>>(q, n);
+      return hipGetLastError();
+    };
+    MOE_BW(zero(a.dWg, (int64_t)H * E));
+    MOE_BW(zero(a.dbias, E));
+    MOE_BW(zero(a.dW1, (int64_t)E * F * H));
+    if (gated) MOE_BW(zero(a.dW3, (int64_t)E * F * H));
+    MOE_BW(zero(a.dW2, (int64_t)E * H * F));
+    return hipSuccess;
+  }
+  const int mr = (int)(R_max < INT32_MAX ? R_max : INT32_MAX);  // rows bound for the ragged-M grids
+  if (R_max > 0) {
+    // 1. u = x[row_token] W1^T, v = x[row_token] W3^T (per expert, the kept rows)
+    GemmArgs g{};
+    g.A = a.x;
+    g.sam = H, g.sak = 1;
+    g.B = a.W1;
+    g.sbk = 1, g.sbn = H, g.b_g = (int64_t)F * H;
+    g.C = u;
+    g.scm = F, g.scn = 1;
+    g.M = mr, g.N = F, g.K = H;
+    g.offs = a.offsets, g.ragged = 0, g.gather = a.row_token;
+    MOE_BW(gemm(bf, bf, g, E, mr, st));
+    if (gated) {
+      g.B = a.W3;
+      g.C = v;
+      MOE_BW(gemm(bf, bf, g, E, mr, st));
+    }
+    // 2. z = act(u) (or silu(u) v)
+    act_fwd_kernel<<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
+    MOE_BW(hipGetLastError());
+    // 3. Y = z W2^T
+    GemmArgs y{};
+    y.A = z;
+    y.sam = F, y.sak = 1;
+    y.B = a.W2;
+    y.sbk = 1, y.sbn = F, y.b_g = (int64_t)H * F;
+    y.C = Y;
+    y.scm = H, y.scn = 1;
+    y.M = mr, y.N = H, y.K = F;
+    y.offs = a.offsets, y.ragged = 0;
+    MOE_BW(gemm(false, bf, y, E, mr, st));
+  }
+  // 4. combine backward: dY (kept rows), dg
+  float* dg = a.dg ? a.dg : dgw;
+  if (bf)
+    combine_bwd_kernel<uint16_t, float><<<T, 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), Y, a.topk_gate,
+                                                           a.dst_row, dY, dg, H, k);
+  else
+    combine_bwd_kernel<float, float><<<T, 256, 0, st>>>(static_cast<const float*>(a.dy), Y, a.topk_gate, a.dst_row,
+                                                        dY, dg, H, k);
+  MOE_BW(hipGetLastError());
+  if (R_max > 0) {
+    // 5. dz = dY W2 (W2 [E][H][F]: B(k = h, n = f))
+    GemmArgs g{};
+    g.A = dY;
+    g.sam = H, g.sak = 1;
+    g.B = a.W2;
+    g.sbk = F, g.sbn = 1, g.b_g = (int64_t)H * F;
+    g.C = dz;
+    g.scm = F, g.scn = 1;
+    g.M = mr, g.N = F, g.K = H;
+    g.offs = a.offsets, g.ragged = 0;
+    MOE_BW(gemm(false, bf, g, E, mr, st));
+    // 6. du (, dv)
+    act_bwd_kernel<<<grid_1d(R_max * F, 256), 256, 0, st>>>(dz, u, v, du, dv, a.offsets, E, F, a.act);
+    MOE_BW(hipGetLastError());
+    // 7. dX = du W1 (+ dv W3)  (W1 [E][F][H]: B(k = f, n = h))
+    GemmArgs x{};
+    x.A = du;
+    x.sam = F, x.sak = 1;
+    x.B = a.W1;
+    x.sbk = H, x.sbn = 1, x.b_g = (int64_t)F * H;
+    x.C = dX;
+    x.scm = H, x.scn = 1;
+    x.M = mr, x.N = H, x.K = F;
+    x.offs = a.offsets, x.ragged = 0;
+    MOE_BW(gemm(false, bf, x, E, mr, st));
+    if (gated) {
+      x.A = dv;
+      x.B = a.W3;
+      x.accumulate = 1;
+      MOE_BW(gemm(false, bf, x, E, mr, st));
+    }
+  }
+  // 8. dx = sum of the token's kept rows of dX
+  if (R_max > 0)
+    gather_sum_kernel<<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
+  else
+    zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
+  MOE_BW(hipGetLastError());
+  // 9. weight gradients, ragged over each expert's rows
+  {
+    GemmArgs g{};
+    g.M = H, g.N = F, g.K = 0;
+    g.offs = a.offsets, g.ragged = 1;
+    // dW2[e][h][f] = sum_r dY[r][h] z[r][f]
+    g.A = dY, g.sam = 1, g.sak = H;
+    g.B = z, g.sbk = F, g.sbn = 1;
+    g.C = a.dW2, g.scm = F, g.scn = 1, g.c_g = (int64_t)H * F;
+    MOE_BW(gemm(false, false, g, E, H, st));
+    // dW1[e][f][h] = sum_r du[r][f] x[row_token[r]][h]  (dW3 with dv)
+    GemmArgs w1{};
+    w1.M = F, w1.N = H, w1.K = 0;
+    w1.offs = a.offsets, w1.ragged = 1, w1.gather = a.row_token;
+    w1.A = du, w1.sam = 1, w1.sak = F;
+    w1.B = a.x, w1.sbk = H, w1.sbn = 1;
+    w1.C = a.dW1, w1.scm = H, w1.scn = 1, w1.c_g = (int64_t)F * H;
+    MOE_BW(gemm(false, bf, w1, E, F, st));
+    if (gated) {
+      w1.A = dv;
+      w1.C = a.dW3;
+      MOE_BW(gemm(false, bf, w1, E, F, st));
+    }
+  }
+  // 10. router: dl = gate Jacobian^T dg (+ training terms)
+  const bool terms = a.with_losses && (a.aux_coeff != 0.0 || a.z_coeff != 0.0);
+  if (terms && a.aux_coeff != 0.0) {
+    aux_f_kernel<<<1, 1024, 0, st>>>(a.demand, a.topk_idx, T, E, k, a.aux_mode, f);
+    MOE_BW(hipGetLastError());
+  }
+  float* dlo = dl;
+  gate_bwd_kernel<<<T, 64, 0, st>>>(a.logits, a.topk_idx, dg, (terms && a.aux_coeff != 0.0) ? f : nullptr, dlo, T, E,
+                                    k, a.gate_mode, a.score_fn, terms ? a.aux_coeff : 0.0, terms ? a.z_coeff : 0.0);
+  MOE_BW(hipGetLastError());
+  // 11. dWg = x^T dl, dbias = sum_t dl, dx += dl Wg^T
+  {
+    GemmArgs g{};
+    g.A = a.x, g.sam = 1, g.sak = H;
+    g.B = dlo, g.sbk = E, g.sbn = 1;
+    g.C = a.dWg, g.scm = E, g.scn = 1;
+    g.M = H, g.N = E, g.K = T;
+    MOE_BW(gemm(bf, false, g, 1, H, st));
+    if (a.dbias) {
+      col_sum_kernel<<<(E + 63) / 64, 256, 0, st>>>(dlo, a.dbias, T, E);
+      MOE_BW(hipGetLastError());
+    }
+    GemmArgs x{};
+    x.A = dlo, x.sam = E, x.sak = 1;
+    x.B = a.Wg, x.sbk = 1, x.sbn = E;
+    x.C = a.dx, x.scm = H, x.scn = 1;
+    x.M = T, x.N = H, x.K = E;
+    x.accumulate = 1;
+    MOE_BW(gemm(false, false, x, 1, T, st));
+  }
+#undef MOE_BW
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -126,4 +126,41 @@ hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* ga
 // off[0] = 0, off[1] = T: the offsets of one expert holding every token.
 hipError_t launch_dense_offsets(int32_t* off, int T, hipStream_t st);
 
+// ---- backward ----------------------------------------------------------------
+// Strided GEMM over groups (backward.hip): C (+)= A B with A(m, k) = A[row(m) *
+// sam + k * sak], B(k, n) = B[krow(k) * sbk + n * sbn], C(m, n) = C[m * scm + n *
+// scn]; group g adds a_g, b_g, c_g elements.  ragged 0: group g owns rows
+// offs[g] .. offs[g+1]-1 (A's row through gather when given); ragged 1: group g
+// owns reduction indices offs[g] .. offs[g+1]-1 (B's row through gather).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  float* C;
+  int M, N, K;
+  int64_t sam, sak, sbk, sbn, scm, scn;
+  int64_t a_g, b_g, c_g;
+  const int32_t* offs;
+  int ragged;
+  const int32_t* gather;
+  int accumulate;
+};
+
+struct BackwardArgs {
+  int T, H, E, k, F, act, gate_mode, score_fn, aux_mode;
+  int64_t R_max;
+  bool bf16;
+  bool with_losses;
+  double aux_coeff, z_coeff;
+  const void* x;
+  const float* Wg;
+  const void *W1, *W3, *W2;
+  const int32_t *topk_idx, *dst_row, *offsets, *row_token, *demand;
+  const float *topk_gate, *logits;
+  const void* dy;
+  float *dx, *dWg, *dbias, *dW1, *dW3, *dW2, *dg;  // dbias, dg optional
+  void* ws;
+};
+size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
+
 }  // namespace moe

@@ -199,6 +199,11 @@ size_t moe_workspace_bytes(const moe_config* c) {
   return layout_of(c).total;
 }
 
+size_t moe_backward_workspace_bytes(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return 0;
+  return moe::backward_workspace_bytes(c->T, c->H, c->E, c->k, c->F, max_rows_of(c));
+}
+
 const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";
@@ -472,6 +477,36 @@ moe_status moe_forward_shared(const moe_config* c, const void* x, const float* W
   void* Ys = static_cast<char*>(ws) + L.ys;
   if ((s = moe_shared_expert(c, x, Ws1, Ws3, Ws2, Ys, ws, ws_bytes, stream)) != MOE_OK) return s;
   return moe_combine_shared(c, Y, plan, residual, Ys, y, stream);
+}
+
+moe_status moe_backward(const moe_config* c, const void* x, const float* Wg, const void* W1, const void* W3,
+                        const void* W2, const moe_plan* plan, const void* dy, const moe_grads* g, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status s = moe_validate(c);
+  if (s != MOE_OK) return s;
+  if (!g || !plan || !Wg || !W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!g->dWg || !g->dW1 || !g->dW2 || (c->act == MOE_SWIGLU && !g->dW3)) return MOE_ERR_INVALID_ARG;
+  if (c->T > 0 && (!x || !dy || !g->dx || !plan->topk_idx || !plan->topk_gate || !plan->dst_row || !plan->demand ||
+                   !plan->offsets || !plan->row_token || !plan->logits))
+    return MOE_ERR_INVALID_ARG;
+  if (!plan->offsets) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_backward_workspace_bytes(c);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  moe::BackwardArgs a{};
+  a.T = c->T, a.H = c->H, a.E = c->E, a.k = c->k, a.F = c->F;
+  a.act = c->act, a.gate_mode = c->gate_mode, a.score_fn = c->score_fn, a.aux_mode = c->aux_mode;
+  a.R_max = max_rows_of(c);
+  a.bf16 = c->dtype == MOE_BF16;
+  a.with_losses = plan->losses != nullptr;
+  a.aux_coeff = c->aux_coeff, a.z_coeff = c->z_coeff;
+  a.x = x, a.Wg = Wg, a.W1 = W1, a.W3 = W3, a.W2 = W2;
+  a.topk_idx = plan->topk_idx, a.dst_row = plan->dst_row, a.offsets = plan->offsets, a.row_token = plan->row_token;
+  a.demand = plan->demand, a.topk_gate = plan->topk_gate, a.logits = plan->logits;
+  a.dy = dy;
+  a.dx = g->dx, a.dWg = g->dWg, a.dbias = g->dbias, a.dW1 = g->dW1, a.dW3 = g->dW3, a.dW2 = g->dW2, a.dg = g->dg;
+  a.ws = ws;
+  hipError_t e = moe::launch_backward(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "backward");
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@ RELU, GELU, SWIGLU = 0, 1, 2
 
 J_X, J_WG, J_BIAS, J_W1, J_W3, J_W2 = 0, 1, 2, 3, 4, 5
 J_S1, J_S3, J_S2 = 6, 7, 8  # shared expert
+J_DY = 9  # upstream gradient of the layer output (backward)
 
 
 @dataclass(frozen=True)
@@ -132,6 +133,11 @@ def gen_shared_weight(run: Run, which: str, Fs: int):
     out_f, in_f = (Fs, run.H) if which in ("s1", "s3") else (run.H, Fs)
     return normal(tensor_seed(run.run_id, j), out_f * in_f, math.sqrt(run.s / in_f),
                   act_dtype(run)).reshape(1, out_f, in_f)
+
+
+def gen_dy(run: Run):
+    """Upstream gradient dL/dy of the layer output, N(0, 1) in the activation dtype, [T, H]."""
+    return normal(tensor_seed(run.run_id, J_DY), run.T * run.H, 1.0, act_dtype(run)).reshape(run.T, run.H)
 
 
 def gen_all(run: Run):
