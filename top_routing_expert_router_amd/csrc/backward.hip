@@ -21,10 +21,15 @@
 //   dW2_e = dY_e^T z_e;  dW1_e = du_e^T X_e;  dW3_e = dv_e^T X_e;
 //   dl = gate Jacobian^T dg (+ training terms);  dWg = x^T dl;  dbias = sum_t dl;
 //   dx += dl Wg^T.
-// Every product here is a tiled fp32-accumulate GEMM with arbitrary strides,
-// over groups of rows (one per expert: ragged M) or of reduction indices
-// (ragged K), so that no operand needs a transposed copy; the order of every
-// sum is fixed, so results are deterministic.
+// Generic path (any dtype and shape): every product is a tiled fp32-accumulate
+// GEMM with arbitrary strides, over groups of rows (one per expert: ragged M) or
+// of reduction indices (ragged K), so that no operand needs a transposed copy,
+// and every intermediate is fp32.  Matrix-core path (bf16, H and F multiples of
+// 64): the recomputation and the two data-gradient products run on the expert
+// FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates), which takes
+// its second operand as [N][K] rows, so W2 and [W1; W3] are transposed once per
+// call; the weight gradients stay on the strided GEMM, reading the bf16
+// intermediates.  The order of every sum is fixed: results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,6 +47,8 @@ template <>
 __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
+__device__ __forceinline__ void sto(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void sto(uint16_t* p, int64_t i, float v) { p[i] = (uint16_t)f32_to_bf16_bits(v); }
 
 // ---------------------------------------------------------------------------
 // C (+)= A B per group g (blockIdx.z), fp32 accumulation in k order:
@@ -136,28 +143,33 @@ __device__ __forceinline__ float gelu_grad_f(float u) {
 }
 
 // z = act(u), or silu(u) * v; rows of the kept range only (R read on the device)
-__global__ void act_fwd_kernel(const float* __restrict__ u, const float* __restrict__ v, float* __restrict__ z,
+template <typename T>
+__global__ void act_fwd_kernel(const T* __restrict__ u, const T* __restrict__ v, T* __restrict__ z,
                                const int32_t* __restrict__ offsets, int E, int F, int act) {
   const int64_t n = (int64_t)offsets[E] * F;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const float a = u[i];
-    z[i] = act == 2 ? silu_f(a) * v[i] : (act == 0 ? (a > 0.0f ? a : 0.0f) : gelu_f(a));
+    const float a = ld(u, i);
+    sto(z, i, act == 2 ? silu_f(a) * ld(v, i) : (act == 0 ? (a > 0.0f ? a : 0.0f) : gelu_f(a)));
   }
 }
 
-// du = dz * act'(u); SwiGLU: du = dz * v * silu'(u), dv = dz * silu(u)
-__global__ void act_bwd_kernel(const float* __restrict__ dz, const float* __restrict__ u, const float* __restrict__ v,
-                               float* __restrict__ du, float* __restrict__ dv, const int32_t* __restrict__ offsets,
-                               int E, int F, int act) {
+// du = dz * act'(u); SwiGLU: du = dz * v * silu'(u), dv = dz * silu(u).  du and
+// dv rows have stride ldd (du, dv side by side in one [R][2F] buffer on the
+// matrix-core path).
+template <typename T>
+__global__ void act_bwd_kernel(const T* __restrict__ dz, const T* __restrict__ u, const T* __restrict__ v,
+                               T* __restrict__ du, T* __restrict__ dv, const int32_t* __restrict__ offsets, int E,
+                               int F, int64_t ldd, int act) {
   const int64_t n = (int64_t)offsets[E] * F;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const float a = u[i], d = dz[i];
+    const int64_t r = i / F, c = i - r * F, o = r * ldd + c;
+    const float a = ld(u, i), d = ld(dz, i);
     if (act == 2) {
       const float s = 1.0f / (1.0f + __expf(-a));
-      du[i] = d * v[i] * (s * (1.0f + a * (1.0f - s)));
-      dv[i] = d * (a * s);
+      sto(du, o, d * ld(v, i) * (s * (1.0f + a * (1.0f - s))));
+      sto(dv, o, d * (a * s));
     } else {
-      du[i] = d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a));
+      sto(du, o, d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a)));
     }
   }
 }
@@ -177,7 +189,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 template <typename TD, typename TY>
 __global__ void __launch_bounds__(256) combine_bwd_kernel(const TD* __restrict__ dy, const TY* __restrict__ Y,
                                                           const float* __restrict__ gate,
-                                                          const int32_t* __restrict__ dst, float* __restrict__ dY,
+                                                          const int32_t* __restrict__ dst, TY* __restrict__ dY,
                                                           float* __restrict__ dg, int H, int k) {
   __shared__ float red[4];
   const int t = blockIdx.x;
@@ -192,7 +204,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const TD* __restrict__
     for (int h = threadIdx.x; h < H; h += 256) {
       const float d = ld(dy, (int64_t)t * H + h);
       part = __builtin_fmaf(ld(Y, (int64_t)row * H + h), d, part);
-      dY[(int64_t)row * H + h] = g * d;
+      sto(dY, (int64_t)row * H + h, g * d);
     }
     const float s = block_sum256(part, red);
     if (threadIdx.x == 0) dg[(int64_t)t * k + r] = s;
@@ -200,14 +212,15 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const TD* __restrict__
 }
 
 // Dispatch backward: dx[t] = sum over r ascending of the kept rows of dX.
-__global__ void __launch_bounds__(256) gather_sum_kernel(const float* __restrict__ dX, const int32_t* __restrict__ dst,
+template <typename T>
+__global__ void __launch_bounds__(256) gather_sum_kernel(const T* __restrict__ dX, const int32_t* __restrict__ dst,
                                                          float* __restrict__ dx, int H, int k) {
   const int t = blockIdx.x;
   for (int h = threadIdx.x; h < H; h += 256) {
     float acc = 0.0f;
     for (int r = 0; r < k; ++r) {
       const int row = dst[(int64_t)t * k + r];
-      if (row >= 0) acc += dX[(int64_t)row * H + h];
+      if (row >= 0) acc += ld(dX, (int64_t)row * H + h);
     }
     dx[(int64_t)t * H + h] = acc;
   }
@@ -354,6 +367,25 @@ __global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ 
   if (ph == 0 && e < E) out[e] = (part[0][el] + part[1][el]) + (part[2][el] + part[3][el]);
 }
 
+// out_b[c * ldo + col0 + r] = in_b[r * C + c] for each batch b (in_b = in + b*R*C,
+// out_b = out + b*C*ldo): bf16, 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                             int R, int C, int64_t ldo, int col0) {
+  __shared__ uint16_t tile[64][65];
+  const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* ib = in + (int64_t)b * R * C;
+  uint16_t* ob = out + (int64_t)b * C * ldo;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    if (r0 + rr < R && c0 + cc < C) tile[rr][cc] = ib[(int64_t)(r0 + rr) * C + c0 + cc];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    if (r0 + rr < R && c0 + cc < C) ob[(int64_t)(c0 + cc) * ldo + col0 + r0 + rr] = tile[rr][cc];
+  }
+}
+
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.0f;
@@ -381,41 +413,131 @@ static hipError_t gemm(bool a_bf16, bool b_bf16, const GemmArgs& p, int groups, 
   return launch_gemm_generic<float, float>(p, groups, max_m, st);
 }
 
-size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max) {
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t RF = al(sizeof(float) * (size_t)R_max * (size_t)F), RH = al(sizeof(float) * (size_t)R_max * (size_t)H);
-  // u, v, z, dz, du, dv [R][F]; Y, dY, dX [R][H]; dl [T][E]; f [E]; dg [T][k]
-  return 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E) + al(sizeof(double) * (size_t)E) +
-         al(sizeof(float) * (size_t)T * (size_t)k) + 256;
+namespace {
+
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
+// dX [R][H], fp32.  Matrix-core: the same in bf16 with du and dv side by side
+// ([R][2F]), plus W2^T [E][F][H] and [W1; W3]^T [E][H][2F] (or W1^T [E][H][F]).
+// Both end with dl [T][E] fp32, f [E] binary64 and dg [T][k] fp32.
+struct BwdLayout {
+  size_t u, v, z, dz, du, Y, dY, dX, w2t, w13t, dl, f, dg, total;
+};
+
+BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast, bool gated) {
+  BwdLayout L{};
+  const size_t eb = fast ? 2 : 4;
+  const size_t RF = al256(eb * (size_t)R_max * (size_t)F), RH = al256(eb * (size_t)R_max * (size_t)H);
+  size_t o = 0;
+  L.u = o, o += RF;
+  L.v = o, o += RF;
+  L.z = o, o += RF;
+  L.dz = o, o += RF;
+  L.du = o, o += 2 * RF;  // generic: du then dv; matrix-core: [R][2F] rows
+  L.Y = o, o += RH;
+  L.dY = o, o += RH;
+  L.dX = o, o += RH;
+  L.w2t = L.w13t = o;
+  if (fast) {
+    const size_t EFH = (size_t)E * (size_t)F * (size_t)H * 2;
+    L.w2t = o, o += al256(EFH);
+    L.w13t = o, o += al256(EFH * (gated ? 2 : 1));
+  }
+  L.dl = o, o += al256(sizeof(float) * (size_t)T * (size_t)E);
+  L.f = o, o += al256(sizeof(double) * (size_t)E);
+  L.dg = o, o += al256(sizeof(float) * (size_t)T * (size_t)k);
+  L.total = o + 256;
+  return L;
+}
+
+// Router part, common to both paths: dl from dg (+ training terms), dWg, dbias,
+// dx += dl Wg^T.
+hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const float* dg, hipStream_t st) {
+  char* w = static_cast<char*>(a.ws);
+  float* dl = reinterpret_cast<float*>(w + L.dl);
+  double* f = reinterpret_cast<double*>(w + L.f);
+  const int T = a.T, H = a.H, E = a.E, k = a.k;
+  hipError_t err;
+  const bool aux = a.with_losses && a.aux_coeff != 0.0;
+  const bool zl = a.with_losses && a.z_coeff != 0.0;
+  if (aux) {
+    aux_f_kernel<<<1, 1024, 0, st>>>(a.demand, a.topk_idx, T, E, k, a.aux_mode, f);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  gate_bwd_kernel<<<T, 64, 0, st>>>(a.logits, a.topk_idx, dg, aux ? f : nullptr, dl, T, E, k, a.gate_mode, a.score_fn,
+                                    aux ? a.aux_coeff : 0.0, zl ? a.z_coeff : 0.0);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  GemmArgs g{};  // dWg[h][e] = sum_t x[t][h] dl[t][e]
+  g.A = a.x, g.sam = 1, g.sak = H;
+  g.B = dl, g.sbk = E, g.sbn = 1;
+  g.C = a.dWg, g.scm = E, g.scn = 1;
+  g.M = H, g.N = E, g.K = T;
+  if ((err = gemm(a.bf16, false, g, 1, H, st)) != hipSuccess) return err;
+  if (a.dbias) {
+    col_sum_kernel<<<(E + 63) / 64, 256, 0, st>>>(dl, a.dbias, T, E);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  GemmArgs x{};  // dx[t][h] += sum_e dl[t][e] Wg[h][e]
+  x.A = dl, x.sam = E, x.sak = 1;
+  x.B = a.Wg, x.sbk = 1, x.sbn = E;
+  x.C = a.dx, x.scm = H, x.scn = 1;
+  x.M = T, x.N = H, x.K = E;
+  x.accumulate = 1;
+  return gemm(false, false, x, 1, T, st);
+}
+
+// Weight gradients on the strided GEMM, ragged over each expert's rows:
+// dW2[e][h][f] = sum_r dY[r][h] z[r][f]; dW1[e][f][h] = sum_r du[r][f] x[row_token[r]][h]
+// (dW3 with dv).  du / dv rows have stride ldd.
+template <typename T>
+hipError_t weight_grads(const BackwardArgs& a, const T* dY, const T* z, const T* du, const T* dv, int64_t ldd,
+                        hipStream_t st) {
+  const int H = a.H, E = a.E, F = a.F;
+  constexpr bool kb = sizeof(T) == 2;
+  hipError_t err;
+  GemmArgs g{};
+  g.M = H, g.N = F;
+  g.offs = a.offsets, g.ragged = 1;
+  g.A = dY, g.sam = 1, g.sak = H;
+  g.B = z, g.sbk = F, g.sbn = 1;
+  g.C = a.dW2, g.scm = F, g.scn = 1, g.c_g = (int64_t)H * F;
+  if ((err = gemm(kb, kb, g, E, H, st)) != hipSuccess) return err;
+  GemmArgs w{};
+  w.M = F, w.N = H;
+  w.offs = a.offsets, w.ragged = 1, w.gather = a.row_token;
+  w.A = du, w.sam = 1, w.sak = ldd;
+  w.B = a.x, w.sbk = H, w.sbn = 1;
+  w.C = a.dW1, w.scm = H, w.scn = 1, w.c_g = (int64_t)F * H;
+  if ((err = gemm(kb, a.bf16, w, E, F, st)) != hipSuccess) return err;
+  if (a.act == 2) {
+    w.A = dv;
+    w.C = a.dW3;
+    if ((err = gemm(kb, a.bf16, w, E, F, st)) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool backward_fast_shape(bool bf16, int H, int F) { return bf16 && H % 64 == 0 && F % 64 == 0; }
+
+size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max, bool bf16, int act) {
+  const size_t g = bwd_layout(T, H, E, k, F, R_max, false, act == 2).total;
+  if (!backward_fast_shape(bf16, H, F)) return g;
+  const size_t f = bwd_layout(T, H, E, k, F, R_max, true, act == 2).total;
+  return f > g ? f : g;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   const int T = a.T, H = a.H, E = a.E, k = a.k, F = a.F;
   const int64_t R_max = a.R_max;
-  const bool bf = a.bf16;
-  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  char* w = static_cast<char*>(a.ws);
-  const size_t RF = al(sizeof(float) * (size_t)R_max * (size_t)F), RH = al(sizeof(float) * (size_t)R_max * (size_t)H);
-  float* u = reinterpret_cast<float*>(w);
-  float* v = reinterpret_cast<float*>(w + RF);
-  float* z = reinterpret_cast<float*>(w + 2 * RF);
-  float* dz = reinterpret_cast<float*>(w + 3 * RF);
-  float* du = reinterpret_cast<float*>(w + 4 * RF);
-  float* dv = reinterpret_cast<float*>(w + 5 * RF);
-  float* Y = reinterpret_cast<float*>(w + 6 * RF);
-  float* dY = reinterpret_cast<float*>(w + 6 * RF + RH);
-  float* dX = reinterpret_cast<float*>(w + 6 * RF + 2 * RH);
-  float* dl = reinterpret_cast<float*>(w + 6 * RF + 3 * RH);
-  double* f = reinterpret_cast<double*>(w + 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E));
-  float* dgw = reinterpret_cast<float*>(w + 6 * RF + 3 * RH + al(sizeof(float) * (size_t)T * (size_t)E) +
-                                        al(sizeof(double) * (size_t)E));
-  const bool gated = a.act == 2;
+  const bool bf = a.bf16, gated = a.act == 2;
   hipError_t err = hipSuccess;
-#define MOE_BW(call)                                \
-  do {                                              \
-    if ((err = (call)) != hipSuccess) return err;   \
+#define MOE_BW(call)                              \
+  do {                                            \
+    if ((err = (call)) != hipSuccess) return err; \
   } while (0)
-
   if (T == 0) {  // no tokens: every gradient is zero
     auto zero = [&](float* q, int64_t n) {
       if (q && n > 0) zero_f32_kernel<<<grid_1d(n, 256), 256, 0, st>>>(q, n);
@@ -428,7 +550,74 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     MOE_BW(zero(a.dW2, (int64_t)E * H * F));
     return hipSuccess;
   }
-  const int mr = (int)(R_max < INT32_MAX ? R_max : INT32_MAX);  // rows bound for the ragged-M grids
+  const BwdLayout L = bwd_layout(T, H, E, k, F, R_max, a.fast, gated);
+  char* w = static_cast<char*>(a.ws);
+  float* dgw = reinterpret_cast<float*>(w + L.dg);
+  float* dg = a.dg ? a.dg : dgw;
+  const int mr = (int)(R_max < INT32_MAX ? R_max : INT32_MAX);  // rows bound of the ragged-M grids
+
+  if (a.fast) {
+    uint16_t* u = reinterpret_cast<uint16_t*>(w + L.u);
+    uint16_t* v = reinterpret_cast<uint16_t*>(w + L.v);
+    uint16_t* z = reinterpret_cast<uint16_t*>(w + L.z);
+    uint16_t* dz = reinterpret_cast<uint16_t*>(w + L.dz);
+    uint16_t* dcat = reinterpret_cast<uint16_t*>(w + L.du);  // [R][2F]: du | dv (or [R][F])
+    uint16_t* Y = reinterpret_cast<uint16_t*>(w + L.Y);
+    uint16_t* dY = reinterpret_cast<uint16_t*>(w + L.dY);
+    uint16_t* dX = reinterpret_cast<uint16_t*>(w + L.dX);
+    uint16_t* w2t = reinterpret_cast<uint16_t*>(w + L.w2t);
+    uint16_t* w13t = reinterpret_cast<uint16_t*>(w + L.w13t);
+    const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
+    const int64_t rc = a.rows_cap;
+    if (R_max > 0) {
+      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T, z, Y = z W2^T
+      MOE_BW(launch_grouped_gemm_bf16(a.x, a.W1, u, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+      if (gated) MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+      act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
+      MOE_BW(hipGetLastError());
+      MOE_BW(launch_grouped_gemm_bf16(z, a.W2, Y, a.offsets, E, H, F, R_max, rc, true, st));
+      // the second operands of the data-gradient products as [N][K] rows
+      transpose_bf16_kernel<<<dim3((F + 63) / 64, (H + 63) / 64, E), 256, 0, st>>>(
+          static_cast<const uint16_t*>(a.W2), w2t, H, F, H, 0);  // W2_e [H][F] -> [F][H]
+      MOE_BW(hipGetLastError());
+      transpose_bf16_kernel<<<dim3((H + 63) / 64, (F + 63) / 64, E), 256, 0, st>>>(
+          static_cast<const uint16_t*>(a.W1), w13t, F, H, KC, 0);  // W1_e [F][H] -> [H][F] at column 0
+      MOE_BW(hipGetLastError());
+      if (gated) {
+        transpose_bf16_kernel<<<dim3((H + 63) / 64, (F + 63) / 64, E), 256, 0, st>>>(
+            static_cast<const uint16_t*>(a.W3), w13t, F, H, KC, F);  // W3_e -> columns F .. 2F-1
+        MOE_BW(hipGetLastError());
+      }
+    }
+    combine_bwd_kernel<uint16_t, uint16_t><<<T, 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), Y, a.topk_gate,
+                                                              a.dst_row, dY, dg, H, k);
+    MOE_BW(hipGetLastError());
+    if (R_max > 0) {
+      MOE_BW(launch_grouped_gemm_bf16(dY, w2t, dz, a.offsets, E, F, H, R_max, rc, true, st));  // dz = dY W2
+      act_bwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(dz, u, v, dcat, dcat + F, a.offsets, E, F,
+                                                                         KC, a.act);
+      MOE_BW(hipGetLastError());
+      MOE_BW(launch_grouped_gemm_bf16(dcat, w13t, dX, a.offsets, E, H, KC, R_max, rc, true, st));  // dX
+      gather_sum_kernel<uint16_t><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
+      MOE_BW(hipGetLastError());
+    } else {
+      zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
+      MOE_BW(hipGetLastError());
+    }
+    MOE_BW(weight_grads<uint16_t>(a, dY, z, dcat, dcat + F, KC, st));
+    MOE_BW(router_backward(a, L, dg, st));
+    return hipSuccess;
+  }
+
+  float* u = reinterpret_cast<float*>(w + L.u);
+  float* v = reinterpret_cast<float*>(w + L.v);
+  float* z = reinterpret_cast<float*>(w + L.z);
+  float* dz = reinterpret_cast<float*>(w + L.dz);
+  float* du = reinterpret_cast<float*>(w + L.du);
+  float* dv = du + (size_t)R_max * F;
+  float* Y = reinterpret_cast<float*>(w + L.Y);
+  float* dY = reinterpret_cast<float*>(w + L.dY);
+  float* dX = reinterpret_cast<float*>(w + L.dX);
   if (R_max > 0) {
     // 1. u = x[row_token] W1^T, v = x[row_token] W3^T (per expert, the kept rows)
     GemmArgs g{};
@@ -447,7 +636,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       MOE_BW(gemm(bf, bf, g, E, mr, st));
     }
     // 2. z = act(u) (or silu(u) v)
-    act_fwd_kernel<<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
+    act_fwd_kernel<float><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
     MOE_BW(hipGetLastError());
     // 3. Y = z W2^T
     GemmArgs y{};
@@ -462,7 +651,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     MOE_BW(gemm(false, bf, y, E, mr, st));
   }
   // 4. combine backward: dY (kept rows), dg
-  float* dg = a.dg ? a.dg : dgw;
   if (bf)
     combine_bwd_kernel<uint16_t, float><<<T, 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), Y, a.topk_gate,
                                                            a.dst_row, dY, dg, H, k);
@@ -483,7 +671,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     g.offs = a.offsets, g.ragged = 0;
     MOE_BW(gemm(false, bf, g, E, mr, st));
     // 6. du (, dv)
-    act_bwd_kernel<<<grid_1d(R_max * F, 256), 256, 0, st>>>(dz, u, v, du, dv, a.offsets, E, F, a.act);
+    act_bwd_kernel<float><<<grid_1d(R_max * F, 256), 256, 0, st>>>(dz, u, v, du, dv, a.offsets, E, F, F, a.act);
     MOE_BW(hipGetLastError());
     // 7. dX = du W1 (+ dv W3)  (W1 [E][F][H]: B(k = f, n = h))
     GemmArgs x{};
@@ -502,67 +690,15 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       x.accumulate = 1;
       MOE_BW(gemm(false, bf, x, E, mr, st));
     }
-  }
-  // 8. dx = sum of the token's kept rows of dX
-  if (R_max > 0)
-    gather_sum_kernel<<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
-  else
+    // 8. dx = sum of the token's kept rows of dX
+    gather_sum_kernel<float><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
+  } else {
     zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
+  }
   MOE_BW(hipGetLastError());
-  // 9. weight gradients, ragged over each expert's rows
-  {
-    GemmArgs g{};
-    g.M = H, g.N = F, g.K = 0;
-    g.offs = a.offsets, g.ragged = 1;
-    // dW2[e][h][f] = sum_r dY[r][h] z[r][f]
-    g.A = dY, g.sam = 1, g.sak = H;
-    g.B = z, g.sbk = F, g.sbn = 1;
-    g.C = a.dW2, g.scm = F, g.scn = 1, g.c_g = (int64_t)H * F;
-    MOE_BW(gemm(false, false, g, E, H, st));
-    // dW1[e][f][h] = sum_r du[r][f] x[row_token[r]][h]  (dW3 with dv)
-    GemmArgs w1{};
-    w1.M = F, w1.N = H, w1.K = 0;
-    w1.offs = a.offsets, w1.ragged = 1, w1.gather = a.row_token;
-    w1.A = du, w1.sam = 1, w1.sak = F;
-    w1.B = a.x, w1.sbk = H, w1.sbn = 1;
-    w1.C = a.dW1, w1.scm = H, w1.scn = 1, w1.c_g = (int64_t)F * H;
-    MOE_BW(gemm(false, bf, w1, E, F, st));
-    if (gated) {
-      w1.A = dv;
-      w1.C = a.dW3;
-      MOE_BW(gemm(false, bf, w1, E, F, st));
-    }
-  }
-  // 10. router: dl = gate Jacobian^T dg (+ training terms)
-  const bool terms = a.with_losses && (a.aux_coeff != 0.0 || a.z_coeff != 0.0);
-  if (terms && a.aux_coeff != 0.0) {
-    aux_f_kernel<<<1, 1024, 0, st>>>(a.demand, a.topk_idx, T, E, k, a.aux_mode, f);
-    MOE_BW(hipGetLastError());
-  }
-  float* dlo = dl;
-  gate_bwd_kernel<<<T, 64, 0, st>>>(a.logits, a.topk_idx, dg, (terms && a.aux_coeff != 0.0) ? f : nullptr, dlo, T, E,
-                                    k, a.gate_mode, a.score_fn, terms ? a.aux_coeff : 0.0, terms ? a.z_coeff : 0.0);
-  MOE_BW(hipGetLastError());
-  // 11. dWg = x^T dl, dbias = sum_t dl, dx += dl Wg^T
-  {
-    GemmArgs g{};
-    g.A = a.x, g.sam = 1, g.sak = H;
-    g.B = dlo, g.sbk = E, g.sbn = 1;
-    g.C = a.dWg, g.scm = E, g.scn = 1;
-    g.M = H, g.N = E, g.K = T;
-    MOE_BW(gemm(bf, false, g, 1, H, st));
-    if (a.dbias) {
-      col_sum_kernel<<<(E + 63) / 64, 256, 0, st>>>(dlo, a.dbias, T, E);
-      MOE_BW(hipGetLastError());
-    }
-    GemmArgs x{};
-    x.A = dlo, x.sam = E, x.sak = 1;
-    x.B = a.Wg, x.sbk = 1, x.sbn = E;
-    x.C = a.dx, x.scm = H, x.scn = 1;
-    x.M = T, x.N = H, x.K = E;
-    x.accumulate = 1;
-    MOE_BW(gemm(false, false, x, 1, T, st));
-  }
+  // 9. weight gradients; 10-11. router
+  MOE_BW(weight_grads<float>(a, dY, z, du, dv, F, st));
+  MOE_BW(router_backward(a, L, dg, st));
 #undef MOE_BW
   return hipSuccess;
 }

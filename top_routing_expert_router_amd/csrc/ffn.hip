@@ -1163,4 +1163,11 @@ hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, cons
   return launch_one<EPI_NONE>(vec, bf16, h, W2, nullptr, Y, offsets, E, H, F, R_max, rows_cap, st);
 }
 
+hipError_t launch_grouped_gemm_bf16(const void* A, const void* B, void* C, const int32_t* offsets, int E, int N, int K,
+                                    int64_t R_max, int64_t rows_cap, bool vec, hipStream_t st, const int32_t* gather,
+                                    int xrows) {
+  if (R_max == 0) return hipSuccess;
+  return launch_one<EPI_NONE>(vec, true, A, B, nullptr, C, offsets, E, N, K, R_max, rows_cap, st, gather, xrows);
+}
+
 }  // namespace moe

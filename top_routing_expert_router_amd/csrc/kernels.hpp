@@ -147,8 +147,9 @@ struct GemmArgs {
 
 struct BackwardArgs {
   int T, H, E, k, F, act, gate_mode, score_fn, aux_mode;
-  int64_t R_max;
+  int64_t R_max, rows_cap;
   bool bf16;
+  bool fast;  // matrix-core path (backward_fast_shape and 16-byte aligned buffers)
   bool with_losses;
   double aux_coeff, z_coeff;
   const void* x;
@@ -160,7 +161,15 @@ struct BackwardArgs {
   float *dx, *dWg, *dbias, *dW1, *dW3, *dW2, *dg;  // dbias, dg optional
   void* ws;
 };
-size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max);
+// C[r] = A[r] . B_e^T for the rows r of expert e (B_e = B + e*N*K, [N][K] row-major),
+// bf16 in and out, fp32 accumulation: the grouped GEMM of the expert FFN with no
+// epilogue (A's row through gather when given: then A has xrows rows).
+hipError_t launch_grouped_gemm_bf16(const void* A, const void* B, void* C, const int32_t* offsets, int E, int N, int K,
+                                    int64_t R_max, int64_t rows_cap, bool vec, hipStream_t st,
+                                    const int32_t* gather = nullptr, int xrows = 0);
+// the matrix-core path of the backward: bf16, H and F multiples of 64
+bool backward_fast_shape(bool bf16, int H, int F);
+size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max, bool bf16, int act);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
 
 }  // namespace moe

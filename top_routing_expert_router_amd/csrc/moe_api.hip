@@ -201,7 +201,7 @@ size_t moe_workspace_bytes(const moe_config* c) {
 
 size_t moe_backward_workspace_bytes(const moe_config* c) {
   if (moe_validate(c) != MOE_OK) return 0;
-  return moe::backward_workspace_bytes(c->T, c->H, c->E, c->k, c->F, max_rows_of(c));
+  return moe::backward_workspace_bytes(c->T, c->H, c->E, c->k, c->F, max_rows_of(c), c->dtype == MOE_BF16, c->act);
 }
 
 const char* moe_status_str(moe_status s) {
@@ -496,7 +496,11 @@ moe_status moe_backward(const moe_config* c, const void* x, const float* Wg, con
   a.T = c->T, a.H = c->H, a.E = c->E, a.k = c->k, a.F = c->F;
   a.act = c->act, a.gate_mode = c->gate_mode, a.score_fn = c->score_fn, a.aux_mode = c->aux_mode;
   a.R_max = max_rows_of(c);
+  a.rows_cap = expert_rows_cap(c, a.R_max);
   a.bf16 = c->dtype == MOE_BF16;
+  // the matrix-core path reads x, the weights and its workspace 16 bytes at a time
+  a.fast = moe::backward_fast_shape(a.bf16, c->H, c->F) && aligned16(x) && aligned16(W1) && aligned16(W3) &&
+           aligned16(W2) && aligned16(ws);
   a.with_losses = plan->losses != nullptr;
   a.aux_coeff = c->aux_coeff, a.z_coeff = c->z_coeff;
   a.x = x, a.Wg = Wg, a.W1 = W1, a.W3 = W3, a.W2 = W2;
