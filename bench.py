@@ -394,7 +394,7 @@ def main():
     # Extra measurements (cold stages, training terms, routing variants, shared
     # expert) are skipped with --core-only, which the profiler runs use so that
     # every launch they record belongs to the routed layer.
-    stage_cold_us, losses_us, variants, shared_out, cold_sets = None, None, None, None, None
+    stage_cold_us, losses_us, variants, shared_out, cold_sets, backward_out = None, None, None, None, None, None
     if not args.core_only:
         # cold: the stage runs back to back over rotating copies of its buffers, as many
         # sets as make 1 GiB of traffic per rotation (four times the 256 MB Infinity
@@ -469,6 +469,39 @@ def main():
                       "tokens_per_s": round(run.T / (fwd_s_us * 1e-6), 1), "shared_ffn_us": round(shared_ffn_us, 2),
                       "shared_ffn_tflops": round(shared_flops / (shared_ffn_us * 1e-6) / 1e12, 1)}
         del ws_s, Ys, sws
+
+        # ---- backward (moe_backward): the gradients in x, Wg, bias and the expert
+        # weights (fp32) for an upstream gradient dy, the routing held fixed; it
+        # recomputes the forward's activations.  Its floor: the weights of the
+        # non-empty experts read once and the fp32 weight gradients written once.
+        plan_b = dict(plan)
+        plan_b["logits"] = torch.empty((run.T, run.E), dtype=torch.float32, device=dev)
+        B.route(cfg, x, wg, bias, plan_b, ws)
+        dy = up(recipes.gen_dy(run))
+        grads = B.alloc_grads(cfg, dev)
+        bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=dev)
+        nb = max(2, min(args.steps, 10))
+        B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(nb):
+            B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_us = e0.elapsed_time(e1) / nb * 1e3
+        kept_b = plan["kept"].cpu().numpy()
+        R_b = int(kept_b.sum())
+        bwd_bytes = (int((kept_b > 0).sum()) * run.m * run.H * run.F * eb + run.E * run.m * run.H * run.F * 4 +
+                     3.0 * run.T * run.H * eb)
+        bwd_flops = 2 * 2.0 * R_b * run.H * run.F * run.m  # data and weight gradients (no recomputation)
+        backward_out = {"ms": round(bwd_us / 1e3, 4), "tokens_per_s": round(run.T / (bwd_us * 1e-6), 1),
+                        "calls": nb, "floor_bytes": bwd_bytes, "hbm_frac": round(bwd_bytes / (bwd_us * 1e-6) / 8e12, 4),
+                        "gradient_tflops": round(bwd_flops / (bwd_us * 1e-6) / 1e12, 1),
+                        "workspace_GiB": round(bws.numel() / 2 ** 30, 2),
+                        "note": "fp32 gradients of x, Wg, bias, W1, W3, W2; activations recomputed from x"}
+        log(f"[bench] backward: {bwd_us / 1e3:.2f} ms ({backward_out['hbm_frac']:.3f} of the HBM floor)")
+        del grads, bws, dy
 
         variants = {}
         for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
@@ -581,6 +614,7 @@ def main():
         "router_training_terms": losses_us,
         "routing_variants": variants,
         "shared_expert": shared_out,
+        "backward": backward_out,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

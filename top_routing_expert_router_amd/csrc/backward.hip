@@ -368,22 +368,172 @@ __global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ 
 }
 
 // out_b[c * ldo + col0 + r] = in_b[r * C + c] for each batch b (in_b = in + b*R*C,
-// out_b = out + b*C*ldo): bf16, 64 x 64 tiles through LDS.
+// out_b = out + b*C*ldo): bf16, 64 x 64 tiles through LDS, 16-byte loads and
+// stores (R, C, ldo and col0 multiples of 8; 16-byte aligned buffers).
 __global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
                                                              int R, int C, int64_t ldo, int col0) {
-  __shared__ uint16_t tile[64][65];
+  __shared__ uint16_t tile[64][72];  // 144-byte rows: the 8 rows a column read spans hit different banks
   const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const uint16_t* ib = in + (int64_t)b * R * C;
   uint16_t* ob = out + (int64_t)b * C * ldo;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // 64 rows x 8 chunks of 8 columns
+    const int p = threadIdx.x + 256 * q, rr = p >> 3, ch = p & 7;
+    if (r0 + rr < R && c0 + 8 * ch < C) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ib + (int64_t)(r0 + rr) * C + c0 + 8 * ch);
+      *reinterpret_cast<u32x4_t*>(&tile[rr][8 * ch]) = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // 64 output rows (input columns) x 8 chunks of 8 input rows
+    const int p = threadIdx.x + 256 * q, cc = p >> 3, ch = p & 7;
+    if (c0 + cc < C && r0 + 8 * ch < R) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)tile[8 * ch + 2 * j][cc] | ((uint32_t)tile[8 * ch + 2 * j + 1][cc] << 16);
+      *reinterpret_cast<u32x4_t*>(ob + (int64_t)(c0 + cc) * ldo + col0 + r0 + 8 * ch) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradients on the matrix cores.  dW_e = A_e B_e^T where A_e and B_e are
+// the expert's rows of two activations, transposed: each operand row holds one
+// feature over the expert's rows, in a column segment that starts at poff[e]
+// and is padded with zeros to a multiple of 64 (so the reduction runs in whole
+// 64-wide stages of 128-byte rows, the grouped GEMM's stage shape).
+// ---------------------------------------------------------------------------
+
+// poff[e] = sum over e' < e of the expert's rows rounded up to 64; poff[E] = total.
+__global__ void __launch_bounds__(1024) seg_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           int32_t* __restrict__ poff) {
+  __shared__ int tmp[1024 / 64 + 1];
+  const int e = threadIdx.x;
+  const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int total;
+  const int ex = block_exclusive_scan((rows + 63) / 64 * 64, tmp, &total);
+  if (e < E) poff[e] = ex;
+  if (e == 0) poff[E] = total;
+}
+
+// out[c * ldo + poff[e] + (r - offsets[e])] = in[row(r) * ldi + ci + c] for the kept
+// rows r of expert e (row(r) = gather[r] when given), 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256) seg_transpose_kernel(const uint16_t* __restrict__ in, int64_t ldi, int ci,
+                                                            const int32_t* __restrict__ gather,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ poff, int E, int C,
+                                                            uint16_t* __restrict__ out, int64_t ldo) {
+  __shared__ uint16_t tile[64][65];
+  __shared__ int col[64];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int R = offsets[E];
+  if (r0 >= R) return;
+  if (threadIdx.x < 64) {  // destination column of each row of the tile
+    const int r = r0 + threadIdx.x;
+    int c = -1;
+    if (r < R) {
+      int lo = 0, hi = E;  // last expert with offsets[e] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      c = poff[lo] + (r - offsets[lo]);
+    }
+    col[threadIdx.x] = c;
+  }
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int rr = i / 64, cc = i % 64;
-    if (r0 + rr < R && c0 + cc < C) tile[rr][cc] = ib[(int64_t)(r0 + rr) * C + c0 + cc];
+    const int r = r0 + rr;
+    if (r < R && c0 + cc < C) {
+      const int64_t src = gather ? (int64_t)gather[r] : (int64_t)r;
+      tile[rr][cc] = in[src * ldi + ci + c0 + cc];
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int cc = i / 64, rr = i % 64;
-    if (r0 + rr < R && c0 + cc < C) ob[(int64_t)(c0 + cc) * ldo + col0 + r0 + rr] = tile[rr][cc];
+    if (col[rr] >= 0 && c0 + cc < C) out[(int64_t)(c0 + cc) * ldo + col[rr]] = tile[rr][cc];
   }
+}
+
+__global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// C_e[m][n] = sum_k A[m][poff[e] + k] B[n][poff[e] + k], k < poff[e+1] - poff[e]
+// (fp32 accumulation, fp32 out, C_e = C + e * M * N).  128 x 128 tiles, 4 waves
+// as 2 x 2 (each 2 x 2 fragments of v_mfma_f32_32x32x16_bf16), 64-wide k stages
+// of 128-byte rows in two LDS buffers filled by direct-to-LDS loads (chunk c of
+// row r at slot c ^ ((r >> 1) & 7)).  Rows past M or N read row M-1 / N-1 and
+// are not stored.
+__global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ B, float* __restrict__ C,
+                                                         const int32_t* __restrict__ poff, int M, int N, int64_t ld) {
+  constexpr int BM = 128, BN = 128, ROWS = BM + BN, STAGE = ROWS * 64;
+  __shared__ __align__(16) uint16_t smem[2 * STAGE];
+  const int e = blockIdx.z, m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int kb = poff[e], nk = (poff[e + 1] - kb) / 64;
+  auto lds_pos = [](int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; };
+  // this thread's 8 pieces per stage: piece p = q * 256 + tid -> row p / 8, LDS slot p % 8
+  const uint16_t* src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int p = q * 256 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+    const int64_t row = r < BM ? (int64_t)min(m0 + r, M - 1) : (int64_t)min(n0 + r - BM, N - 1);
+    src[q] = (r < BM ? A : B) + row * ld + kb + c * 8;
+  }
+  auto issue = [&](int buf, int j) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds(src[q] + j * 64, smem + buf * STAGE + (q * 4 + w) * 512, 16, 0, 0);
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  if (nk > 0) issue(0, 0);
+  for (int j = 0; j < nk; ++j) {
+    wait_vmcnt<0>();
+    __syncthreads();  // stage j is in LDS and every wave is done with stage j - 1
+    if (j + 1 < nk) issue((j + 1) & 1, j + 1);
+    const uint16_t* st = smem + (j & 1) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(wm * 64 + i * 32 + (lane & 31), c));
+        b[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(BM + wn * 64 + i * 32 + (lane & 31), c));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+    }
+  }
+  // accumulator element 4g + q of lane l: row 8g + 4(l / 32) + q of the A fragment, column l % 32
+  float* Ce = C + (int64_t)e * M * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + q;
+          const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
+          if (m < M && n < N) Ce[(int64_t)m * N + n] = acc[i][jj][4 * g + q];
+        }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
@@ -422,7 +572,8 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 // ([R][2F]), plus W2^T [E][F][H] and [W1; W3]^T [E][H][2F] (or W1^T [E][H][F]).
 // Both end with dl [T][E] fp32, f [E] binary64 and dg [T][k] fp32.
 struct BwdLayout {
-  size_t u, v, z, dz, du, Y, dY, dX, w2t, w13t, dl, f, dg, total;
+  size_t u, v, z, dz, du, Y, dY, dX, w2t, w13t, poff, dyt, zt, dt, xt, dl, f, dg, total;
+  int64_t ldt;  // row stride of the transposed activations (rows of each expert padded to 64)
 };
 
 BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast, bool gated) {
@@ -438,11 +589,20 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.Y = o, o += RH;
   L.dY = o, o += RH;
   L.dX = o, o += RH;
-  L.w2t = L.w13t = o;
+  L.w2t = L.w13t = L.poff = L.dyt = L.zt = L.dt = L.xt = o;
+  L.ldt = (R_max + 63 * (int64_t)E + 63) / 64 * 64;
   if (fast) {
     const size_t EFH = (size_t)E * (size_t)F * (size_t)H * 2;
+    const size_t KC = gated ? 2 * (size_t)F : (size_t)F, ld = (size_t)L.ldt;
     L.w2t = o, o += al256(EFH);
     L.w13t = o, o += al256(EFH * (gated ? 2 : 1));
+    L.poff = o, o += al256(sizeof(int32_t) * ((size_t)E + 1));
+    // dY^T [H], z^T [F], [du | dv]^T [KC], x^T [H] rows of ldt, contiguous (zeroed together)
+    L.dyt = o;
+    L.zt = L.dyt + 2 * (size_t)H * ld;
+    L.dt = L.zt + 2 * (size_t)F * ld;
+    L.xt = L.dt + 2 * KC * ld;
+    o = al256(L.xt + 2 * (size_t)H * ld);
   }
   L.dl = o, o += al256(sizeof(float) * (size_t)T * (size_t)E);
   L.f = o, o += al256(sizeof(double) * (size_t)E);
@@ -604,7 +764,41 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
       MOE_BW(hipGetLastError());
     }
-    MOE_BW(weight_grads<uint16_t>(a, dY, z, dcat, dcat + F, KC, st));
+    // weight gradients on the matrix cores: the expert's rows of dY, z, [du | dv]
+    // and x transposed into zero-padded 64-aligned column segments
+    int32_t* poff = reinterpret_cast<int32_t*>(w + L.poff);
+    uint16_t* dyt = reinterpret_cast<uint16_t*>(w + L.dyt);
+    uint16_t* zt = reinterpret_cast<uint16_t*>(w + L.zt);
+    uint16_t* dt = reinterpret_cast<uint16_t*>(w + L.dt);
+    uint16_t* xt = reinterpret_cast<uint16_t*>(w + L.xt);
+    const int64_t ld = L.ldt;
+    seg_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, E, poff);
+    MOE_BW(hipGetLastError());
+    const int64_t nt = (2 * (int64_t)H + F + KC) * ld;
+    zero_u16_kernel<<<grid_1d(nt, 256), 256, 0, st>>>(dyt, nt);
+    MOE_BW(hipGetLastError());
+    if (R_max > 0) {
+      const unsigned gy = (unsigned)((R_max + 63) / 64);
+      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(dY, H, 0, nullptr, a.offsets, poff, E, H, dyt, ld);
+      MOE_BW(hipGetLastError());
+      seg_transpose_kernel<<<dim3((F + 63) / 64, gy), 256, 0, st>>>(z, F, 0, nullptr, a.offsets, poff, E, F, zt, ld);
+      MOE_BW(hipGetLastError());
+      seg_transpose_kernel<<<dim3((KC + 63) / 64, gy), 256, 0, st>>>(dcat, KC, 0, nullptr, a.offsets, poff, E, KC, dt,
+                                                                     ld);
+      MOE_BW(hipGetLastError());
+      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(static_cast<const uint16_t*>(a.x), H, 0,
+                                                                    a.row_token, a.offsets, poff, E, H, xt, ld);
+      MOE_BW(hipGetLastError());
+    }
+    wgrad_mfma_kernel<<<dim3((F + 127) / 128, (H + 127) / 128, E), 256, 0, st>>>(dyt, zt, a.dW2, poff, H, F, ld);
+    MOE_BW(hipGetLastError());
+    wgrad_mfma_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(dt, xt, a.dW1, poff, F, H, ld);
+    MOE_BW(hipGetLastError());
+    if (gated) {
+      wgrad_mfma_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(dt + (int64_t)F * ld, xt, a.dW3,
+                                                                                    poff, F, H, ld);
+      MOE_BW(hipGetLastError());
+    }
     MOE_BW(router_backward(a, L, dg, st));
     return hipSuccess;
   }
