@@ -223,6 +223,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the brief runs of the other workloads")
     ap.add_argument("--core-only", action="store_true",
                     help="skip the extra measurements (for profiler runs: only the routed layer's launches)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="route once, then time moe_backward alone (--steps calls after one warm-up call)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 256 MiB (the PMC byte-counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DB", help="print the kernel summary of a rocprofv3 database")
@@ -298,6 +300,11 @@ def main():
     ws = B.alloc_workspace(cfg, dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s: {workload}, R_max={rmax}, ws={ws.numel() / 2**20:.1f} MiB")
+
+    if args.backward_only:
+        out = measure_backward(run, cfg, dev, up, x, wg, bias, w1, w3, w2, plan, ws, max(1, args.steps))
+        print(json.dumps({"workload": workload, "backward": out}), flush=True)
+        return
 
     def step():
         B.forward(cfg, x, wg, bias, w1, w3, w2, x, y, plan, X, Y, ws)
@@ -470,38 +477,8 @@ def main():
                       "shared_ffn_tflops": round(shared_flops / (shared_ffn_us * 1e-6) / 1e12, 1)}
         del ws_s, Ys, sws
 
-        # ---- backward (moe_backward): the gradients in x, Wg, bias and the expert
-        # weights (fp32) for an upstream gradient dy, the routing held fixed; it
-        # recomputes the forward's activations.  Its floor: the weights of the
-        # non-empty experts read once and the fp32 weight gradients written once.
-        plan_b = dict(plan)
-        plan_b["logits"] = torch.empty((run.T, run.E), dtype=torch.float32, device=dev)
-        B.route(cfg, x, wg, bias, plan_b, ws)
-        dy = up(recipes.gen_dy(run))
-        grads = B.alloc_grads(cfg, dev)
-        bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=dev)
-        nb = max(2, min(args.steps, 10))
-        B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(nb):
-            B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
-        e1.record()
-        torch.cuda.synchronize()
-        bwd_us = e0.elapsed_time(e1) / nb * 1e3
-        kept_b = plan["kept"].cpu().numpy()
-        R_b = int(kept_b.sum())
-        bwd_bytes = (int((kept_b > 0).sum()) * run.m * run.H * run.F * eb + run.E * run.m * run.H * run.F * 4 +
-                     3.0 * run.T * run.H * eb)
-        bwd_flops = 2 * 2.0 * R_b * run.H * run.F * run.m  # data and weight gradients (no recomputation)
-        backward_out = {"ms": round(bwd_us / 1e3, 4), "tokens_per_s": round(run.T / (bwd_us * 1e-6), 1),
-                        "calls": nb, "floor_bytes": bwd_bytes, "hbm_frac": round(bwd_bytes / (bwd_us * 1e-6) / 8e12, 4),
-                        "gradient_tflops": round(bwd_flops / (bwd_us * 1e-6) / 1e12, 1),
-                        "workspace_GiB": round(bws.numel() / 2 ** 30, 2),
-                        "note": "fp32 gradients of x, Wg, bias, W1, W3, W2; activations recomputed from x"}
-        log(f"[bench] backward: {bwd_us / 1e3:.2f} ms ({backward_out['hbm_frac']:.3f} of the HBM floor)")
-        del grads, bws, dy
+        backward_out = measure_backward(run, cfg, dev, up, x, wg, bias, w1, w3, w2, plan, ws,
+                                        max(2, min(args.steps, 10)))
 
         variants = {}
         for name, kw in (("position", {}), ("probs", {"drop_policy": 1}), ("sigmoid", {"score_fn": 1})):
@@ -623,6 +600,47 @@ def main():
         log("[bench] extra workloads: " + ", ".join(f"{n}={v['ms_per_step']:.3f} ms" for n, v in
                                                      out["extra_workloads"].items()))
     print(json.dumps(out), flush=True)
+
+
+def measure_backward(run, cfg, dev, up, x, wg, bias, w1, w3, w2, plan, ws, calls):
+    """moe_backward: the fp32 gradients in x, Wg, bias and the expert weights for an
+    upstream gradient dy, the routing held fixed (it recomputes the forward's
+    activations).  Routes once (with logits), then one warm-up call and `calls` timed
+    calls.  Its floor: the weights of the non-empty experts read once and the fp32
+    weight gradients written once (plus x, dy and dx)."""
+    import torch
+
+    from top_routing_expert_router_amd import binding as B
+    from top_routing_expert_router_amd.synth import recipes
+
+    eb = run.elem_bytes
+    plan_b = dict(plan)
+    plan_b["logits"] = torch.empty((run.T, run.E), dtype=torch.float32, device=dev)
+    B.route(cfg, x, wg, bias, plan_b, ws)
+    dy = up(recipes.gen_dy(run))
+    grads = B.alloc_grads(cfg, dev)
+    bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=dev)
+    B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / calls * 1e3
+    kept = plan_b["kept"].cpu().numpy()
+    R = int(kept.sum())
+    floor = (int((kept > 0).sum()) * run.m * run.H * run.F * eb + run.E * run.m * run.H * run.F * 4 +
+             3.0 * run.T * run.H * eb)
+    flops = 2 * 2.0 * R * run.H * run.F * run.m  # data and weight gradients (no recomputation)
+    out = {"ms": round(us / 1e3, 4), "tokens_per_s": round(run.T / (us * 1e-6), 1), "calls": calls,
+           "floor_bytes": floor, "hbm_frac": round(floor / (us * 1e-6) / 8e12, 4),
+           "gradient_tflops": round(flops / (us * 1e-6) / 1e12, 1), "workspace_GiB": round(bws.numel() / 2 ** 30, 2),
+           "note": "fp32 gradients of x, Wg, bias, W1, W3, W2; activations recomputed from x"}
+    log(f"[bench] backward: {us / 1e3:.2f} ms ({out['hbm_frac']:.3f} of the HBM floor)")
+    del grads, bws, dy
+    return out
 
 
 def extra_workload(name, steps, warmup):
