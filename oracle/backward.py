@@ -37,7 +37,7 @@ def _f64(a, dtype=None):
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+    return a.astype(np.float64, copy=False)
 
 
 def _silu(z):

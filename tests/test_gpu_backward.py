@@ -187,3 +187,90 @@ def test_backward_empty_batch_and_refusals(gpu):
         B.backward(cfg2, U.dev(d["x"], gpu), U.dev(d["wg"], gpu), U.dev(d["w1"], gpu), None, U.dev(d["w2"], gpu),
                    B.alloc_plan(cfg2, gpu, logits=True), U.dev(recipes.gen_dy(r2), gpu), B.alloc_grads(cfg2, gpu),
                    torch.empty(16, dtype=torch.uint8, device=gpu))
+
+
+@pytest.mark.parametrize("name", ["2", "4", "5"])
+def test_backward_full_size_sampled(gpu, name):
+    """Full-size runs: the weight gradients of the largest, a median and the smallest
+    non-empty expert (the oracle on exactly those experts' rows) and of an empty expert
+    (exactly zero), and dx, dg of 64 sampled tokens (expert and router paths: the oracle
+    takes each token's choices one by one).  The router weight and bias gradients need
+    every token's expert outputs and are compared at the reduced sizes above."""
+    import torch
+
+    r = recipes.RUNS[name]
+    cfg = B.MoEConfig.from_run(r)
+    x_h = recipes.gen_x(r)
+    wg_h, bias_h = recipes.gen_router(r)
+    dy_h = recipes.gen_dy(r)
+    x, wg, dy = U.dev(x_h, gpu), U.dev(wg_h, gpu), U.dev(dy_h, gpu)
+    names = ("w1", "w3", "w2") if r.act == recipes.SWIGLU else ("w1", "w2")
+    w = {n: U.upload_expert_weight(r, n, gpu)[0] for n in names}
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    B.route(cfg, x, wg, U.dev(bias_h, gpu), plan, B.alloc_workspace(cfg, gpu))
+    grads = B.alloc_grads(cfg, gpu, dg=True)
+    bws = torch.empty(B.backward_workspace_bytes(cfg), dtype=torch.uint8, device=gpu)
+    B.backward(cfg, x, wg, w["w1"], w.get("w3"), w["w2"], plan, dy, grads, bws)
+    torch.cuda.synchronize()
+    oplan = oracle.route(x_h, r.dtype, wg_h, bias_h, r.k, r.gate_mode, _cap(r))
+    U.assert_plan_equal(plan, oplan, f"full run {name}")
+    kept, off, rt = oplan["kept"], oplan["offsets"], oplan["row_token"]
+    dst, idx, gate = oplan["dst_row"], oplan["topk_idx"], oplan["topk_gate"]
+    order = np.argsort(kept, kind="stable")
+    nonempty = order[kept[order] > 0]
+    experts = sorted({int(nonempty[-1]), int(nonempty[len(nonempty) // 2]), int(nonempty[0])})
+    empty = [int(e) for e in order[kept[order] == 0][:1]]
+    # row -> (token, choice)
+    choice_of_row = np.full(oplan["R"], -1, np.int64)
+    kt, kr = np.nonzero(dst >= 0)
+    choice_of_row[dst[kt, kr]] = kr
+    dyf = U.as_f64(dy_h)
+    for e in experts:
+        rows = np.arange(off[e], off[e + 1])
+        toks = rt[rows]
+        wts = {n: recipes.gen_expert_weight(r, n, experts=[e])[e][None] for n in names}
+        Xe = x_h[toks]
+        dYe = gate[toks, choice_of_row[rows]][:, None].astype(np.float64) * dyf[toks]
+        _, dW1, dW3, dW2 = OB.expert_backward(Xe, np.array([0, rows.size]), r.act, wts["w1"], wts.get("w3"), wts["w2"],
+                                              dYe)
+        got = {"dW1": grads["dW1"][e].cpu().numpy().astype(np.float64)[None],
+               "dW2": grads["dW2"][e].cpu().numpy().astype(np.float64)[None]}
+        ref = {"dW1": dW1, "dW2": dW2}
+        if r.act == recipes.SWIGLU:
+            got["dW3"] = grads["dW3"][e].cpu().numpy().astype(np.float64)[None]
+            ref["dW3"] = dW3
+        _compare(f"full run {name} expert {e} ({rows.size} rows)", got, ref, GRAD_RELL2_MC)
+    for e in empty:
+        for n in ("dW1", "dW3", "dW2"):
+            if n in grads:
+                assert bool((grads[n][e] == 0).all()), (n, e)
+    # sampled tokens: dg from the token's own expert outputs, dx from its kept rows
+    # (expert path) plus dl Wg^T (router path, dl from the gate Jacobian of its dg)
+    rng = np.random.default_rng(int(name.encode()[0]))
+    toks = np.sort(rng.choice(r.T, size=64, replace=False))
+    cache = {}
+
+    def wt(e):  # the expert's weights, as generated and in binary64 (converted once)
+        if e not in cache:
+            raw = {n: recipes.gen_expert_weight(r, n, experts=[e])[e][None] for n in names}
+            cache[e] = (raw, {n: OB._f64(v) for n, v in raw.items()})
+        return cache[e]
+
+    dg_ref = np.zeros((r.T, r.k))
+    dx_ref = np.zeros((toks.size, r.H))
+    for i, t in enumerate(toks):
+        for c in range(r.k):
+            if dst[t, c] < 0:
+                continue
+            e = int(idx[t, c])
+            raw, w64 = wt(e)
+            Yrow = oracle.expert_rows(x_h[t:t + 1], [0], r.dtype, r.act, raw["w1"], raw.get("w3"), raw["w2"])[0]
+            dg_ref[t, c] = float(Yrow @ dyf[t])
+            dX, _, _, _ = OB.expert_backward(x_h[t:t + 1], np.array([0, 1]), r.act, w64["w1"], w64.get("w3"),
+                                             w64["w2"], float(gate[t, c]) * dyf[t:t + 1])
+            dx_ref[i] += dX[0]
+    dl = OB.gate_backward(oplan["logits"], oplan, dg_ref, r.gate_mode)
+    dx_ref += dl[toks] @ wg_h.astype(np.float64).T
+    got = {"dx": grads["dx"].cpu().numpy().astype(np.float64)[toks],
+           "dg": grads["dg"].cpu().numpy().astype(np.float64)[toks]}
+    _compare(f"full run {name} tokens", got, {"dx": dx_ref, "dg": dg_ref[toks]}, GRAD_RELL2_MC)
