@@ -25,11 +25,14 @@
 // GEMM with arbitrary strides, over groups of rows (one per expert: ragged M) or
 // of reduction indices (ragged K), so that no operand needs a transposed copy,
 // and every intermediate is fp32.  Matrix-core path (bf16, H and F multiples of
-// 64): the recomputation and the two data-gradient products run on the expert
-// FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates), which takes
-// its second operand as [N][K] rows, so W2 and [W1; W3] are transposed once per
-// call; the weight gradients stay on the strided GEMM, reading the bf16
-// intermediates.  The order of every sum is fixed: results are deterministic.
+// 64): the recomputation of u and v and the two data-gradient products run on
+// the expert FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates),
+// which takes its second operand as [N][K] rows, so W2 and [W1; W3] are
+// transposed once per call.  There the first product takes the tokens' dy rows
+// unscaled, dzr = dy W2, so that dg = <Y, dy> = <z, dzr> needs no Y, and the
+// gate enters du, dv and (through g z) dW2 = sum dy^T (g z).  The weight
+// gradients run on a grouped MFMA kernel over each expert's rows.  The order of
+// every sum is fixed: results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -223,6 +226,46 @@ __global__ void __launch_bounds__(256) gather_sum_kernel(const T* __restrict__ d
       if (row >= 0) acc += ld(dX, (int64_t)row * H + h);
     }
     dx[(int64_t)t * H + h] = acc;
+  }
+}
+
+// Matrix-core path, one block per token, for each kept choice (row = its packed
+// row, g = its gate), from dzr = dy[t] W2_e (the rows of the dz product taken on
+// the token's unscaled dy):
+//   dg = <Y[row], dy[t]> = <z[row], dzr[row]>  (Y = z W2_e^T, so no Y is formed);
+//   du = g dzr act'(u)  (SwiGLU: du = g dzr v silu'(u), dv = g dzr silu(u));
+//   row_gate[row] = g.  A dropped or absent choice gets dg = 0.
+__global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restrict__ dzr, const uint16_t* __restrict__ u,
+                                                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ z,
+                                                        const float* __restrict__ gate, const int32_t* __restrict__ dst,
+                                                        uint16_t* __restrict__ du, uint16_t* __restrict__ dv,
+                                                        int64_t ldd, float* __restrict__ dg,
+                                                        float* __restrict__ row_gate, int F, int k, int act) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  for (int c = 0; c < k; ++c) {
+    const int row = dst[(int64_t)t * k + c];
+    if (row < 0) {
+      if (threadIdx.x == 0) dg[(int64_t)t * k + c] = 0.0f;
+      continue;
+    }
+    const float g = gate[(int64_t)t * k + c];
+    if (threadIdx.x == 0) row_gate[row] = g;
+    const int64_t rb = (int64_t)row * F, ob = (int64_t)row * ldd;
+    float part = 0.0f;
+    for (int f = threadIdx.x; f < F; f += 256) {
+      const float d = ld(dzr, rb + f), a = ld(u, rb + f);
+      part = __builtin_fmaf(ld(z, rb + f), d, part);
+      if (act == 2) {
+        const float s = 1.0f / (1.0f + __expf(-a));
+        sto(du, ob + f, g * d * ld(v, rb + f) * (s * (1.0f + a * (1.0f - s))));
+        sto(dv, ob + f, g * d * (a * s));
+      } else {
+        sto(du, ob + f, g * d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a)));
+      }
+    }
+    const float sum = block_sum256(part, red);
+    if (threadIdx.x == 0) dg[(int64_t)t * k + c] = sum;
   }
 }
 
@@ -424,7 +467,8 @@ __global__ void __launch_bounds__(256) seg_transpose_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ gather,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ poff, int E, int C,
-                                                            uint16_t* __restrict__ out, int64_t ldo) {
+                                                            uint16_t* __restrict__ out, int64_t ldo,
+                                                            const float* __restrict__ rscale = nullptr) {
   __shared__ uint16_t tile[64][65];
   __shared__ int col[64];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -449,7 +493,9 @@ __global__ void __launch_bounds__(256) seg_transpose_kernel(const uint16_t* __re
     const int r = r0 + rr;
     if (r < R && c0 + cc < C) {
       const int64_t src = gather ? (int64_t)gather[r] : (int64_t)r;
-      tile[rr][cc] = in[src * ldi + ci + c0 + cc];
+      const uint16_t b = in[src * ldi + ci + c0 + cc];
+      // rscale: each row multiplied by its factor (rounded once to bf16)
+      tile[rr][cc] = rscale ? (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)b << 16) * rscale[r]) : b;
     }
   }
   __syncthreads();
@@ -722,20 +768,18 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     uint16_t* z = reinterpret_cast<uint16_t*>(w + L.z);
     uint16_t* dz = reinterpret_cast<uint16_t*>(w + L.dz);
     uint16_t* dcat = reinterpret_cast<uint16_t*>(w + L.du);  // [R][2F]: du | dv (or [R][F])
-    uint16_t* Y = reinterpret_cast<uint16_t*>(w + L.Y);
-    uint16_t* dY = reinterpret_cast<uint16_t*>(w + L.dY);
+    uint16_t* Y = reinterpret_cast<uint16_t*>(w + L.Y);  // space only (row gates)
     uint16_t* dX = reinterpret_cast<uint16_t*>(w + L.dX);
     uint16_t* w2t = reinterpret_cast<uint16_t*>(w + L.w2t);
     uint16_t* w13t = reinterpret_cast<uint16_t*>(w + L.w13t);
     const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
     const int64_t rc = a.rows_cap;
     if (R_max > 0) {
-      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T, z, Y = z W2^T
+      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T, z
       MOE_BW(launch_grouped_gemm_bf16(a.x, a.W1, u, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
       if (gated) MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
       act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
       MOE_BW(hipGetLastError());
-      MOE_BW(launch_grouped_gemm_bf16(z, a.W2, Y, a.offsets, E, H, F, R_max, rc, true, st));
       // the second operands of the data-gradient products as [N][K] rows
       transpose_bf16_kernel<<<dim3((F + 63) / 64, (H + 63) / 64, E), 256, 0, st>>>(
           static_cast<const uint16_t*>(a.W2), w2t, H, F, H, 0);  // W2_e [H][F] -> [F][H]
@@ -749,14 +793,15 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
         MOE_BW(hipGetLastError());
       }
     }
-    combine_bwd_kernel<uint16_t, uint16_t><<<T, 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), Y, a.topk_gate,
-                                                              a.dst_row, dY, dg, H, k);
+    float* row_gate = reinterpret_cast<float*>(Y);  // [R]: the gate of each packed row
+    if (R_max > 0) {
+      // dzr = dy[row_token] W2 per kept row (the gate is applied in token_bwd_kernel)
+      MOE_BW(launch_grouped_gemm_bf16(a.dy, w2t, dz, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+    }
+    token_bwd_kernel<<<T, 256, 0, st>>>(dz, u, v, z, a.topk_gate, a.dst_row, dcat, dcat + F, KC, dg, row_gate, F, k,
+                                        a.act);
     MOE_BW(hipGetLastError());
     if (R_max > 0) {
-      MOE_BW(launch_grouped_gemm_bf16(dY, w2t, dz, a.offsets, E, F, H, R_max, rc, true, st));  // dz = dY W2
-      act_bwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(dz, u, v, dcat, dcat + F, a.offsets, E, F,
-                                                                         KC, a.act);
-      MOE_BW(hipGetLastError());
       MOE_BW(launch_grouped_gemm_bf16(dcat, w13t, dX, a.offsets, E, H, KC, R_max, rc, true, st));  // dX
       gather_sum_kernel<uint16_t><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
       MOE_BW(hipGetLastError());
@@ -764,8 +809,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
       MOE_BW(hipGetLastError());
     }
-    // weight gradients on the matrix cores: the expert's rows of dY, z, [du | dv]
-    // and x transposed into zero-padded 64-aligned column segments
+    // weight gradients on the matrix cores: the expert's rows of dy (gathered), g z,
+    // [du | dv] and x (gathered) transposed into zero-padded 64-aligned column
+    // segments; dW2 = sum over the rows of dy^T (g z)
     int32_t* poff = reinterpret_cast<int32_t*>(w + L.poff);
     uint16_t* dyt = reinterpret_cast<uint16_t*>(w + L.dyt);
     uint16_t* zt = reinterpret_cast<uint16_t*>(w + L.zt);
@@ -779,9 +825,11 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     MOE_BW(hipGetLastError());
     if (R_max > 0) {
       const unsigned gy = (unsigned)((R_max + 63) / 64);
-      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(dY, H, 0, nullptr, a.offsets, poff, E, H, dyt, ld);
+      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), H, 0,
+                                                                    a.row_token, a.offsets, poff, E, H, dyt, ld);
       MOE_BW(hipGetLastError());
-      seg_transpose_kernel<<<dim3((F + 63) / 64, gy), 256, 0, st>>>(z, F, 0, nullptr, a.offsets, poff, E, F, zt, ld);
+      seg_transpose_kernel<<<dim3((F + 63) / 64, gy), 256, 0, st>>>(z, F, 0, nullptr, a.offsets, poff, E, F, zt, ld,
+                                                                    row_gate);
       MOE_BW(hipGetLastError());
       seg_transpose_kernel<<<dim3((KC + 63) / 64, gy), 256, 0, st>>>(dcat, KC, 0, nullptr, a.offsets, poff, E, KC, dt,
                                                                      ld);

@@ -499,8 +499,8 @@ moe_status moe_backward(const moe_config* c, const void* x, const float* Wg, con
   a.rows_cap = expert_rows_cap(c, a.R_max);
   a.bf16 = c->dtype == MOE_BF16;
   // the matrix-core path reads x, the weights and its workspace 16 bytes at a time
-  a.fast = moe::backward_fast_shape(a.bf16, c->H, c->F) && aligned16(x) && aligned16(W1) && aligned16(W3) &&
-           aligned16(W2) && aligned16(ws);
+  a.fast = moe::backward_fast_shape(a.bf16, c->H, c->F) && aligned16(x) && aligned16(dy) && aligned16(W1) &&
+           aligned16(W3) && aligned16(W2) && aligned16(ws);
   a.with_losses = plan->losses != nullptr;
   a.aux_coeff = c->aux_coeff, a.z_coeff = c->z_coeff;
   a.x = x, a.Wg = Wg, a.W1 = W1, a.W3 = W3, a.W2 = W2;
