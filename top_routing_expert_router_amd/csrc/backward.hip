@@ -26,9 +26,9 @@
 // of reduction indices (ragged K), so that no operand needs a transposed copy,
 // and every intermediate is fp32.  Matrix-core path (bf16, H and F multiples of
 // 64): the recomputation of u and v and the two data-gradient products run on
-// the expert FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates),
-// which takes its second operand as [N][K] rows, so W2 and [W1; W3] are
-// transposed once per call.  There the first product takes the tokens' dy rows
+// the expert FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates);
+// the data-gradient products use its k-major form, which reads W2 and W1, W3
+// as stored (no transposed copies).  There the first product takes the tokens' dy rows
 // unscaled, dzr = dy W2, so that dg = <Y, dy> = <z, dzr> needs no Y, and the
 // gate enters du, dv and (through g z) dW2 = sum dy^T (g z).  The weight
 // gradients run on a grouped MFMA kernel over each expert's rows.  The order of
@@ -410,37 +410,6 @@ __global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ 
   if (ph == 0 && e < E) out[e] = (part[0][el] + part[1][el]) + (part[2][el] + part[3][el]);
 }
 
-// out_b[c * ldo + col0 + r] = in_b[r * C + c] for each batch b (in_b = in + b*R*C,
-// out_b = out + b*C*ldo): bf16, 64 x 64 tiles through LDS, 16-byte loads and
-// stores (R, C, ldo and col0 multiples of 8; 16-byte aligned buffers).
-__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                             int R, int C, int64_t ldo, int col0) {
-  __shared__ uint16_t tile[64][72];  // 144-byte rows: the 8 rows a column read spans hit different banks
-  const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const uint16_t* ib = in + (int64_t)b * R * C;
-  uint16_t* ob = out + (int64_t)b * C * ldo;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // 64 rows x 8 chunks of 8 columns
-    const int p = threadIdx.x + 256 * q, rr = p >> 3, ch = p & 7;
-    if (r0 + rr < R && c0 + 8 * ch < C) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ib + (int64_t)(r0 + rr) * C + c0 + 8 * ch);
-      *reinterpret_cast<u32x4_t*>(&tile[rr][8 * ch]) = v;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {  // 64 output rows (input columns) x 8 chunks of 8 input rows
-    const int p = threadIdx.x + 256 * q, cc = p >> 3, ch = p & 7;
-    if (c0 + cc < C && r0 + 8 * ch < R) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)tile[8 * ch + 2 * j][cc] | ((uint32_t)tile[8 * ch + 2 * j + 1][cc] << 16);
-      *reinterpret_cast<u32x4_t*>(ob + (int64_t)(c0 + cc) * ldo + col0 + r0 + 8 * ch) = u32x4_t{w[0], w[1], w[2], w[3]};
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Weight gradients on the matrix cores.  dW_e = A_e B_e^T where A_e and B_e are
 // the expert's rows of two activations, transposed: each operand row holds one
@@ -512,31 +481,38 @@ __global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
 
 // C_e[m][n] = sum_k A[m][poff[e] + k] B[n][poff[e] + k], k < poff[e+1] - poff[e]
 // (fp32 accumulation, fp32 out, C_e = C + e * M * N).  128 x 128 tiles, 4 waves
-// as 2 x 2 (each 2 x 2 fragments of v_mfma_f32_32x32x16_bf16), 64-wide k stages
-// of 128-byte rows in two LDS buffers filled by direct-to-LDS loads (chunk c of
-// row r at slot c ^ ((r >> 1) & 7)).  Rows past M or N read row M-1 / N-1 and
-// are not stored.
+// as 2 x 2 (each 2 x 2 fragments of v_mfma_f32_32x32x16_bf16), 32-wide k stages
+// of 64-byte rows in two 16 KB LDS buffers filled by direct-to-LDS loads (chunk
+// c of row r at slot c ^ ((r >> 2) & 3): the 16 rows of a 16-byte read phase
+// land in distinct bank groups); small stages keep several workgroups per CU.
+// The kernel is bound by its fp32 stores (the reduction per expert is short):
+// each wave stages its 64 x 64 block through LDS, 32 rows at a time ([32][68]
+// fp32, the padding puts rows 4 apart in different banks), and writes whole
+// 256-byte row pieces with 16-byte non-temporal stores (the gradient is not
+// read again here).  Rows past M or N read row M-1 / N-1 and are not stored;
+// N % 4 == 0.
 __global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ B, float* __restrict__ C,
                                                          const int32_t* __restrict__ poff, int M, int N, int64_t ld) {
-  constexpr int BM = 128, BN = 128, ROWS = BM + BN, STAGE = ROWS * 64;
-  __shared__ __align__(16) uint16_t smem[2 * STAGE];
+  constexpr int BM = 128, BN = 128, BK = 32, ROWS = BM + BN, STAGE = ROWS * BK;
+  constexpr int PAD = 68, EPI = 4 * 32 * PAD * 2;  // epilogue staging, in bf16 units
+  __shared__ __align__(16) uint16_t smem[2 * STAGE > EPI ? 2 * STAGE : EPI];
   const int e = blockIdx.z, m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int kb = poff[e], nk = (poff[e + 1] - kb) / 64;
-  auto lds_pos = [](int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; };
-  // this thread's 8 pieces per stage: piece p = q * 256 + tid -> row p / 8, LDS slot p % 8
-  const uint16_t* src[8];
+  const int kb = poff[e], nk = (poff[e + 1] - kb) / BK;
+  auto lds_pos = [](int r, int c) { return (r * 4 + (c ^ ((r >> 2) & 3))) * 8; };
+  // this thread's 4 pieces per stage: piece p = q * 256 + tid -> row p / 4, LDS slot p % 4
+  const uint16_t* src[4];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int p = q * 256 + tid, r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+  for (int q = 0; q < 4; ++q) {
+    const int p = q * 256 + tid, r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
     const int64_t row = r < BM ? (int64_t)min(m0 + r, M - 1) : (int64_t)min(n0 + r - BM, N - 1);
     src[q] = (r < BM ? A : B) + row * ld + kb + c * 8;
   }
   auto issue = [&](int buf, int j) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds(src[q] + j * 64, smem + buf * STAGE + (q * 4 + w) * 512, 16, 0, 0);
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(src[q] + j * BK, smem + buf * STAGE + (q * 4 + w) * 512, 16, 0, 0);
   };
   f32x16_t acc[2][2];
 #pragma unroll
@@ -552,7 +528,7 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restr
     if (j + 1 < nk) issue((j + 1) & 1, j + 1);
     const uint16_t* st = smem + (j & 1) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < 2; ++kk) {
       const int c = kk * 2 + (lane >> 5);
       bf16x8_t a[2], b[2];
 #pragma unroll
@@ -566,20 +542,30 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restr
         for (int jj = 0; jj < 2; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
     }
   }
+  __syncthreads();  // every wave is done reading the stages: their space stages the stores
   // accumulator element 4g + q of lane l: row 8g + 4(l / 32) + q of the A fragment, column l % 32
+  float* sw = reinterpret_cast<float*>(smem) + w * 32 * PAD;
   float* Ce = C + (int64_t)e * M * N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * g + 4 * (lane >> 5) + q;
-          const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-          if (m < M && n < N) Ce[(int64_t)m * N + n] = acc[i][jj][4 * g + q];
-        }
+        for (int q = 0; q < 4; ++q) sw[(8 * g + 4 * (lane >> 5) + q) * PAD + jj * 32 + (lane & 31)] = acc[i][jj][4 * g + q];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {  // 4 rows x 64 columns per store instruction
+      const int r = s * 4 + (lane >> 4), c = (lane & 15) * 4;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(sw + r * PAD + c);
+      const int m = m0 + wm * 64 + i * 32 + r, n = n0 + wn * 64 + c;
+      if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(Ce + (int64_t)m * N + n));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next half overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
@@ -615,10 +601,10 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
 // dX [R][H], fp32.  Matrix-core: the same in bf16 with du and dv side by side
-// ([R][2F]), plus W2^T [E][F][H] and [W1; W3]^T [E][H][2F] (or W1^T [E][H][F]).
+// ([R][2F]), plus the transposed activations of the weight gradients.
 // Both end with dl [T][E] fp32, f [E] binary64 and dg [T][k] fp32.
 struct BwdLayout {
-  size_t u, v, z, dz, du, Y, dY, dX, w2t, w13t, poff, dyt, zt, dt, xt, dl, f, dg, total;
+  size_t u, v, z, dz, du, Y, dY, dX, poff, dyt, zt, dt, xt, dl, f, dg, total;
   int64_t ldt;  // row stride of the transposed activations (rows of each expert padded to 64)
 };
 
@@ -635,13 +621,10 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.Y = o, o += RH;
   L.dY = o, o += RH;
   L.dX = o, o += RH;
-  L.w2t = L.w13t = L.poff = L.dyt = L.zt = L.dt = L.xt = o;
+  L.poff = L.dyt = L.zt = L.dt = L.xt = o;
   L.ldt = (R_max + 63 * (int64_t)E + 63) / 64 * 64;
   if (fast) {
-    const size_t EFH = (size_t)E * (size_t)F * (size_t)H * 2;
     const size_t KC = gated ? 2 * (size_t)F : (size_t)F, ld = (size_t)L.ldt;
-    L.w2t = o, o += al256(EFH);
-    L.w13t = o, o += al256(EFH * (gated ? 2 : 1));
     L.poff = o, o += al256(sizeof(int32_t) * ((size_t)E + 1));
     // dY^T [H], z^T [F], [du | dv]^T [KC], x^T [H] rows of ldt, contiguous (zeroed together)
     L.dyt = o;
@@ -770,8 +753,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     uint16_t* dcat = reinterpret_cast<uint16_t*>(w + L.du);  // [R][2F]: du | dv (or [R][F])
     uint16_t* Y = reinterpret_cast<uint16_t*>(w + L.Y);  // space only (row gates)
     uint16_t* dX = reinterpret_cast<uint16_t*>(w + L.dX);
-    uint16_t* w2t = reinterpret_cast<uint16_t*>(w + L.w2t);
-    uint16_t* w13t = reinterpret_cast<uint16_t*>(w + L.w13t);
     const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
     const int64_t rc = a.rows_cap;
     if (R_max > 0) {
@@ -780,29 +761,21 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       if (gated) MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
       act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
       MOE_BW(hipGetLastError());
-      // the second operands of the data-gradient products as [N][K] rows
-      transpose_bf16_kernel<<<dim3((F + 63) / 64, (H + 63) / 64, E), 256, 0, st>>>(
-          static_cast<const uint16_t*>(a.W2), w2t, H, F, H, 0);  // W2_e [H][F] -> [F][H]
-      MOE_BW(hipGetLastError());
-      transpose_bf16_kernel<<<dim3((H + 63) / 64, (F + 63) / 64, E), 256, 0, st>>>(
-          static_cast<const uint16_t*>(a.W1), w13t, F, H, KC, 0);  // W1_e [F][H] -> [H][F] at column 0
-      MOE_BW(hipGetLastError());
-      if (gated) {
-        transpose_bf16_kernel<<<dim3((H + 63) / 64, (F + 63) / 64, E), 256, 0, st>>>(
-            static_cast<const uint16_t*>(a.W3), w13t, F, H, KC, F);  // W3_e -> columns F .. 2F-1
-        MOE_BW(hipGetLastError());
-      }
     }
     float* row_gate = reinterpret_cast<float*>(Y);  // [R]: the gate of each packed row
     if (R_max > 0) {
-      // dzr = dy[row_token] W2 per kept row (the gate is applied in token_bwd_kernel)
-      MOE_BW(launch_grouped_gemm_bf16(a.dy, w2t, dz, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+      // dzr = dy[row_token] W2 per kept row (the gate is applied in token_bwd_kernel);
+      // W2_e [H][F] is the k-major second operand as stored
+      MOE_BW(launch_grouped_gemm_bf16_kn(a.dy, a.W2, nullptr, dz, a.offsets, E, F, H, H, R_max, rc, st, a.row_token,
+                                         T));
     }
     token_bwd_kernel<<<T, 256, 0, st>>>(dz, u, v, z, a.topk_gate, a.dst_row, dcat, dcat + F, KC, dg, row_gate, F, k,
                                         a.act);
     MOE_BW(hipGetLastError());
     if (R_max > 0) {
-      MOE_BW(launch_grouped_gemm_bf16(dcat, w13t, dX, a.offsets, E, H, KC, R_max, rc, true, st));  // dX
+      // dX = du W1 (+ dv W3): W1_e, W3_e [F][H] are the two k-major halves
+      MOE_BW(launch_grouped_gemm_bf16_kn(dcat, a.W1, gated ? a.W3 : nullptr, dX, a.offsets, E, H, KC, F, R_max, rc,
+                                         st));
       gather_sum_kernel<uint16_t><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
       MOE_BW(hipGetLastError());
     } else {

@@ -13,6 +13,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -148,6 +149,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) of the 8 bytes at p, an LDS
+// address: in each group of 16 lanes, lane i receives element i % 4 of the
+// reads of lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12, in that order.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
 }
 
 // Workgroup barrier ordering LDS accesses for the compiler, without the

@@ -304,6 +304,18 @@ __global__ void __launch_bounds__(64) grouped_gemm_scalar_kernel(const void* __r
 // of the device-side tile list (expert-major, then n-tile, then m-tile).  The
 // stage ring runs on across tile boundaries, so the next tile's first loads
 // are in flight while the current tile's epilogue runs.
+//
+// BT (k-major weights, plain products only): the weight operand is stored
+// [E][K][N] (N contiguous), as W2 is for dY W2 and W1, W3 for du W1 + dv W3,
+// and a stage holds BK k-rows of WR columns instead of WR rows of BK k.  Slot
+// ch of k-row kr holds the columns of chunk ch ^ 4 (kr & 3).  The weight
+// fragment (column l % 32, k 8 (l / 32) .. +7 of lane l) comes from two
+// transposing LDS reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// s addresses 4 columns 4 (s % 4) .. +3 of k-row s / 4, and lane i receives
+// column i of those 16 for the 4 k-rows.  The 32 lanes of a read phase touch 4
+// k-rows x 4 chunks, which the swizzle puts in 16 distinct bank groups.  W2 is
+// then an optional second weight tensor that continues the contraction: k < k1
+// from W ([E][k1][N]), k >= k1 from W2 (same shape, K = 2 k1).
 // ---------------------------------------------------------------------------
 struct PipeTile {
   int e, row0, rows, n0;
@@ -373,7 +385,7 @@ __device__ __forceinline__ int clamp_row(int tok, int xrows) { return tok < 0 ? 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
 // as WGM (token direction) x NW / WGM (weight direction); at most 256 registers
 // per wave (two waves per SIMD: one workgroup of 8 waves or two of 4 per CU).
-template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW, bool NTW>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW, bool NTW, bool BT = false>
 __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
@@ -381,7 +393,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
                                                                    const int32_t* __restrict__ gather, int xrows,
-                                                                   Combine1 cmb, int rlo, int rhi) {
+                                                                   Combine1 cmb, int rlo, int rhi, int k1) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -397,7 +409,10 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   constexpr int KS = BK / 16;                             // MFMA k-steps per stage
   static_assert(ROWS * CPR % (64 * NW) == 0 && BM % 64 == 0 && (CPR == 4 || CPR == 8 || CPR == 2), "tile");
   static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
-  static_assert(MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
+  static_assert(BT || MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
+  static_assert(!BT || (EPI == EPI_NONE && WR % 128 == 0), "k-major weights: plain products, 16+ chunks per k-row");
+  constexpr int NRD = MF + (BT ? 2 : 1) * NF;              // LDS reads per k-step
+  constexpr int NIL = MF * NF < NRD ? MF * NF : NRD;        // of them interleaved one by one with MFMAs
   static_assert(S >= 2 && S - 2 <= 4 && (S - 1) * L < 64 && KS % 2 == 0, "stages");
   extern __shared__ __align__(16) uint16_t smem[];
   int* s_ts = reinterpret_cast<int*>(smem + S * STAGE);  // [E+1] first tile of each expert
@@ -497,6 +512,11 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
         const int src = gather ? clamp_row(s_gidx[gbuf][w][q * RPL + lane / CPR], xrows) : t.row0 + rr;
         rowp[q] = (r >= t.rows && K <= kZeroRowElems) ? reinterpret_cast<uintptr_t>(g_zero_row + c * 8)
                                                       : reinterpret_cast<uintptr_t>(A + (size_t)src * K + c * 8);
+      } else if constexpr (BT) {
+        const int pw = p - BM * CPR, kr = pw / (WR / 8), ch = (pw % (WR / 8)) ^ (4 * (kr & 3));
+        int n = t.n0 + ch * 8;
+        n = n < N - 8 ? n : N - 8;  // chunks past N: whole chunks, never stored
+        rowp[q] = reinterpret_cast<uintptr_t>(W + ((size_t)t.e * k1 + kr) * N + n);
       } else {
         const int wr = r - BM;
         const uint16_t* base = (kGated && wr >= WR / 2) ? W2 : W;
@@ -506,12 +526,17 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
       }
     }
   };
+  // k-major weights: byte distance from W to W2 (the k >= k1 half)
+  const uintptr_t wdelta = BT ? reinterpret_cast<uintptr_t>(W2) - reinterpret_cast<uintptr_t>(W) : 0;
   auto issue = [&](int buf, int kstep) {
     uint16_t* st = smem + buf * STAGE;
     const int k0 = kstep * BK;
+    uintptr_t woff = 0;  // k-major weights: byte offset of the stage's first k-row
+    if constexpr (BT) woff = k0 < k1 ? (uintptr_t)k0 * N * 2 : wdelta + (uintptr_t)(k0 - k1) * N * 2;
 #pragma unroll
     for (int q = 0; q < L; ++q) {
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(rowp[q]) + k0;
+      const uint16_t* src = (BT && q >= NA) ? reinterpret_cast<const uint16_t*>(rowp[q] + woff)
+                                            : reinterpret_cast<const uint16_t*>(rowp[q]) + k0;
       if (NTW && q >= NA) __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, kLoadNT);
       else __builtin_amdgcn_global_load_lds(src, st + (q * NW + w) * 512, 16, 0, 0);
     }
@@ -535,9 +560,17 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int r = BM + (kGated ? (f / HF) * (WR / 2) + wn * (HF * 32) + (f % HF) * 32 : wn * (NF * 32) + f * 32) +
-                    (lane & 31);
-      fr.w[f] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+      if constexpr (BT) {
+        const int n = wn * (NF * 32) + f * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int kr = kk * 16 + 8 * (lane >> 5) + ((lane >> 2) & 3);
+        const uint16_t* wp = st + BM * BK + kr * WR + (((n >> 3) ^ (4 * (kr & 3))) << 3) + (n & 7);
+        const s16x4_t lo = lds_read_tr16(wp), hi = lds_read_tr16(wp + 4 * WR);
+        fr.w[f] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        const int r = BM + (kGated ? (f / HF) * (WR / 2) + wn * (HF * 32) + (f % HF) * 32 : wn * (NF * 32) + f * 32) +
+                      (lane & 31);
+        fr.w[f] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+      }
     }
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
@@ -660,11 +693,12 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
         // one fragment read of the next k-step between consecutive MFMAs, so
         // the LDS latency hides behind the matrix pipe instead of a full drain
 #pragma unroll
-        for (int q = 0; q < MF + NF; ++q) {
+        for (int q = 0; q < NIL; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - (MF + NF), 0);
+        if constexpr (!BT || MF * NF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - NIL, 0);
+        if constexpr (BT && NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
       }
     }
     if (j + 1 < total_steps) {
@@ -1013,10 +1047,10 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
 }
 
 // rlo, rhi: only the experts with rlo < rows <= rhi
-template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8, bool BT = false>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              const Combine1& cmb, hipStream_t st, int rlo = -1, int rhi = INT32_MAX) {
+                              const Combine1& cmb, hipStream_t st, int rlo = -1, int rhi = INT32_MAX, int k1 = 0) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -1025,11 +1059,11 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   const int grid = (int)(tiles < slots ? tiles : slots);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
   constexpr int kMaxShm = sizeof(uint16_t) * S * (BM + WR) * BK + sizeof(int) * 2 * (1024 + 1);  // E <= 1024
-  hipError_t err = lds_limit_once<grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW>>(kMaxShm);
+  hipError_t err = lds_limit_once<grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT>>(kMaxShm);
   if (err != hipSuccess) return err;
-  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW><<<dim3(grid), dim3(64 * NW), shm, st>>>(
+  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb, rlo, rhi);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb, rlo, rhi, k1);
   return hipGetLastError();
 }
 
@@ -1168,6 +1202,34 @@ hipError_t launch_grouped_gemm_bf16(const void* A, const void* B, void* C, const
                                     int xrows) {
   if (R_max == 0) return hipSuccess;
   return launch_one<EPI_NONE>(vec, true, A, B, nullptr, C, offsets, E, N, K, R_max, rows_cap, st, gather, xrows);
+}
+
+hipError_t launch_grouped_gemm_bf16_kn(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets,
+                                       int E, int N, int K, int k1, int64_t R_max, int64_t rows_cap, hipStream_t st,
+                                       const int32_t* gather, int xrows) {
+  if (R_max == 0) return hipSuccess;
+  if (K % 64 != 0 || N % 8 != 0 || N < 8 || (B2 ? (2 * k1 != K || k1 % 64 != 0) : k1 != K))
+    return hipErrorInvalidValue;
+  int cus = 0;
+  hipError_t err = device_cus(&cus);
+  if (err != hipSuccess) return err;
+  const Combine1 cmb{};
+  // the row-major form's tile choice, pipe tiles only: 128 x 256 for experts of
+  // at most 128 rows, 256 x 256 for the larger ones
+  if (R_max / E > 128 || rows_cap > 128) {
+    if (R_max / E <= 128) {
+      err = launch_pipe<128, 256, 64, 3, 2, EPI_NONE, true, 8, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather,
+                                                                     xrows, cmb, st, -1, 128, k1);
+      if (err != hipSuccess) return err;
+    }
+    const int rlo = R_max / E > 128 ? -1 : 128;
+    return rows_cap <= 256 ? launch_pipe<256, 256, 64, 2, 2, EPI_NONE, true, 8, true>(
+                                 A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st, rlo, INT32_MAX, k1)
+                           : launch_pipe<256, 256, 64, 2, 2, EPI_NONE, false, 8, true>(
+                                 A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st, rlo, INT32_MAX, k1);
+  }
+  return launch_pipe<128, 256, 64, 3, 2, EPI_NONE, true, 8, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather,
+                                                                  xrows, cmb, st, -1, INT32_MAX, k1);
 }
 
 }  // namespace moe

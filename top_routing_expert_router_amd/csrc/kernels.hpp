@@ -167,6 +167,12 @@ struct BackwardArgs {
 hipError_t launch_grouped_gemm_bf16(const void* A, const void* B, void* C, const int32_t* offsets, int E, int N, int K,
                                     int64_t R_max, int64_t rows_cap, bool vec, hipStream_t st,
                                     const int32_t* gather = nullptr, int xrows = 0);
+// The same with the second operand k-major: C[r] = A[r] . B_e for the rows r of
+// expert e, B_e = B + e*k1*N ([k1][N] row-major) for k < k1 and, when B2 is given
+// (K = 2 k1), B2 + e*k1*N for k >= k1.  K % 64 == 0, N % 8 == 0, k1 % 64 == 0.
+hipError_t launch_grouped_gemm_bf16_kn(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets,
+                                       int E, int N, int K, int k1, int64_t R_max, int64_t rows_cap, hipStream_t st,
+                                       const int32_t* gather = nullptr, int xrows = 0);
 // the matrix-core path of the backward: bf16, H and F multiples of 64
 bool backward_fast_shape(bool bf16, int H, int F);
 size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max, bool bf16, int act);
