@@ -234,13 +234,13 @@ __global__ void __launch_bounds__(256) gather_sum_kernel(const T* __restrict__ d
 // the token's unscaled dy):
 //   dg = <Y[row], dy[t]> = <z[row], dzr[row]>  (Y = z W2_e^T, so no Y is formed);
 //   du = g dzr act'(u)  (SwiGLU: du = g dzr v silu'(u), dv = g dzr silu(u));
-//   row_gate[row] = g.  A dropped or absent choice gets dg = 0.
+//   z[row] <- g z[row] (rounded to bf16: the operand of dW2 = sum dy^T (g z)).
+// A dropped or absent choice gets dg = 0.
 __global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restrict__ dzr, const uint16_t* __restrict__ u,
-                                                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ z,
+                                                        const uint16_t* __restrict__ v, uint16_t* __restrict__ z,
                                                         const float* __restrict__ gate, const int32_t* __restrict__ dst,
                                                         uint16_t* __restrict__ du, uint16_t* __restrict__ dv,
-                                                        int64_t ldd, float* __restrict__ dg,
-                                                        float* __restrict__ row_gate, int F, int k, int act) {
+                                                        int64_t ldd, float* __restrict__ dg, int F, int k, int act) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   for (int c = 0; c < k; ++c) {
@@ -250,12 +250,12 @@ __global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restri
       continue;
     }
     const float g = gate[(int64_t)t * k + c];
-    if (threadIdx.x == 0) row_gate[row] = g;
     const int64_t rb = (int64_t)row * F, ob = (int64_t)row * ldd;
     float part = 0.0f;
     for (int f = threadIdx.x; f < F; f += 256) {
-      const float d = ld(dzr, rb + f), a = ld(u, rb + f);
-      part = __builtin_fmaf(ld(z, rb + f), d, part);
+      const float d = ld(dzr, rb + f), a = ld(u, rb + f), zf = ld(z, rb + f);
+      part = __builtin_fmaf(zf, d, part);
+      sto(z, rb + f, g * zf);
       if (act == 2) {
         const float s = 1.0f / (1.0f + __expf(-a));
         sto(du, ob + f, g * d * ld(v, rb + f) * (s * (1.0f + a * (1.0f - s))));
@@ -411,108 +411,80 @@ __global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Weight gradients on the matrix cores.  dW_e = A_e B_e^T where A_e and B_e are
-// the expert's rows of two activations, transposed: each operand row holds one
-// feature over the expert's rows, in a column segment that starts at poff[e]
-// and is padded with zeros to a multiple of 64 (so the reduction runs in whole
-// 64-wide stages of 128-byte rows, the grouped GEMM's stage shape).
+// Weight gradients on the matrix cores: dW_e = A_e^T B_e over the expert's
+// packed rows, both operands read as stored (rows of features, the k-major
+// form of the expert GEMMs' data-gradient products), so that no activation is
+// transposed or padded.
 // ---------------------------------------------------------------------------
 
-// poff[e] = sum over e' < e of the expert's rows rounded up to 64; poff[E] = total.
-__global__ void __launch_bounds__(1024) seg_offsets_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int32_t* __restrict__ poff) {
-  __shared__ int tmp[1024 / 64 + 1];
-  const int e = threadIdx.x;
-  const int rows = e < E ? offsets[e + 1] - offsets[e] : 0;
-  int total;
-  const int ex = block_exclusive_scan((rows + 63) / 64 * 64, tmp, &total);
-  if (e < E) poff[e] = ex;
-  if (e == 0) poff[E] = total;
-}
+// Zeros that the weight-gradient loads read for rows past an expert's end (a
+// direct-to-LDS load cannot substitute a value); never written.
+__device__ __align__(16) uint16_t g_wgrad_zero[8];
 
-// out[c * ldo + poff[e] + (r - offsets[e])] = in[row(r) * ldi + ci + c] for the kept
-// rows r of expert e (row(r) = gather[r] when given), 64 x 64 tiles through LDS.
-__global__ void __launch_bounds__(256) seg_transpose_kernel(const uint16_t* __restrict__ in, int64_t ldi, int ci,
-                                                            const int32_t* __restrict__ gather,
-                                                            const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ poff, int E, int C,
-                                                            uint16_t* __restrict__ out, int64_t ldo,
-                                                            const float* __restrict__ rscale = nullptr) {
-  __shared__ uint16_t tile[64][65];
-  __shared__ int col[64];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int R = offsets[E];
-  if (r0 >= R) return;
-  if (threadIdx.x < 64) {  // destination column of each row of the tile
-    const int r = r0 + threadIdx.x;
-    int c = -1;
-    if (r < R) {
-      int lo = 0, hi = E;  // last expert with offsets[e] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (offsets[mid] <= r) lo = mid;
-        else hi = mid;
-      }
-      c = poff[lo] + (r - offsets[lo]);
-    }
-    col[threadIdx.x] = c;
-  }
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;
-    const int r = r0 + rr;
-    if (r < R && c0 + cc < C) {
-      const int64_t src = gather ? (int64_t)gather[r] : (int64_t)r;
-      const uint16_t b = in[src * ldi + ci + c0 + cc];
-      // rscale: each row multiplied by its factor (rounded once to bf16)
-      tile[rr][cc] = rscale ? (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)b << 16) * rscale[r]) : b;
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    if (col[rr] >= 0 && c0 + cc < C) out[(int64_t)(c0 + cc) * ldo + col[rr]] = tile[rr][cc];
-  }
-}
-
-__global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
-// C_e[m][n] = sum_k A[m][poff[e] + k] B[n][poff[e] + k], k < poff[e+1] - poff[e]
-// (fp32 accumulation, fp32 out, C_e = C + e * M * N).  128 x 128 tiles, 4 waves
-// as 2 x 2 (each 2 x 2 fragments of v_mfma_f32_32x32x16_bf16), 32-wide k stages
-// of 64-byte rows in two 16 KB LDS buffers filled by direct-to-LDS loads (chunk
-// c of row r at slot c ^ ((r >> 2) & 3): the 16 rows of a 16-byte read phase
-// land in distinct bank groups); small stages keep several workgroups per CU.
-// The kernel is bound by its fp32 stores (the reduction per expert is short):
-// each wave stages its 64 x 64 block through LDS, 32 rows at a time ([32][68]
-// fp32, the padding puts rows 4 apart in different banks), and writes whole
-// 256-byte row pieces with 16-byte non-temporal stores (the gradient is not
-// read again here).  Rows past M or N read row M-1 / N-1 and are not stored;
-// N % 4 == 0.
-__global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ B, float* __restrict__ C,
-                                                         const int32_t* __restrict__ poff, int M, int N, int64_t ld) {
-  constexpr int BM = 128, BN = 128, BK = 32, ROWS = BM + BN, STAGE = ROWS * BK;
+// C_e[m][n] = sum over the packed rows r of expert e, in row order, of
+// A(r)[m] B(r)[n] (fp32 accumulation, fp32 out, C_e = C + e * M * N), where A(r)
+// is row ga[r] of A (row r when ga is null; lda elements per row), likewise B;
+// the expert's rows are offsets[e] .. offsets[e+1]-1, clamped to rmax.
+// 128 x 128 tiles, 4 waves as 2 x 2, each 2 x 2 fragments of
+// v_mfma_f32_32x32x16_bf16.  A stage holds 32 rows of each operand's 128
+// features of the tile (256 B per row), filled by direct-to-LDS loads: slot ch
+// of stage row kr holds chunk ch ^ 4 (kr & 3), and a fragment (feature l % 32,
+// rows 8 (l / 32) .. +7 of lane l) is two transposing LDS reads, as in the
+// k-major grouped GEMM (the 4 rows x 4 chunks of a 32-lane read phase fall in
+// 16 distinct bank groups).  The gathered operand's source rows are fetched one
+// stage ahead.  The kernel is bound by its fp32 stores (the reduction per
+// expert is short): each wave stages its 64 x 64 block through LDS, 32 rows at
+// a time ([32][68] fp32, the padding puts rows 4 apart in different banks), and
+// writes whole 256-byte row pieces with 16-byte non-temporal stores (the
+// gradient is not read again here).  Features past M or N read the last whole
+// chunk and are not stored; M, N multiples of 8, N % 4 == 0.
+__global__ void __launch_bounds__(256) wgrad_kn_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                       const int32_t* __restrict__ ga, const uint16_t* __restrict__ B,
+                                                       int64_t ldb, const int32_t* __restrict__ gb,
+                                                       float* __restrict__ C, const int32_t* __restrict__ offsets,
+                                                       int64_t rmax, int xrows, int M, int N) {
+  constexpr int BM = 128, BN = 128, BK = 32, RS = BK * BM, STAGE = 2 * RS;  // operand A rows, then B rows
   constexpr int PAD = 68, EPI = 4 * 32 * PAD * 2;  // epilogue staging, in bf16 units
+  static_assert(BM == BN && BM / 8 == 16, "16 chunks per stage row");
   __shared__ __align__(16) uint16_t smem[2 * STAGE > EPI ? 2 * STAGE : EPI];
   const int e = blockIdx.z, m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int kb = poff[e], nk = (poff[e + 1] - kb) / BK;
-  auto lds_pos = [](int r, int c) { return (r * 4 + (c ^ ((r >> 2) & 3))) * 8; };
-  // this thread's 4 pieces per stage: piece p = q * 256 + tid -> row p / 4, LDS slot p % 4
-  const uint16_t* src[4];
+  const int64_t r1 = min((int64_t)offsets[e + 1], rmax), r0 = min((int64_t)offsets[e], r1);
+  const int nk = (int)((r1 - r0 + BK - 1) / BK);
+  // this thread's 4 pieces per stage: piece p = q * 256 + tid of operand q / 2,
+  // stage row kr0 + 16 (q % 2), slot tid % 16 (LDS element p * 8)
+  const int kr0 = tid >> 4, ch = (tid & 15) ^ (4 * (kr0 & 3));
+  const int fa = min(m0 + ch * 8, M - 8), fb = min(n0 + ch * 8, N - 8);
+  int src[2][2];  // source rows of the next stage to load, [operand][half]; -1: past the expert's end
+  auto fetch_rows = [&](int j) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = q * 256 + tid, r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
-    const int64_t row = r < BM ? (int64_t)min(m0 + r, M - 1) : (int64_t)min(n0 + r - BM, N - 1);
-    src[q] = (r < BM ? A : B) + row * ld + kb + c * 8;
-  }
-  auto issue = [&](int buf, int j) {
+    for (int op = 0; op < 2; ++op)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(src[q] + j * BK, smem + buf * STAGE + (q * 4 + w) * 512, 16, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int64_t r = r0 + (int64_t)j * BK + kr0 + 16 * h;
+        const int32_t* g = op ? gb : ga;
+        int s = -1;
+        if (r < r1) {
+          s = g ? g[r] : (int)r;
+          if (g) s = s < 0 ? 0 : (s < xrows ? s : xrows - 1);
+        }
+        src[op][h] = s;
+      }
+  };
+  auto issue = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int op = q >> 1, s = src[op][q & 1];
+      const uint16_t* p = s < 0 ? g_wgrad_zero : (op ? B + (int64_t)s * ldb + fb : A + (int64_t)s * lda + fa);
+      __builtin_amdgcn_global_load_lds(p, smem + buf * STAGE + (q * 4 + w) * 512, 16, 0, 0);
+    }
+  };
+  auto frag = [&](const uint16_t* region, int f0, int kk) {
+    const int f = f0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int kr = kk * 16 + 8 * (lane >> 5) + ((lane >> 2) & 3);
+    const uint16_t* p = region + kr * BM + (((f >> 3) ^ (4 * (kr & 3))) << 3) + (f & 7);
+    const s16x4_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * BM);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   f32x16_t acc[2][2];
 #pragma unroll
@@ -521,20 +493,26 @@ __global__ void __launch_bounds__(256) wgrad_mfma_kernel(const uint16_t* __restr
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  if (nk > 0) issue(0, 0);
+  if (nk > 0) {
+    fetch_rows(0);
+    issue(0);
+    if (nk > 1) fetch_rows(1);
+  }
   for (int j = 0; j < nk; ++j) {
     wait_vmcnt<0>();
-    __syncthreads();  // stage j is in LDS and every wave is done with stage j - 1
-    if (j + 1 < nk) issue((j + 1) & 1, j + 1);
+    __syncthreads();  // stage j is in LDS, every wave is done with stage j - 1, the rows of stage j + 1 are in
+    if (j + 1 < nk) {
+      issue((j + 1) & 1);
+      if (j + 2 < nk) fetch_rows(j + 2);
+    }
     const uint16_t* st = smem + (j & 1) * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
+    for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(wm * 64 + i * 32 + (lane & 31), c));
-        b[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(BM + wn * 64 + i * 32 + (lane & 31), c));
+        a[i] = frag(st, wm * 64 + i * 32, kk);
+        b[i] = frag(st + RS, wn * 64 + i * 32, kk);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -600,15 +578,14 @@ namespace {
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
-// dX [R][H], fp32.  Matrix-core: the same in bf16 with du and dv side by side
-// ([R][2F]), plus the transposed activations of the weight gradients.
-// Both end with dl [T][E] fp32, f [E] binary64 and dg [T][k] fp32.
+// dX [R][H], fp32.  Matrix-core: u, v, z, dz [R][F], [du | dv] [R][2F] and dX
+// [R][H] in bf16 (no Y, dY).  Both end with dl [T][E] fp32, f [E] binary64 and
+// dg [T][k] fp32.
 struct BwdLayout {
-  size_t u, v, z, dz, du, Y, dY, dX, poff, dyt, zt, dt, xt, dl, f, dg, total;
-  int64_t ldt;  // row stride of the transposed activations (rows of each expert padded to 64)
+  size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, total;
 };
 
-BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast, bool gated) {
+BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast) {
   BwdLayout L{};
   const size_t eb = fast ? 2 : 4;
   const size_t RF = al256(eb * (size_t)R_max * (size_t)F), RH = al256(eb * (size_t)R_max * (size_t)H);
@@ -618,21 +595,9 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.z = o, o += RF;
   L.dz = o, o += RF;
   L.du = o, o += 2 * RF;  // generic: du then dv; matrix-core: [R][2F] rows
-  L.Y = o, o += RH;
-  L.dY = o, o += RH;
+  L.Y = o, o += fast ? 0 : RH;
+  L.dY = o, o += fast ? 0 : RH;
   L.dX = o, o += RH;
-  L.poff = L.dyt = L.zt = L.dt = L.xt = o;
-  L.ldt = (R_max + 63 * (int64_t)E + 63) / 64 * 64;
-  if (fast) {
-    const size_t KC = gated ? 2 * (size_t)F : (size_t)F, ld = (size_t)L.ldt;
-    L.poff = o, o += al256(sizeof(int32_t) * ((size_t)E + 1));
-    // dY^T [H], z^T [F], [du | dv]^T [KC], x^T [H] rows of ldt, contiguous (zeroed together)
-    L.dyt = o;
-    L.zt = L.dyt + 2 * (size_t)H * ld;
-    L.dt = L.zt + 2 * (size_t)F * ld;
-    L.xt = L.dt + 2 * KC * ld;
-    o = al256(L.xt + 2 * (size_t)H * ld);
-  }
   L.dl = o, o += al256(sizeof(float) * (size_t)T * (size_t)E);
   L.f = o, o += al256(sizeof(double) * (size_t)E);
   L.dg = o, o += al256(sizeof(float) * (size_t)T * (size_t)k);
@@ -712,9 +677,9 @@ hipError_t weight_grads(const BackwardArgs& a, const T* dY, const T* z, const T*
 bool backward_fast_shape(bool bf16, int H, int F) { return bf16 && H % 64 == 0 && F % 64 == 0; }
 
 size_t backward_workspace_bytes(int64_t T, int H, int E, int k, int F, int64_t R_max, bool bf16, int act) {
-  const size_t g = bwd_layout(T, H, E, k, F, R_max, false, act == 2).total;
+  const size_t g = bwd_layout(T, H, E, k, F, R_max, false).total;
   if (!backward_fast_shape(bf16, H, F)) return g;
-  const size_t f = bwd_layout(T, H, E, k, F, R_max, true, act == 2).total;
+  const size_t f = bwd_layout(T, H, E, k, F, R_max, true).total;
   return f > g ? f : g;
 }
 
@@ -739,7 +704,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     MOE_BW(zero(a.dW2, (int64_t)E * H * F));
     return hipSuccess;
   }
-  const BwdLayout L = bwd_layout(T, H, E, k, F, R_max, a.fast, gated);
+  const BwdLayout L = bwd_layout(T, H, E, k, F, R_max, a.fast);
   char* w = static_cast<char*>(a.ws);
   float* dgw = reinterpret_cast<float*>(w + L.dg);
   float* dg = a.dg ? a.dg : dgw;
@@ -751,7 +716,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     uint16_t* z = reinterpret_cast<uint16_t*>(w + L.z);
     uint16_t* dz = reinterpret_cast<uint16_t*>(w + L.dz);
     uint16_t* dcat = reinterpret_cast<uint16_t*>(w + L.du);  // [R][2F]: du | dv (or [R][F])
-    uint16_t* Y = reinterpret_cast<uint16_t*>(w + L.Y);  // space only (row gates)
     uint16_t* dX = reinterpret_cast<uint16_t*>(w + L.dX);
     const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
     const int64_t rc = a.rows_cap;
@@ -762,15 +726,13 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
       MOE_BW(hipGetLastError());
     }
-    float* row_gate = reinterpret_cast<float*>(Y);  // [R]: the gate of each packed row
     if (R_max > 0) {
       // dzr = dy[row_token] W2 per kept row (the gate is applied in token_bwd_kernel);
       // W2_e [H][F] is the k-major second operand as stored
       MOE_BW(launch_grouped_gemm_bf16_kn(a.dy, a.W2, nullptr, dz, a.offsets, E, F, H, H, R_max, rc, st, a.row_token,
                                          T));
     }
-    token_bwd_kernel<<<T, 256, 0, st>>>(dz, u, v, z, a.topk_gate, a.dst_row, dcat, dcat + F, KC, dg, row_gate, F, k,
-                                        a.act);
+    token_bwd_kernel<<<T, 256, 0, st>>>(dz, u, v, z, a.topk_gate, a.dst_row, dcat, dcat + F, KC, dg, F, k, a.act);
     MOE_BW(hipGetLastError());
     if (R_max > 0) {
       // dX = du W1 (+ dv W3): W1_e, W3_e [F][H] are the two k-major halves
@@ -782,42 +744,19 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
       MOE_BW(hipGetLastError());
     }
-    // weight gradients on the matrix cores: the expert's rows of dy (gathered), g z,
-    // [du | dv] and x (gathered) transposed into zero-padded 64-aligned column
-    // segments; dW2 = sum over the rows of dy^T (g z)
-    int32_t* poff = reinterpret_cast<int32_t*>(w + L.poff);
-    uint16_t* dyt = reinterpret_cast<uint16_t*>(w + L.dyt);
-    uint16_t* zt = reinterpret_cast<uint16_t*>(w + L.zt);
-    uint16_t* dt = reinterpret_cast<uint16_t*>(w + L.dt);
-    uint16_t* xt = reinterpret_cast<uint16_t*>(w + L.xt);
-    const int64_t ld = L.ldt;
-    seg_offsets_kernel<<<1, 1024, 0, st>>>(a.offsets, E, poff);
+    // weight gradients on the matrix cores, over each expert's packed rows:
+    // dW2 = dy[row_token]^T (g z), dW1 = du^T x[row_token], dW3 = dv^T x[row_token]
+    const uint16_t* dy16 = static_cast<const uint16_t*>(a.dy);
+    const uint16_t* x16 = static_cast<const uint16_t*>(a.x);
+    wgrad_kn_kernel<<<dim3((F + 127) / 128, (H + 127) / 128, E), 256, 0, st>>>(dy16, H, a.row_token, z, F, nullptr,
+                                                                               a.dW2, a.offsets, R_max, T, H, F);
     MOE_BW(hipGetLastError());
-    const int64_t nt = (2 * (int64_t)H + F + KC) * ld;
-    zero_u16_kernel<<<grid_1d(nt, 256), 256, 0, st>>>(dyt, nt);
-    MOE_BW(hipGetLastError());
-    if (R_max > 0) {
-      const unsigned gy = (unsigned)((R_max + 63) / 64);
-      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(static_cast<const uint16_t*>(a.dy), H, 0,
-                                                                    a.row_token, a.offsets, poff, E, H, dyt, ld);
-      MOE_BW(hipGetLastError());
-      seg_transpose_kernel<<<dim3((F + 63) / 64, gy), 256, 0, st>>>(z, F, 0, nullptr, a.offsets, poff, E, F, zt, ld,
-                                                                    row_gate);
-      MOE_BW(hipGetLastError());
-      seg_transpose_kernel<<<dim3((KC + 63) / 64, gy), 256, 0, st>>>(dcat, KC, 0, nullptr, a.offsets, poff, E, KC, dt,
-                                                                     ld);
-      MOE_BW(hipGetLastError());
-      seg_transpose_kernel<<<dim3((H + 63) / 64, gy), 256, 0, st>>>(static_cast<const uint16_t*>(a.x), H, 0,
-                                                                    a.row_token, a.offsets, poff, E, H, xt, ld);
-      MOE_BW(hipGetLastError());
-    }
-    wgrad_mfma_kernel<<<dim3((F + 127) / 128, (H + 127) / 128, E), 256, 0, st>>>(dyt, zt, a.dW2, poff, H, F, ld);
-    MOE_BW(hipGetLastError());
-    wgrad_mfma_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(dt, xt, a.dW1, poff, F, H, ld);
+    wgrad_kn_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(dcat, KC, nullptr, x16, H, a.row_token,
+                                                                               a.dW1, a.offsets, R_max, T, F, H);
     MOE_BW(hipGetLastError());
     if (gated) {
-      wgrad_mfma_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(dt + (int64_t)F * ld, xt, a.dW3,
-                                                                                    poff, F, H, ld);
+      wgrad_kn_kernel<<<dim3((H + 127) / 128, (F + 127) / 128, E), 256, 0, st>>>(
+          dcat + F, KC, nullptr, x16, H, a.row_token, a.dW3, a.offsets, R_max, T, F, H);
       MOE_BW(hipGetLastError());
     }
     MOE_BW(router_backward(a, L, dg, st));

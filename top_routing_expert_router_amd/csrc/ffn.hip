@@ -413,6 +413,10 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   static_assert(!BT || (EPI == EPI_NONE && WR % 128 == 0), "k-major weights: plain products, 16+ chunks per k-row");
   constexpr int NRD = MF + (BT ? 2 : 1) * NF;              // LDS reads per k-step
   constexpr int NIL = MF * NF < NRD ? MF * NF : NRD;        // of them interleaved one by one with MFMAs
+  // more reads than MFMAs per k-step (k-major 128-row tiles): the extra reads go
+  // first, and they are the token fragments, so that the first MFMAs of the next
+  // k-step wait only for reads issued early in this one
+  constexpr bool kXFirst = NRD > NIL;
   static_assert(S >= 2 && S - 2 <= 4 && (S - 1) * L < 64 && KS % 2 == 0, "stages");
   extern __shared__ __align__(16) uint16_t smem[];
   int* s_ts = reinterpret_cast<int*>(smem + S * STAGE);  // [E+1] first tile of each expert
@@ -558,6 +562,13 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   auto read_frags = [&](int buf, int kk, Frags& fr) {
     const uint16_t* st = smem + buf * STAGE;
     const int c = kk * 2 + (lane >> 5);
+    if constexpr (kXFirst) {
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int r = wm * (MF * 32) + i * 32 + (lane & 31);
+        fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+      }
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (BT) {
@@ -572,10 +583,12 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
         fr.w[f] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
       }
     }
+    if constexpr (!kXFirst) {
 #pragma unroll
-    for (int i = 0; i < MF; ++i) {
-      const int r = wm * (MF * 32) + i * 32 + (lane & 31);
-      fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+      for (int i = 0; i < MF; ++i) {
+        const int r = wm * (MF * 32) + i * 32 + (lane & 31);
+        fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
+      }
     }
   };
   auto mfma = [&](const Frags& fr) {
@@ -692,13 +705,13 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
       if (kk + 1 < KS) {
         // one fragment read of the next k-step between consecutive MFMAs, so
         // the LDS latency hides behind the matrix pipe instead of a full drain
+        if constexpr (kXFirst) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
 #pragma unroll
         for (int q = 0; q < NIL; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         if constexpr (!BT || MF * NF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - NIL, 0);
-        if constexpr (BT && NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
       }
     }
     if (j + 1 < total_steps) {
