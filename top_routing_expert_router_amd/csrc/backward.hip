@@ -395,19 +395,30 @@ __global__ void __launch_bounds__(64) gate_bwd_kernel(const float* __restrict__ 
   }
 }
 
-// dbias[e] = sum over t of dl[t][e]: 64 experts per block, four token phases
-// summed in a fixed order.
-__global__ void __launch_bounds__(256) col_sum_kernel(const float* __restrict__ dl, float* __restrict__ out, int T,
-                                                     int E) {
-  __shared__ float part[4][64];
+// dbias[e] = sum over t of dl[t][e] in two passes of fixed order.  Pass one:
+// block (x, c) sums rows c * rows .. of 64 experts in four token phases into
+// part[c][e]; pass two adds the chunks in order.
+__global__ void __launch_bounds__(256) col_sum_part_kernel(const float* __restrict__ dl, float* __restrict__ part,
+                                                          int T, int E, int rows) {
+  __shared__ float red[4][64];
   const int el = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + el;
+  const int e = blockIdx.x * 64 + el, c = blockIdx.y;
+  const int t1 = min(T, (c + 1) * rows);
   float s = 0.0f;
   if (e < E)
-    for (int t = ph; t < T; t += 4) s += dl[(int64_t)t * E + e];
-  part[ph][el] = s;
+    for (int t = c * rows + ph; t < t1; t += 4) s += dl[(int64_t)t * E + e];
+  red[ph][el] = s;
   __syncthreads();
-  if (ph == 0 && e < E) out[e] = (part[0][el] + part[1][el]) + (part[2][el] + part[3][el]);
+  if (ph == 0 && e < E) part[(int64_t)c * E + e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
+}
+
+__global__ void __launch_bounds__(256) col_sum_final_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           int chunks, int E) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.0f;
+  for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * E + e];
+  out[e] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -579,10 +590,10 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
 // dX [R][H], fp32.  Matrix-core: u, v, z, dz [R][F], [du | dv] [R][2F] and dX
-// [R][H] in bf16 (no Y, dY).  Both end with dl [T][E] fp32, f [E] binary64 and
-// dg [T][k] fp32.
+// [R][H] in bf16 (no Y, dY).  Both end with dl [T][E] fp32, f [E] binary64, dg
+// [T][k] fp32 and the bias gradient's chunk sums [256][E] fp32.
 struct BwdLayout {
-  size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, total;
+  size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, cs, total;
 };
 
 BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast) {
@@ -601,6 +612,7 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.dl = o, o += al256(sizeof(float) * (size_t)T * (size_t)E);
   L.f = o, o += al256(sizeof(double) * (size_t)E);
   L.dg = o, o += al256(sizeof(float) * (size_t)T * (size_t)k);
+  L.cs = o, o += al256(sizeof(float) * 256 * (size_t)E);
   L.total = o + 256;
   return L;
 }
@@ -629,7 +641,11 @@ hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const floa
   g.M = H, g.N = E, g.K = T;
   if ((err = gemm(a.bf16, false, g, 1, H, st)) != hipSuccess) return err;
   if (a.dbias) {
-    col_sum_kernel<<<(E + 63) / 64, 256, 0, st>>>(dl, a.dbias, T, E);
+    float* part = reinterpret_cast<float*>(w + L.cs);
+    const int rows = T > 256 * 64 ? (T + 255) / 256 : 64, chunks = (T + rows - 1) / rows;  // chunks <= 256
+    col_sum_part_kernel<<<dim3((E + 63) / 64, chunks), 256, 0, st>>>(dl, part, T, E, rows);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    col_sum_final_kernel<<<(E + 255) / 256, 256, 0, st>>>(part, a.dbias, chunks, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   GemmArgs x{};  // dx[t][h] += sum_e dl[t][e] Wg[h][e]
