@@ -59,8 +59,10 @@ __device__ __forceinline__ void sto(uint16_t* p, int64_t i, float v) { p[i] = (u
 //   C(m, n) = C[m * scm + n * scn]  (+ the group's offsets a_g, b_g, c_g).
 // ragged 0: group g owns the rows offs[g] .. offs[g+1]-1 (global row indices for
 // A and C; A's row goes through `gather` when given); ragged 1: group g owns the
-// reduction indices offs[g] .. offs[g+1]-1 (B's row goes through `gather`).  An
-// empty reduction writes zeros (or leaves C unchanged when accumulating).
+// reduction indices offs[g] .. offs[g+1]-1 (B's row goes through `gather`).
+// With no offs and ksplit > 0, group g owns the reduction indices g*ksplit ..
+// (g+1)*ksplit-1 (a split reduction into per-group partial sums).  An empty
+// reduction writes zeros (or leaves C unchanged when accumulating).
 // ---------------------------------------------------------------------------
 template <typename TA, typename TB>
 __global__ void __launch_bounds__(256) gemm_generic_kernel(GemmArgs p) {
@@ -78,6 +80,9 @@ __global__ void __launch_bounds__(256) gemm_generic_kernel(GemmArgs p) {
       k_lo = lo;
       k_n = hi - lo;
     }
+  } else if (p.ksplit > 0) {
+    k_lo = (int64_t)g * p.ksplit;
+    k_n = (int)(p.K - k_lo < p.ksplit ? p.K - k_lo : p.ksplit);
   }
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   if (m0 >= m_n || n0 >= p.N) return;
@@ -412,6 +417,16 @@ __global__ void __launch_bounds__(256) col_sum_part_kernel(const float* __restri
   if (ph == 0 && e < E) part[(int64_t)c * E + e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
 }
 
+// out[i] = sum over g < parts of part[g * n + i], in g order.
+__global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
+                                                       float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int g = 0; g < parts; ++g) s += part[(int64_t)g * n + i];
+    out[i] = s;
+  }
+}
+
 __global__ void __launch_bounds__(256) col_sum_final_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                            int chunks, int E) {
   const int e = blockIdx.x * 256 + threadIdx.x;
@@ -591,9 +606,11 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 // Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
 // dX [R][H], fp32.  Matrix-core: u, v, z, dz [R][F], [du | dv] [R][2F] and dX
 // [R][H] in bf16 (no Y, dY).  Both end with dl [T][E] fp32, f [E] binary64, dg
-// [T][k] fp32 and the bias gradient's chunk sums [256][E] fp32.
+// [T][k] fp32, the bias gradient's chunk sums [256][E] fp32 and the router
+// weight gradient's partial sums [kRouterSplits][H][E] fp32.
+constexpr int kRouterSplits = 8;
 struct BwdLayout {
-  size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, cs, total;
+  size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, cs, rp, total;
 };
 
 BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool fast) {
@@ -613,6 +630,7 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.f = o, o += al256(sizeof(double) * (size_t)E);
   L.dg = o, o += al256(sizeof(float) * (size_t)T * (size_t)k);
   L.cs = o, o += al256(sizeof(float) * 256 * (size_t)E);
+  L.rp = o, o += al256(sizeof(float) * kRouterSplits * (size_t)H * (size_t)E);
   L.total = o + 256;
   return L;
 }
@@ -639,7 +657,21 @@ hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const floa
   g.B = dl, g.sbk = E, g.sbn = 1;
   g.C = a.dWg, g.scm = E, g.scn = 1;
   g.M = H, g.N = E, g.K = T;
-  if ((err = gemm(a.bf16, false, g, 1, H, st)) != hipSuccess) return err;
+  // a long reduction over few output tiles: split it into S chunks of tokens
+  // (partial sums, then summed in chunk order) so that the grid fills the GPU
+  const int64_t tiles = (int64_t)((E + 63) / 64) * ((H + 63) / 64);
+  int S = 1;
+  while (S < kRouterSplits && tiles * S < 2048 && T / (2 * S) >= 256) S *= 2;
+  if (S > 1) {
+    float* part = reinterpret_cast<float*>(w + L.rp);
+    g.C = part, g.c_g = (int64_t)H * E;
+    g.ksplit = (T + S - 1) / S;
+    if ((err = gemm(a.bf16, false, g, S, H, st)) != hipSuccess) return err;
+    sum_parts_kernel<<<grid_1d((int64_t)H * E, 256), 256, 0, st>>>(part, S, (int64_t)H * E, a.dWg);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  } else if ((err = gemm(a.bf16, false, g, 1, H, st)) != hipSuccess) {
+    return err;
+  }
   if (a.dbias) {
     float* part = reinterpret_cast<float*>(w + L.cs);
     const int rows = T > 256 * 64 ? (T + 255) / 256 : 64, chunks = (T + rows - 1) / rows;  // chunks <= 256

@@ -143,6 +143,7 @@ struct GemmArgs {
   int ragged;
   const int32_t* gather;
   int accumulate;
+  int ksplit;  // with no offs: group g takes the reduction indices g*ksplit .. (g+1)*ksplit-1
 };
 
 struct BackwardArgs {
