@@ -283,8 +283,11 @@ moe_status moe_forward_shared(const moe_config *cfg, const void *x, const float 
  * `plan` are constants, roundings are taken as the identity, and a dropped or
  * absent choice gets no gradient from y while still entering the Jacobian of the
  * other gates.  The residual's gradient is dy itself and is not written.  The
- * hidden activations and expert outputs are recomputed from x (no forward
- * buffers are needed). */
+ * hidden activations are recomputed from x (no forward buffers are needed).
+ * bf16 with H and F multiples of 64 and 16-byte aligned x, dy, W1, W3, W2 and
+ * ws runs on the matrix cores with bf16 intermediates (the expert weights and
+ * activations read as stored); every other case on fp32 strided products with
+ * fp32 intermediates (the expert outputs recomputed as well). */
 typedef struct {
   float *dx;    /* [T][H]    dL/dx (expert and router paths), fp32, required            */
   float *dWg;   /* [H][E]    dL/dWg, fp32, required                                     */
