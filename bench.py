@@ -639,6 +639,37 @@ def measure_backward(run, cfg, dev, up, x, wg, bias, w1, w3, w2, plan, ws, calls
            "gradient_tflops": round(flops / (us * 1e-6) / 1e12, 1), "workspace_GiB": round(bws.numel() / 2 ** 30, 2),
            "note": "fp32 gradients of x, Wg, bias, W1, W3, W2; activations recomputed from x"}
     log(f"[bench] backward: {us / 1e3:.2f} ms ({out['hbm_frac']:.3f} of the HBM floor)")
+    if cfg.dtype == B.BF16 and run.H % 64 == 0 and run.F % 8 == 0:
+        # training with the forward's pre-activations kept (moe_forward_save): the
+        # forward with and without keeping them, and the backward given them
+        R_max = max(B.max_rows(cfg), 1)
+        act = torch.empty(B.saved_act_bytes(cfg), dtype=torch.uint8, device=dev)
+        X = torch.empty((R_max, run.H), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty_like(X)
+        y = torch.empty((run.T, run.H), dtype=torch.bfloat16, device=dev)
+
+        def timed_calls(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(calls):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / calls * 1e3
+
+        f_us = timed_calls(lambda: B.forward(cfg, x, wg, bias, w1, w3, w2, x, y, plan_b, X, Y, ws))
+        fs_us = timed_calls(lambda: B.forward_save(cfg, x, wg, bias, w1, w3, w2, x, y, plan_b, X, Y, act, ws))
+        kb_us = timed_calls(lambda: B.backward(cfg, x, wg, w1, w3, w2, plan_b, dy, grads, bws, act=act))
+        out["kept_preactivations"] = {
+            "backward_ms": round(kb_us / 1e3, 4), "hbm_frac": round(floor / (kb_us * 1e-6) / 8e12, 4),
+            "forward_ms": round(f_us / 1e3, 4), "forward_save_ms": round(fs_us / 1e3, 4),
+            "kept_GiB": round(act.numel() / 2 ** 30, 3),
+            "note": "moe_forward_save keeps u (and v) for moe_backward, which then skips their recomputation"}
+        log(f"[bench] backward with kept pre-activations: {kb_us / 1e3:.2f} ms "
+            f"({out['kept_preactivations']['hbm_frac']:.3f} of the HBM floor); forward {f_us / 1e3:.3f} ms, "
+            f"keeping them {fs_us / 1e3:.3f} ms")
+        del act, X, Y, y
     del grads, bws, dy
     return out
 

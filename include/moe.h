@@ -248,6 +248,25 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, co
                        const void *W3, const void *W2, const void *residual, void *y, const moe_plan *plan,
                        void *X, void *Y, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the pre-activations moe_forward_save keeps: m1 * R_max * F * 2, m1 = 2
+ * for SwiGLU, else 1 (0 when the configuration is invalid).  Host only. */
+size_t moe_saved_act_bytes(const moe_config *cfg);
+
+/* moe_forward for training ([EP] layer walk-through: the forward's activations
+ * kept for the backward instead of recomputed): the first expert GEMM also
+ * writes its pre-activations of every kept row as bf16, act[0][row][f] = u =
+ * X W1_e^T and, for SwiGLU, act[1][row][f] = v = X W3_e^T (act: device
+ * [m1][R_max][F], 16-byte aligned, moe_saved_act_bytes; rows past offsets[E]
+ * are not written).  Passed to moe_backward with the same plan, they replace
+ * its recomputation and give the same gradients bit for bit.  y is as
+ * moe_forward's.  Only where the expert GEMMs run on the tiled bf16 path (bf16,
+ * H % 64 == 0, F % 8 == 0, 16-byte aligned buffers): MOE_ERR_UNSUPPORTED
+ * otherwise; act NULL: MOE_ERR_INVALID_ARG. */
+moe_status moe_forward_save(const moe_config *cfg, const void *x, const float *Wg, const float *bias,
+                            const void *W1, const void *W3, const void *W2, const void *residual, void *y,
+                            const moe_plan *plan, void *X, void *Y, void *act, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* ---- shared expert ([EP] layer walk-through: a dense MLP outside the router
  * and the all-to-all, run on every token, its output added to the routed
  * experts' output; Megatron-Core SharedExpertMLP, DeepSpeed Residual-MoE).  Taken
@@ -283,7 +302,8 @@ moe_status moe_forward_shared(const moe_config *cfg, const void *x, const float 
  * `plan` are constants, roundings are taken as the identity, and a dropped or
  * absent choice gets no gradient from y while still entering the Jacobian of the
  * other gates.  The residual's gradient is dy itself and is not written.  The
- * hidden activations are recomputed from x (no forward buffers are needed).
+ * hidden activations are recomputed from x (no forward buffers are needed), or
+ * taken from the pre-activations moe_forward_save kept.
  * bf16 with H and F multiples of 64 and 16-byte aligned x, dy, W1, W3, W2 and
  * ws runs on the matrix cores with bf16 intermediates (the expert weights and
  * activations read as stored); every other case on fp32 strided products with
@@ -305,14 +325,17 @@ size_t moe_backward_workspace_bytes(const moe_config *cfg);
  * W2: the expert weights (W3 iff SwiGLU).  plan: the routing moe_route made for x
  * (topk_idx, topk_gate, dst_row, demand, offsets, row_token) with plan->logits
  * written; plan->losses != NULL adds the gradients of the training terms of cfg
- * (aux_mode, aux_coeff, z_coeff, score_fn).  dy: device [T][H] dtype.  Every
+ * (aux_mode, aux_coeff, z_coeff, score_fn).  dy: device [T][H] dtype.  act: the
+ * pre-activations moe_forward_save kept for this x, plan and weights, or NULL to
+ * recompute them; used on the matrix-core path (where it must be 16-byte
+ * aligned), ignored on the other, whose fp32 intermediates are recomputed.  Every
  * sum is accumulated in fp32 in a fixed order (binary64 inside the per-token
  * gate Jacobian), so results are deterministic.  ws: device, >=
  * moe_backward_workspace_bytes.  The shared expert is not part of this
  * gradient. */
 moe_status moe_backward(const moe_config *cfg, const void *x, const float *Wg, const void *W1, const void *W3,
-                        const void *W2, const moe_plan *plan, const void *dy, const moe_grads *grads, void *ws,
-                        size_t ws_bytes, void *stream);
+                        const void *W2, const moe_plan *plan, const void *dy, const void *act,
+                        const moe_grads *grads, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

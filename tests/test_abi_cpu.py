@@ -73,6 +73,16 @@ def test_capacity_and_rows_match_oracle(name):
     assert B.workspace_bytes(c) >= rmax * r.F * r.elem_bytes
 
 
+@pytest.mark.parametrize("name", list(recipes.RUNS))
+def test_saved_act_bytes(name):
+    """moe_saved_act_bytes: u (and v for SwiGLU) of every packed row, bf16."""
+    r = recipes.RUNS[name]
+    c = B.MoEConfig.from_run(r)
+    m1 = 2 if r.act == recipes.SWIGLU else 1
+    assert B.saved_act_bytes(c) == m1 * B.max_rows(c) * r.F * 2
+    assert B.saved_act_bytes(_cfg(k=0)) == 0
+
+
 def test_min_capacity_floor():
     c = _cfg(T=10, E=8, k=1, capacity_factor=1.0, min_capacity=4)
     assert B.capacity(c) == 4
@@ -111,6 +121,15 @@ def test_entry_points_reject_before_launch():
     assert L.moe_forward(ctypes.byref(cc), 256, None, None, 256, None, 256, None, 256, ctypes.byref(good), 256, 256,
                          256, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_validate(None) == B.MOE_ERR_INVALID_ARG
+    # moe_forward_save: act required; only the tiled bf16 path keeps pre-activations
+    assert L.moe_forward_save(ctypes.byref(cc), 256, 256, None, 256, None, 256, None, 256, ctypes.byref(good), 256,
+                              256, None, 256, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    f32 = _cfg(dtype=B.F32).c()
+    assert L.moe_forward_save(ctypes.byref(f32), 256, 256, None, 256, None, 256, None, 256, ctypes.byref(good), 256,
+                              256, 256, 256, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    odd = _cfg(H=96).c()  # H % 64 != 0: not the tiled path
+    assert L.moe_forward_save(ctypes.byref(odd), 256, 256, None, 256, None, 256, None, 256, ctypes.byref(good), 256,
+                              256, 256, 256, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
     # shared expert: needs shared_F > 0, its weights (Ws3 iff SwiGLU) and the workspace
     sh = _cfg(shared_F=384)
     shc = sh.c()

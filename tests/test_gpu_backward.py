@@ -105,6 +105,60 @@ def _compare(what, got, ref, tol=GRAD_RELL2):
         assert mx <= 10 * tol, (what, n, mx)
 
 
+@pytest.mark.parametrize("name", ["2", "3a", "4", "5"])
+def test_backward_with_kept_preactivations(gpu, name):
+    """moe_forward_save keeps the first expert GEMM's pre-activations (u, and v for
+    SwiGLU) of every kept row.  Its layer output equals moe_forward's bit for bit; the
+    kept values are the oracle's X W1_e^T (X W3_e^T) within their bf16 rounding; and
+    moe_backward given them returns, bit for bit, the gradients it computes when it
+    recomputes them (both come from the same k-ordered products)."""
+    import torch
+
+    r = recipes.SMALL[name]
+    d = _inputs(r)
+    cfg = B.MoEConfig.from_run(r)
+    R_max = B.max_rows(cfg)
+    x, wg, bias = U.dev(d["x"], gpu), U.dev(d["wg"], gpu), U.dev(d["bias"], gpu)
+    w1, w3, w2 = U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu)
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    X = torch.empty((max(R_max, 1), r.H), dtype=torch.bfloat16, device=gpu)
+    Y = torch.empty_like(X)
+    y0 = torch.empty((r.T, r.H), dtype=torch.bfloat16, device=gpu)
+    y1 = torch.empty_like(y0)
+    ws = B.alloc_workspace(cfg, gpu)
+    B.forward(cfg, x, wg, bias, w1, w3, w2, x, y0, plan, X, Y, ws)
+    m1 = 2 if r.act == recipes.SWIGLU else 1
+    assert B.saved_act_bytes(cfg) == m1 * R_max * r.F * 2
+    act = torch.full((m1, R_max, r.F), float("nan"), dtype=torch.bfloat16, device=gpu)
+    B.forward_save(cfg, x, wg, bias, w1, w3, w2, x, y1, plan, X, Y, act, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), "forward_save changed y"
+
+    oplan = oracle.route(d["x"], r.dtype, d["wg"], d["bias"], r.k, r.gate_mode, _cap(r))
+    U.assert_plan_equal(plan, oplan, f"kept {name}")
+    R, off = oplan["R"], oplan["offsets"]
+    Xo = U.as_f64(oracle.dispatch(d["x"], r.dtype, oplan))
+    kept = U.as_f64(U.host(act))
+    for j, wn in enumerate(["w1", "w3"][:m1]):
+        W = U.as_f64(d[wn])
+        ref = np.zeros((R, r.F))
+        for e in range(r.E):
+            ref[off[e]:off[e + 1]] = Xo[off[e]:off[e + 1]] @ W[e].T
+        U.assert_close(kept[j, :R], ref, True, f"kept {name} {'uv'[j]}")
+
+    dy = U.dev(d["dy"], gpu)
+    bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=gpu)
+    outs = []
+    for a in (None, act):
+        grads = B.alloc_grads(cfg, gpu, bias=True, dg=True)
+        B.backward(cfg, x, wg, w1, w3, w2, plan, dy, grads, bws, act=a)
+        torch.cuda.synchronize()
+        outs.append({n: t.cpu() for n, t in grads.items()})
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), (name, n)
+    print(f"[backward] kept pre-activations {name}: gradients equal to the recomputed path", flush=True)
+
+
 @pytest.mark.parametrize("name", ["1", "2", "3a", "3c", "4", "5"])
 def test_backward_matches_oracle(gpu, name):
     r = recipes.SMALL[name]

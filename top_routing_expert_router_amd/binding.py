@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 EXPORTS = ("moe_validate", "moe_capacity", "moe_max_rows", "moe_workspace_bytes", "moe_status_str",
            "moe_last_error", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
            "moe_shared_expert", "moe_combine_shared", "moe_forward_shared", "moe_route_noalloc",
-           "moe_backward_workspace_bytes", "moe_backward")
+           "moe_backward_workspace_bytes", "moe_backward", "moe_saved_act_bytes", "moe_forward_save")
 
 
 class MoEError(RuntimeError):
@@ -124,7 +124,11 @@ def lib():
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward_workspace_bytes.argtypes = [cfgp]
         L.moe_backward.restype = ctypes.c_int
-        L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, planp, vp, ctypes.POINTER(_Grads), vp, sz, vp]
+        L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, planp, vp, vp, ctypes.POINTER(_Grads), vp, sz, vp]
+        L.moe_saved_act_bytes.restype = sz
+        L.moe_saved_act_bytes.argtypes = [cfgp]
+        L.moe_forward_save.restype = ctypes.c_int
+        L.moe_forward_save.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, planp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -243,6 +247,20 @@ def forward(cfg, x, wg, bias, w1, w3, w2, residual, y, plan, X, Y, ws, stream=No
     _check(st, "moe_forward")
 
 
+def saved_act_bytes(cfg: MoEConfig):
+    return int(lib().moe_saved_act_bytes(ctypes.byref(cfg.c())))
+
+
+def forward_save(cfg, x, wg, bias, w1, w3, w2, residual, y, plan, X, Y, act, ws, stream=None):
+    """moe_forward_save: moe_forward that also keeps the first GEMM's pre-activations in act
+    (a uint8 or bf16 device tensor of saved_act_bytes bytes)."""
+    c, p = cfg.c(), _plan_struct(plan)
+    st = lib().moe_forward_save(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2),
+                                _ptr(residual), _ptr(y), ctypes.byref(p), _ptr(X), _ptr(Y), _ptr(act), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream))
+    _check(st, "moe_forward_save")
+
+
 def shared_expert(cfg, x, ws1, ws3, ws2, Ys, ws, stream=None):
     c = cfg.c()
     st = lib().moe_shared_expert(ctypes.byref(c), _ptr(x), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(Ys), _ptr(ws),
@@ -286,10 +304,12 @@ def alloc_grads(cfg: MoEConfig, device, bias=True, dg=False):
     return g
 
 
-def backward(cfg, x, wg, w1, w3, w2, plan, dy, grads, ws, stream=None):
-    """moe_backward: grads is a dict of device tensors (see alloc_grads)."""
+def backward(cfg, x, wg, w1, w3, w2, plan, dy, grads, ws, stream=None, act=None):
+    """moe_backward: grads is a dict of device tensors (see alloc_grads); act: the
+    pre-activations forward_save kept, or None to recompute them."""
     c, p = cfg.c(), _plan_struct(plan)
     gs = _Grads(*[_ptr(grads.get(n)) for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dg")])
     st = lib().moe_backward(ctypes.byref(c), _ptr(x), _ptr(wg), _ptr(w1), _ptr(w3), _ptr(w2), ctypes.byref(p),
-                            _ptr(dy), ctypes.byref(gs), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+                            _ptr(dy), _ptr(act), ctypes.byref(gs), _ptr(ws), ws.numel() if ws is not None else 0,
+                            _stream(stream))
     _check(st, "moe_backward")

@@ -14,7 +14,9 @@
 //
 // The forward's hidden activations and expert outputs are recomputed from x
 // and the plan (activation checkpointing): u = x W1^T (and v = x W3^T), z =
-// act(u) (or silu(u) * v), Y = z W2^T.  Then
+// act(u) (or silu(u) * v), Y = z W2^T; on the matrix-core path u and v may
+// instead come from the forward, which can keep them (no recomputation, the
+// same values).  Then
 //   dY = g * dy (kept rows), dg = <Y, dy>;
 //   dz = dY W2;  du = dz * act'(u)  (SwiGLU: du = dz v silu'(u), dv = dz silu(u));
 //   dX = du W1 (+ dv W3);  dx = sum of the token's kept rows of dX;
@@ -759,8 +761,11 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   const int mr = (int)(R_max < INT32_MAX ? R_max : INT32_MAX);  // rows bound of the ragged-M grids
 
   if (a.fast) {
-    uint16_t* u = reinterpret_cast<uint16_t*>(w + L.u);
-    uint16_t* v = reinterpret_cast<uint16_t*>(w + L.v);
+    uint16_t* u_ws = reinterpret_cast<uint16_t*>(w + L.u);  // recomputed u, v
+    uint16_t* v_ws = reinterpret_cast<uint16_t*>(w + L.v);
+    // u and v as read below: the recomputed ones, or those the forward kept
+    const uint16_t* u = a.saved ? static_cast<const uint16_t*>(a.saved) : u_ws;
+    const uint16_t* v = a.saved ? u + (size_t)R_max * F : v_ws;
     uint16_t* z = reinterpret_cast<uint16_t*>(w + L.z);
     uint16_t* dz = reinterpret_cast<uint16_t*>(w + L.dz);
     uint16_t* dcat = reinterpret_cast<uint16_t*>(w + L.du);  // [R][2F]: du | dv (or [R][F])
@@ -768,9 +773,12 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
     const int64_t rc = a.rows_cap;
     if (R_max > 0) {
-      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T, z
-      MOE_BW(launch_grouped_gemm_bf16(a.x, a.W1, u, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
-      if (gated) MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T (unless kept), z
+      if (!a.saved) {
+        MOE_BW(launch_grouped_gemm_bf16(a.x, a.W1, u_ws, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+        if (gated)
+          MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v_ws, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
+      }
       act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
       MOE_BW(hipGetLastError());
     }

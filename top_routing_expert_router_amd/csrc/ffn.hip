@@ -316,6 +316,11 @@ __global__ void __launch_bounds__(64) grouped_gemm_scalar_kernel(const void* __r
 // k-rows x 4 chunks, which the swizzle puts in 16 distinct bank groups.  W2 is
 // then an optional second weight tensor that continues the contraction: k < k1
 // from W ([E][k1][N]), k >= k1 from W2 (same shape, K = 2 k1).
+//
+// SAVE (first GEMM only): the pre-activations of every output element are also
+// stored as bf16 for the backward, u = X W_e^T at save[row][n] and, for
+// SwiGLU, v = X W3_e^T at save[rmax + row][n] (rows of N), with the same lane
+// swaps and 16-byte stores as the activation.
 // ---------------------------------------------------------------------------
 struct PipeTile {
   int e, row0, rows, n0;
@@ -385,7 +390,7 @@ __device__ __forceinline__ int clamp_row(int tok, int xrows) { return tok < 0 ? 
 // BM token rows x WR weight rows per tile, BK k per stage, S stages, NW waves
 // as WGM (token direction) x NW / WGM (weight direction); at most 256 registers
 // per wave (two waves per SIMD: one workgroup of 8 waves or two of 4 per CU).
-template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW, bool NTW, bool BT = false>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, int NW, bool NTW, bool BT = false, bool SAVE = false>
 __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uint16_t* __restrict__ A,
                                                                    const uint16_t* __restrict__ W,
                                                                    const uint16_t* __restrict__ W2,
@@ -393,7 +398,8 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
                                                                    const int32_t* __restrict__ offsets, int E,
                                                                    int N, int K, int rmax,
                                                                    const int32_t* __restrict__ gather, int xrows,
-                                                                   Combine1 cmb, int rlo, int rhi, int k1) {
+                                                                   Combine1 cmb, int rlo, int rhi, int k1,
+                                                                   uint16_t* __restrict__ save) {
   constexpr bool kGated = EPI == EPI_SWIGLU;
   constexpr int BN = kGated ? WR / 2 : WR;                // output columns per tile
   constexpr int ROWS = BM + WR;                           // rows per stage
@@ -411,6 +417,7 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
   static_assert(BT || MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
   static_assert(!BT || (EPI == EPI_NONE && WR % 128 == 0), "k-major weights: plain products, 16+ chunks per k-row");
+  static_assert(!SAVE || EPI == EPI_RELU || EPI == EPI_GELU || EPI == EPI_SWIGLU, "pre-activations of the first GEMM");
   constexpr int NRD = MF + (BT ? 2 : 1) * NF;              // LDS reads per k-step
   constexpr int NIL = MF * NF < NRD ? MF * NF : NRD;        // of them interleaved one by one with MFMAs
   // more reads than MFMAs per k-step (k-major 128-row tiles): the extra reads go
@@ -651,6 +658,25 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
             u32x4_t o = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
             if constexpr (EPI == EPI_COMBINE1) o = combine1_8(o, rv[f][g / 2], gt);
             if (n < N) *reinterpret_cast<u32x4_t*>(crow + n) = o;
+            if constexpr (SAVE) {
+              {  // the pre-activations, rounded to bf16 (the same swaps as above)
+#pragma unroll
+                for (int part = 0; part < (kGated ? 2 : 1); ++part) {
+                  const int fa = part ? HF + f : f;
+                  uint32_t pa[2][2];
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    pa[h][0] = pack_bf16x2(acc[fa][i][4 * (g + h)], acc[fa][i][4 * (g + h) + 1]);
+                    pa[h][1] = pack_bf16x2(acc[fa][i][4 * (g + h) + 2], acc[fa][i][4 * (g + h) + 3]);
+                  }
+                  const auto a0 = __builtin_amdgcn_permlane32_swap(pa[0][0], pa[1][0], false, false);
+                  const auto a1 = __builtin_amdgcn_permlane32_swap(pa[0][1], pa[1][1], false, false);
+                  if (n < N)
+                    *reinterpret_cast<u32x4_t*>(save + ((size_t)part * rmax + crow_i) * N + n) =
+                        u32x4_t{a0[0], a1[0], a0[1], a1[1]};
+                }
+              }
+            }
           }
       }
     }
@@ -1060,10 +1086,11 @@ static hipError_t launch_ring(const void* A, const void* B, const void* B2, void
 }
 
 // rlo, rhi: only the experts with rlo < rows <= rhi
-template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8, bool BT = false>
+template <int BM, int WR, int BK, int S, int WGM, int EPI, bool NTW, int NW = 8, bool BT = false, bool SAVE = false>
 static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
                               int N, int K, int64_t R_max, int cus, const int32_t* gather, int xrows,
-                              const Combine1& cmb, hipStream_t st, int rlo = -1, int rhi = INT32_MAX, int k1 = 0) {
+                              const Combine1& cmb, hipStream_t st, int rlo = -1, int rhi = INT32_MAX, int k1 = 0,
+                              uint16_t* save = nullptr) {
   constexpr int BN = EPI == EPI_SWIGLU ? WR / 2 : WR;
   const int ntn = (N + BN - 1) / BN;
   const int64_t tiles = ((R_max + BM - 1) / BM + (R_max < E ? R_max : E)) * ntn;
@@ -1072,11 +1099,11 @@ static hipError_t launch_pipe(const void* A, const void* B, const void* B2, void
   const int grid = (int)(tiles < slots ? tiles : slots);
   const size_t shm = sizeof(uint16_t) * (size_t)S * (BM + WR) * BK + sizeof(int) * 2 * (size_t)(E + 1);
   constexpr int kMaxShm = sizeof(uint16_t) * S * (BM + WR) * BK + sizeof(int) * 2 * (1024 + 1);  // E <= 1024
-  hipError_t err = lds_limit_once<grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT>>(kMaxShm);
+  hipError_t err = lds_limit_once<grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT, SAVE>>(kMaxShm);
   if (err != hipSuccess) return err;
-  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT><<<dim3(grid), dim3(64 * NW), shm, st>>>(
+  grouped_gemm_pipe_kernel<BM, WR, BK, S, WGM, EPI, NW, NTW, BT, SAVE><<<dim3(grid), dim3(64 * NW), shm, st>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(B2),
-      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb, rlo, rhi, k1);
+      static_cast<uint16_t*>(C), offsets, E, N, K, (int)R_max, gather, xrows, cmb, rlo, rhi, k1, save);
   return hipGetLastError();
 }
 
@@ -1107,11 +1134,11 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool SAVE = false>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
                              const int32_t* offsets, int E, int N, int K, int64_t R_max, int64_t rows_cap,
                              hipStream_t st, const int32_t* gather = nullptr, int xrows = 0,
-                             const Combine1& cmb = Combine1{}) {
+                             const Combine1& cmb = Combine1{}, uint16_t* save = nullptr) {
   if (vec && bf16 && K % 64 == 0) {
     int cus = 0;
     hipError_t err = device_cus(&cus);
@@ -1122,6 +1149,20 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
     // token stages, three weight stages).  Otherwise 128 x 256 tiles (three
     // 48 KB stages).
     constexpr bool kGated = EPI == EPI_SWIGLU;
+    // the pipe tiles: BM x 256 with three 48 KB stages (BM = 128) or two 64 KB
+    // stages (BM = 256); ntw: weight loads non-temporal (one m-tile per expert)
+    auto pipe128 = [&](bool ntw, int rlo, int rhi) {
+      return ntw ? launch_pipe<128, 256, 64, 3, 2, EPI, true, 8, false, SAVE>(A, B, B2, C, offsets, E, N, K, R_max, cus,
+                                                                              gather, xrows, cmb, st, rlo, rhi, 0, save)
+                 : launch_pipe<128, 256, 64, 3, 2, EPI, false, 8, false, SAVE>(
+                       A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st, rlo, rhi, 0, save);
+    };
+    auto pipe256 = [&](bool ntw, int rlo) {
+      return ntw ? launch_pipe<256, 256, 64, 2, 2, EPI, true, 8, false, SAVE>(
+                       A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st, rlo, INT32_MAX, 0, save)
+                 : launch_pipe<256, 256, 64, 2, 2, EPI, false, 8, false, SAVE>(
+                       A, B, B2, C, offsets, E, N, K, R_max, cus, gather, xrows, cmb, st, rlo, INT32_MAX, 0, save);
+    };
     if (R_max / E > 128) {
       auto fill = [&](int bn) {
         const int64_t tiles = (R_max / 256) * ((N + bn - 1) / bn);
@@ -1129,15 +1170,12 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
         return waves > 0 ? (double)tiles / (double)(waves * cus) : 0.0;
       };
       if constexpr (!kGated)
-        if (fill(192) > fill(256) + 0.05)
+        if (fill(192) > fill(256) + 0.05 && !SAVE)
           return rows_cap <= 256 ? launch_ring<256, 192, 3, 4, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
                                                                            gather, xrows, cmb, st)
                                  : launch_ring<256, 192, 3, 4, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
                                                                             gather, xrows, cmb, st);
-      return rows_cap <= 256 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
-                                                                          gather, xrows, cmb, st)
-                             : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
-                                                                           gather, xrows, cmb, st);
+      return pipe256(rows_cap <= 256, -1);
     }
     // With experts of more than 128 rows possible, those take 256 x 256 tiles
     // (a CU's loads per stage carry twice the MFMA work) in a launch of their
@@ -1145,22 +1183,15 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
     // also handles the dropped tokens once per launch: kept in one launch.)
     if constexpr (EPI != EPI_COMBINE1) {
       if (rows_cap > 128) {
-        hipError_t e1 = launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus, gather,
-                                                                   xrows, cmb, st, -1, 128);
+        hipError_t e1 = pipe128(true, -1, 128);
         if (e1 != hipSuccess) return e1;
-        return rows_cap <= 256 ? launch_pipe<256, 256, 64, 2, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
-                                                                            gather, xrows, cmb, st, 128)
-                               : launch_pipe<256, 256, 64, 2, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max,
-                                                                             cus, gather, xrows, cmb, st, 128);
+        return pipe256(rows_cap <= 256, 128);
       }
     }
-    return rows_cap <= 128 ? launch_pipe<128, 256, 64, 3, 2, EPI, true>(A, B, B2, C, offsets, E, N, K, R_max, cus,
-                                                                        gather, xrows, cmb, st)
-                           : launch_pipe<128, 256, 64, 3, 2, EPI, false>(A, B, B2, C, offsets, E, N, K, R_max, cus,
-                                                                         gather, xrows, cmb, st);
+    return pipe128(rows_cap <= 128, -1, INT32_MAX);
   }
-  // only the tiled kernels read gathered rows or combine
-  if (gather || EPI == EPI_COMBINE1) return hipErrorInvalidValue;
+  // only the tiled kernels read gathered rows, combine or keep pre-activations
+  if (gather || EPI == EPI_COMBINE1 || SAVE) return hipErrorInvalidValue;
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
@@ -1183,24 +1214,36 @@ hipError_t device_cus(int* cus) {
 
 bool expert_ffn_gathers(bool bf16, bool vec, int H) { return bf16 && vec && H % 64 == 0; }
 bool expert_ffn_combines(bool bf16, bool vec, int H, int F) { return bf16 && vec && H % 8 == 0 && F % 64 == 0; }
+bool expert_ffn_saves(bool bf16, bool vec, int H, int F) { return bf16 && vec && H % 64 == 0 && F % 8 == 0; }
 
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
                              int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather, int xrows,
-                             const Combine1* cmb) {
+                             const Combine1* cmb, void* saved) {
   if (R_max == 0) return cmb ? hipErrorInvalidValue : hipSuccess;  // the combine needs a launch to run in
   if (gather && !expert_ffn_gathers(bf16, vec, H)) return hipErrorInvalidValue;
+  if (saved && !expert_ffn_saves(bf16, vec, H, F)) return hipErrorInvalidValue;
+  uint16_t* save = static_cast<uint16_t*>(saved);
   if (cmb && !expert_ffn_combines(bf16, vec, H, F)) return hipErrorInvalidValue;
   hipError_t err;
   switch (act) {
     case 0:
-      err = launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
+      err = save ? launch_one<EPI_RELU, true>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st,
+                                              gather, xrows, Combine1{}, save)
+                 : launch_one<EPI_RELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather,
+                                        xrows);
       break;
     case 1:
-      err = launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
+      err = save ? launch_one<EPI_GELU, true>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st,
+                                              gather, xrows, Combine1{}, save)
+                 : launch_one<EPI_GELU>(vec, bf16, X, W1, nullptr, h, offsets, E, F, H, R_max, rows_cap, st, gather,
+                                        xrows);
       break;
     default:
-      err = launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, rows_cap, st, gather, xrows);
+      err = save ? launch_one<EPI_SWIGLU, true>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, rows_cap, st,
+                                                gather, xrows, Combine1{}, save)
+                 : launch_one<EPI_SWIGLU>(vec, bf16, X, W1, W3, h, offsets, E, F, H, R_max, rows_cap, st, gather,
+                                          xrows);
       break;
   }
   if (err != hipSuccess) return err;

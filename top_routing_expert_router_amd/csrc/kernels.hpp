@@ -112,11 +112,15 @@ struct Combine1 {
 // rows_cap: most rows any one expert can hold (the capacity, or R_max when
 // nothing caps it); at most one m-tile per expert lets the weight loads stream.
 // cmb (optional, bf16 tiled path only, see expert_ffn_combines): Y is then the
-// layer output y [T][H] instead of the expert rows.
+// layer output y [T][H] instead of the expert rows.  save (optional, tiled path
+// only, see expert_ffn_saves): the first GEMM's pre-activations are also kept,
+// [m1][R_max][F] bf16 (u, then v for SwiGLU).
 hipError_t launch_expert_ffn(const void* X, const void* W1, const void* W3, const void* W2, void* h, void* Y,
                              const int32_t* offsets, int E, int H, int F, int act, bool bf16, bool vec,
                              int64_t R_max, int64_t rows_cap, hipStream_t st, const int32_t* gather = nullptr,
-                             int xrows = 0, const Combine1* cmb = nullptr);
+                             int xrows = 0, const Combine1* cmb = nullptr, void* save = nullptr);
+// whether launch_expert_ffn can keep the pre-activations for these shapes
+bool expert_ffn_saves(bool bf16, bool vec, int H, int F);
 // whether launch_expert_ffn can take cmb for these shapes
 bool expert_ffn_combines(bool bf16, bool vec, int H, int F);
 // shared (optional): the shared expert's output [T][H], added after the routed terms.
@@ -159,6 +163,7 @@ struct BackwardArgs {
   const int32_t *topk_idx, *dst_row, *offsets, *row_token, *demand;
   const float *topk_gate, *logits;
   const void* dy;
+  const void* saved;  // the forward's pre-activations [m1][R_max][F] bf16, or null (recomputed)
   float *dx, *dWg, *dbias, *dW1, *dW3, *dW2, *dg;  // dbias, dg optional
   void* ws;
 };

@@ -374,16 +374,21 @@ moe_status moe_combine(const moe_config* c, const void* Y, const moe_plan* plan,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine");
 }
 
-moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
-                       const void* W3, const void* W2, const void* residual, void* y, const moe_plan* plan, void* X,
-                       void* Y, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward, and with act != nullptr moe_forward_save (the first GEMM's
+// pre-activations kept, tiled bf16 path only).
+moe_status forward_impl(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
+                        const void* W3, const void* W2, const void* residual, void* y, const moe_plan* plan, void* X,
+                        void* Y, void* act, void* ws, size_t ws_bytes, void* stream) {
   moe_status s = moe_validate(c);
   if (s != MOE_OK) return s;
   if ((s = check_plan(c, plan)) != MOE_OK) return s;
   if (!W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr) || !Wg) return MOE_ERR_INVALID_ARG;
   if (c->T > 0 && (!x || !y || !X || !Y)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < layout_of(c).total) return MOE_ERR_WORKSPACE;
-  if ((s = moe_route(c, x, Wg, bias, plan, ws, ws_bytes, stream)) != MOE_OK) return s;
   // Where the tiled bf16 GEMMs run, the first one reads the token rows of x
   // through plan->row_token itself and the dispatch copy is skipped (X unused).
   const int64_t R_max = max_rows_of(c);
@@ -391,7 +396,10 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
   const bool bf16 = c->dtype == MOE_BF16;
   const bool vec = c->H % 8 == 0 && c->F % 8 == 0 && aligned16(x) && aligned16(Y) && aligned16(W1) &&
                    aligned16(W3) && aligned16(W2) && aligned16(h);
-  if (R_max > 0 && c->T > 0 && moe::expert_ffn_gathers(bf16, vec, c->H)) {
+  const bool tiled = moe::expert_ffn_gathers(bf16, vec, c->H);
+  if (act && (!tiled || !moe::expert_ffn_saves(bf16, vec, c->H, c->F) || !aligned16(act))) return MOE_ERR_UNSUPPORTED;
+  if ((s = moe_route(c, x, Wg, bias, plan, ws, ws_bytes, stream)) != MOE_OK) return s;
+  if (R_max > 0 && c->T > 0 && tiled) {
     // Top-1 on the same path: the second GEMM writes y itself (Y unused).
     const bool fuse = c->k == 1 && moe::expert_ffn_combines(bf16, vec, c->H, c->F) && aligned16(residual) &&
                       aligned16(y);
@@ -400,7 +408,7 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
     hipError_t e = moe::launch_expert_ffn(x, W1, W3, W2, h, fuse ? y : Y, plan->offsets, c->E, c->H, c->F, c->act,
                                           bf16, vec, R_max, expert_rows_cap(c, R_max),
                                           static_cast<hipStream_t>(stream), plan->row_token, c->T,
-                                          fuse ? &cmb : nullptr);
+                                          fuse ? &cmb : nullptr, act);
     if (e != hipSuccess) return hip_fail(e, "expert_ffn");
     if (fuse) return MOE_OK;
   } else {
@@ -408,6 +416,28 @@ moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, cons
     if ((s = moe_expert_ffn(c, X, plan, W1, W3, W2, Y, ws, ws_bytes, stream)) != MOE_OK) return s;
   }
   return moe_combine(c, Y, plan, residual, y, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
+                       const void* W3, const void* W2, const void* residual, void* y, const moe_plan* plan, void* X,
+                       void* Y, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(c, x, Wg, bias, W1, W3, W2, residual, y, plan, X, Y, nullptr, ws, ws_bytes, stream);
+}
+
+size_t moe_saved_act_bytes(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return 0;
+  return (c->act == MOE_SWIGLU ? 2 : 1) * (size_t)max_rows_of(c) * (size_t)c->F * 2;
+}
+
+moe_status moe_forward_save(const moe_config* c, const void* x, const float* Wg, const float* bias, const void* W1,
+                            const void* W3, const void* W2, const void* residual, void* y, const moe_plan* plan,
+                            void* X, void* Y, void* act, void* ws, size_t ws_bytes, void* stream) {
+  if (!act) return MOE_ERR_INVALID_ARG;
+  return forward_impl(c, x, Wg, bias, W1, W3, W2, residual, y, plan, X, Y, act, ws, ws_bytes, stream);
 }
 
 moe_status moe_shared_expert(const moe_config* c, const void* x, const void* Ws1, const void* Ws3, const void* Ws2,
@@ -480,8 +510,8 @@ moe_status moe_forward_shared(const moe_config* c, const void* x, const float* W
 }
 
 moe_status moe_backward(const moe_config* c, const void* x, const float* Wg, const void* W1, const void* W3,
-                        const void* W2, const moe_plan* plan, const void* dy, const moe_grads* g, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const void* W2, const moe_plan* plan, const void* dy, const void* act, const moe_grads* g,
+                        void* ws, size_t ws_bytes, void* stream) {
   moe_status s = moe_validate(c);
   if (s != MOE_OK) return s;
   if (!g || !plan || !Wg || !W1 || !W2 || (c->act == MOE_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
@@ -507,6 +537,7 @@ moe_status moe_backward(const moe_config* c, const void* x, const float* Wg, con
   a.topk_idx = plan->topk_idx, a.dst_row = plan->dst_row, a.offsets = plan->offsets, a.row_token = plan->row_token;
   a.demand = plan->demand, a.topk_gate = plan->topk_gate, a.logits = plan->logits;
   a.dy = dy;
+  a.saved = a.fast && aligned16(act) ? act : nullptr;  // the generic path recomputes in fp32
   a.dx = g->dx, a.dWg = g->dWg, a.dbias = g->dbias, a.dW1 = g->dW1, a.dW3 = g->dW3, a.dW2 = g->dW2, a.dg = g->dg;
   a.ws = ws;
   hipError_t e = moe::launch_backward(a, static_cast<hipStream_t>(stream));
