@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(64) gate_bwd_kernel(const float* __restrict__ 
 
 // dbias[e] = sum over t of dl[t][e] in two passes of fixed order.  Pass one:
 // block (x, c) sums rows c * rows .. of 64 experts in four token phases into
-// part[c][e]; pass two adds the chunks in order.
+// part[c][e]; pass two adds the chunks, in four phases per expert.
 __global__ void __launch_bounds__(256) col_sum_part_kernel(const float* __restrict__ dl, float* __restrict__ part,
                                                           int T, int E, int rows) {
   __shared__ float red[4][64];
@@ -431,11 +431,14 @@ __global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict_
 
 __global__ void __launch_bounds__(256) col_sum_final_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                            int chunks, int E) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
+  __shared__ float red[4][64];
+  const int el = threadIdx.x & 63, ph = threadIdx.x >> 6, e = blockIdx.x * 64 + el;
   float s = 0.0f;
-  for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * E + e];
-  out[e] = s;
+  if (e < E)
+    for (int c = ph; c < chunks; c += 4) s += part[(int64_t)c * E + e];
+  red[ph][el] = s;
+  __syncthreads();
+  if (ph == 0 && e < E) out[e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
 }
 
 // ---------------------------------------------------------------------------
@@ -608,9 +611,18 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 // Workspace of the two paths.  Generic: u, v, z, dz, du, dv [R][F] and Y, dY,
 // dX [R][H], fp32.  Matrix-core: u, v, z, dz [R][F], [du | dv] [R][2F] and dX
 // [R][H] in bf16 (no Y, dY).  Both end with dl [T][E] fp32, f [E] binary64, dg
-// [T][k] fp32, the bias gradient's chunk sums [256][E] fp32 and the router
-// weight gradient's partial sums [kRouterSplits][H][E] fp32.
-constexpr int kRouterSplits = 8;
+// [T][k] fp32, the bias gradient's chunk sums [64][E] fp32 and the router
+// weight gradient's partial sums [router_splits][H][E] fp32.
+
+// Chunks of tokens the router weight gradient's reduction is split into: the
+// grid of its output tiles times the chunks should fill the GPU (2048
+// workgroups), each chunk keeping at least 256 tokens, at most 64 chunks.
+int router_splits(int64_t T, int H, int E) {
+  const int64_t tiles = (int64_t)((E + 63) / 64) * ((H + 63) / 64);
+  int S = 1;
+  while (S < 64 && tiles * S < 2048 && T / (2 * S) >= 256) S *= 2;
+  return S;
+}
 struct BwdLayout {
   size_t u, v, z, dz, du, Y, dY, dX, dl, f, dg, cs, rp, total;
 };
@@ -631,8 +643,9 @@ BwdLayout bwd_layout(int64_t T, int H, int E, int k, int F, int64_t R_max, bool 
   L.dl = o, o += al256(sizeof(float) * (size_t)T * (size_t)E);
   L.f = o, o += al256(sizeof(double) * (size_t)E);
   L.dg = o, o += al256(sizeof(float) * (size_t)T * (size_t)k);
-  L.cs = o, o += al256(sizeof(float) * 256 * (size_t)E);
-  L.rp = o, o += al256(sizeof(float) * kRouterSplits * (size_t)H * (size_t)E);
+  L.cs = o, o += al256(sizeof(float) * 64 * (size_t)E);
+  const int S = router_splits(T, H, E);
+  L.rp = o, o += S > 1 ? al256(sizeof(float) * S * (size_t)H * (size_t)E) : 0;
   L.total = o + 256;
   return L;
 }
@@ -661,9 +674,7 @@ hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const floa
   g.M = H, g.N = E, g.K = T;
   // a long reduction over few output tiles: split it into S chunks of tokens
   // (partial sums, then summed in chunk order) so that the grid fills the GPU
-  const int64_t tiles = (int64_t)((E + 63) / 64) * ((H + 63) / 64);
-  int S = 1;
-  while (S < kRouterSplits && tiles * S < 2048 && T / (2 * S) >= 256) S *= 2;
+  const int S = router_splits(T, H, E);
   if (S > 1) {
     float* part = reinterpret_cast<float*>(w + L.rp);
     g.C = part, g.c_g = (int64_t)H * E;
@@ -676,10 +687,10 @@ hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const floa
   }
   if (a.dbias) {
     float* part = reinterpret_cast<float*>(w + L.cs);
-    const int rows = T > 256 * 64 ? (T + 255) / 256 : 64, chunks = (T + rows - 1) / rows;  // chunks <= 256
+    const int rows = T > 64 * 64 ? (T + 63) / 64 : 64, chunks = (T + rows - 1) / rows;  // chunks <= 64
     col_sum_part_kernel<<<dim3((E + 63) / 64, chunks), 256, 0, st>>>(dl, part, T, E, rows);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    col_sum_final_kernel<<<(E + 255) / 256, 256, 0, st>>>(part, a.dbias, chunks, E);
+    col_sum_final_kernel<<<(E + 63) / 64, 256, 0, st>>>(part, a.dbias, chunks, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   GemmArgs x{};  // dx[t][h] += sum_e dl[t][e] Wg[h][e]
