@@ -238,13 +238,18 @@ __global__ void __launch_bounds__(256) gather_sum_kernel(const T* __restrict__ d
 
 // Matrix-core path, one block per token, for each kept choice (row = its packed
 // row, g = its gate), from dzr = dy[t] W2_e (the rows of the dz product taken on
-// the token's unscaled dy):
-//   dg = <Y[row], dy[t]> = <z[row], dzr[row]>  (Y = z W2_e^T, so no Y is formed);
+// the token's unscaled dy) and the pre-activations u (and v):
+//   z = act(u) (SwiGLU: silu(u) v), in fp32;
+//   dg = <Y[row], dy[t]> = <z, dzr>  (Y = z W2_e^T, so no Y is formed);
 //   du = g dzr act'(u)  (SwiGLU: du = g dzr v silu'(u), dv = g dzr silu(u));
-//   z[row] <- g z[row] (rounded to bf16: the operand of dW2 = sum dy^T (g z)).
-// A dropped or absent choice gets dg = 0.
+//   zg[row] = g z, rounded to bf16 (the operand of dW2 = sum dy^T (g z)).
+// Eight features per thread and step: 16-byte loads and stores (F % 8 == 0,
+// every row 16-byte aligned).  A dropped or absent choice gets dg = 0.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 __global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restrict__ dzr, const uint16_t* __restrict__ u,
-                                                        const uint16_t* __restrict__ v, uint16_t* __restrict__ z,
+                                                        const uint16_t* __restrict__ v, uint16_t* __restrict__ zg,
                                                         const float* __restrict__ gate, const int32_t* __restrict__ dst,
                                                         uint16_t* __restrict__ du, uint16_t* __restrict__ dv,
                                                         int64_t ldd, float* __restrict__ dg, int F, int k, int act) {
@@ -259,20 +264,66 @@ __global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restri
     const float g = gate[(int64_t)t * k + c];
     const int64_t rb = (int64_t)row * F, ob = (int64_t)row * ldd;
     float part = 0.0f;
-    for (int f = threadIdx.x; f < F; f += 256) {
-      const float d = ld(dzr, rb + f), a = ld(u, rb + f), zf = ld(z, rb + f);
-      part = __builtin_fmaf(zf, d, part);
-      sto(z, rb + f, g * zf);
-      if (act == 2) {
-        const float s = 1.0f / (1.0f + __expf(-a));
-        sto(du, ob + f, g * d * ld(v, rb + f) * (s * (1.0f + a * (1.0f - s))));
-        sto(dv, ob + f, g * d * (a * s));
-      } else {
-        sto(du, ob + f, g * d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a)));
+    for (int f = threadIdx.x * 8; f < F; f += 256 * 8) {
+      const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(dzr + rb + f);
+      const u32x4_t uq = *reinterpret_cast<const u32x4_t*>(u + rb + f);
+      const u32x4_t vq = act == 2 ? *reinterpret_cast<const u32x4_t*>(v + rb + f) : u32x4_t{0, 0, 0, 0};
+      u32x4_t zo, duo, dvo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float zz[2], gu[2], gv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float d = h ? bf16_hi(dq[j]) : bf16_lo(dq[j]), a = h ? bf16_hi(uq[j]) : bf16_lo(uq[j]);
+          if (act == 2) {
+            const float b = h ? bf16_hi(vq[j]) : bf16_lo(vq[j]);
+            const float sg = 1.0f / (1.0f + __expf(-a));
+            zz[h] = a * sg * b;
+            gu[h] = g * d * b * (sg * (1.0f + a * (1.0f - sg)));
+            gv[h] = g * d * (a * sg);
+          } else {
+            zz[h] = act == 0 ? (a > 0.0f ? a : 0.0f) : gelu_f(a);
+            gu[h] = g * d * (act == 0 ? (a > 0.0f ? 1.0f : 0.0f) : gelu_grad_f(a));
+            gv[h] = 0.0f;
+          }
+          part = __builtin_fmaf(zz[h], d, part);
+        }
+        zo[j] = pack_bf16x2(g * zz[0], g * zz[1]);
+        duo[j] = pack_bf16x2(gu[0], gu[1]);
+        dvo[j] = pack_bf16x2(gv[0], gv[1]);
       }
+      *reinterpret_cast<u32x4_t*>(zg + rb + f) = zo;
+      *reinterpret_cast<u32x4_t*>(du + ob + f) = duo;
+      if (act == 2) *reinterpret_cast<u32x4_t*>(dv + ob + f) = dvo;
     }
     const float sum = block_sum256(part, red);
     if (threadIdx.x == 0) dg[(int64_t)t * k + c] = sum;
+  }
+}
+
+// Dispatch backward on the matrix-core path: dx[t] = sum over r ascending of the
+// token's kept rows of dX (bf16), eight features per thread (16-byte loads,
+// 32-byte stores; H % 8 == 0, dx 16-byte aligned); the same sums as
+// gather_sum_kernel.
+__global__ void __launch_bounds__(256) gather_sum_vec_kernel(const uint16_t* __restrict__ dX,
+                                                             const int32_t* __restrict__ dst, float* __restrict__ dx,
+                                                             int H, int k) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < k; ++r) {
+      const int row = dst[(int64_t)t * k + r];
+      if (row < 0) continue;
+      const u32x4_t q = *reinterpret_cast<const u32x4_t*>(dX + (int64_t)row * H + h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += bf16_lo(q[j]);
+        acc[2 * j + 1] += bf16_hi(q[j]);
+      }
+    }
+    float* o = dx + (int64_t)t * H + h;
+    *reinterpret_cast<f32x4_t*>(o) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4_t*>(o + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -784,14 +835,13 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
     const int KC = gated ? 2 * F : F;  // reduction length of dX = [du | dv] [W1; W3]
     const int64_t rc = a.rows_cap;
     if (R_max > 0) {
-      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T (unless kept), z
+      // recompute: u = x[row_token] W1^T, v = x[row_token] W3^T (unless kept; z is
+      // formed from them in token_bwd_kernel)
       if (!a.saved) {
         MOE_BW(launch_grouped_gemm_bf16(a.x, a.W1, u_ws, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
         if (gated)
           MOE_BW(launch_grouped_gemm_bf16(a.x, a.W3, v_ws, a.offsets, E, F, H, R_max, rc, true, st, a.row_token, T));
       }
-      act_fwd_kernel<uint16_t><<<grid_1d(R_max * F, 256), 256, 0, st>>>(u, v, z, a.offsets, E, F, a.act);
-      MOE_BW(hipGetLastError());
     }
     if (R_max > 0) {
       // dzr = dy[row_token] W2 per kept row (the gate is applied in token_bwd_kernel);
@@ -805,7 +855,10 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       // dX = du W1 (+ dv W3): W1_e, W3_e [F][H] are the two k-major halves
       MOE_BW(launch_grouped_gemm_bf16_kn(dcat, a.W1, gated ? a.W3 : nullptr, dX, a.offsets, E, H, KC, F, R_max, rc,
                                          st));
-      gather_sum_kernel<uint16_t><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
+      if ((reinterpret_cast<uintptr_t>(a.dx) & 15) == 0)
+        gather_sum_vec_kernel<<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
+      else
+        gather_sum_kernel<uint16_t><<<T, 256, 0, st>>>(dX, a.dst_row, a.dx, H, k);
       MOE_BW(hipGetLastError());
     } else {
       zero_f32_kernel<<<grid_1d((int64_t)T * H, 256), 256, 0, st>>>(a.dx, (int64_t)T * H);
