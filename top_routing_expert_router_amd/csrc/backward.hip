@@ -30,11 +30,12 @@
 // 64): the recomputation of u and v and the two data-gradient products run on
 // the expert FFN's grouped bf16 GEMM (fp32 accumulation, bf16 intermediates);
 // the data-gradient products use its k-major form, which reads W2 and W1, W3
-// as stored (no transposed copies).  There the first product takes the tokens' dy rows
-// unscaled, dzr = dy W2, so that dg = <Y, dy> = <z, dzr> needs no Y, and the
-// gate enters du, dv and (through g z) dW2 = sum dy^T (g z).  The weight
-// gradients run on a grouped MFMA kernel over each expert's rows.  The order of
-// every sum is fixed: results are deterministic.
+// as stored (no transposed copies).  There the first product takes the
+// tokens' dy rows unscaled, dzr = dy W2, so that dg = <Y, dy> = <z, dzr> needs
+// no Y, and the gate enters du, dv and (through g z) dW2 = sum dy^T (g z).  The
+// weight gradients run on a grouped MFMA kernel over each expert's rows that
+// reads the activations as stored as well.  The order of every sum is fixed:
+// results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -248,7 +249,8 @@ __global__ void __launch_bounds__(256) gather_sum_kernel(const T* __restrict__ d
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restrict__ dzr, const uint16_t* __restrict__ u,
+__global__ void __launch_bounds__(256) token_bwd_kernel(const uint16_t* __restrict__ dzr,
+                                                        const uint16_t* __restrict__ u,
                                                         const uint16_t* __restrict__ v, uint16_t* __restrict__ zg,
                                                         const float* __restrict__ gate, const int32_t* __restrict__ dst,
                                                         uint16_t* __restrict__ du, uint16_t* __restrict__ dv,
@@ -599,7 +601,8 @@ __global__ void __launch_bounds__(256) wgrad_kn_kernel(const uint16_t* __restric
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[jj], acc[i][jj], 0, 0, 0);
     }
   }
   __syncthreads();  // every wave is done reading the stages: their space stages the stores
@@ -613,7 +616,8 @@ __global__ void __launch_bounds__(256) wgrad_kn_kernel(const uint16_t* __restric
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sw[(8 * g + 4 * (lane >> 5) + q) * PAD + jj * 32 + (lane & 31)] = acc[i][jj][4 * g + q];
+        for (int q = 0; q < 4; ++q)
+          sw[(8 * g + 4 * (lane >> 5) + q) * PAD + jj * 32 + (lane & 31)] = acc[i][jj][4 * g + q];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
