@@ -11,9 +11,9 @@ every intermediate is fp32 (inputs are the exact bf16 / fp32 values), each
 product an fp32 sum of at most a few thousand terms in a fixed order (error
 ~ sqrt(K) 2^-24 relative for random signs), the transcendental functions within
 a few ulp: near 1e-6 along the chain; bound 1e-4.  Matrix-core path (bf16, H
-and F multiples of 64): the intermediates u, v, z, Y, dY, dz, du, dv and dX are
+and F multiples of 64): the intermediates u, v, g z, dzr, du, dv and dX are
 stored in bf16, each rounding an rms 2^-9 / sqrt(3) ~ 1.1e-3 relative; a
-gradient's chain crosses at most four of them (dx: dY, dz, du, dX), about 2.3e-3
+gradient's chain crosses at most four of them (dx: u, dzr, du, dX), about 2.3e-3
 in quadrature; bound 1e-2.
 """
 import numpy as np
