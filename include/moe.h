@@ -252,8 +252,9 @@ moe_status moe_forward(const moe_config *cfg, const void *x, const float *Wg, co
  * for SwiGLU, else 1 (0 when the configuration is invalid).  Host only. */
 size_t moe_saved_act_bytes(const moe_config *cfg);
 
-/* moe_forward for training ([EP] layer walk-through: the forward's activations
- * kept for the backward instead of recomputed): the first expert GEMM also
+/* moe_forward for training that keeps the forward's activations for the
+ * backward instead of recomputing them (memory for time; the pages leave the
+ * choice open): the first expert GEMM also
  * writes its pre-activations of every kept row as bf16, act[0][row][f] = u =
  * X W1_e^T and, for SwiGLU, act[1][row][f] = v = X W3_e^T (act: device
  * [m1][R_max][F], 16-byte aligned, moe_saved_act_bytes; rows past offsets[E]
