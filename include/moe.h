@@ -66,7 +66,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* bad shape / mode / NULL required pointer */
-  MOE_ERR_UNSUPPORTED = 2, /* valid in principle but not provided by this build */
+  MOE_ERR_UNSUPPORTED = 2, /* valid in principle but not provided by this library */
   MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 4          /* a HIP launch failed */
 } moe_status;
