@@ -159,7 +159,7 @@ def test_backward_with_kept_preactivations(gpu, name):
     print(f"[backward] kept pre-activations {name}: gradients equal to the recomputed path", flush=True)
 
 
-@pytest.mark.parametrize("name", ["1", "2", "3a", "3c", "4", "5"])
+@pytest.mark.parametrize("name", ["1", "2", "3a", "3b", "3c", "4", "5"])
 def test_backward_matches_oracle(gpu, name):
     r = recipes.SMALL[name]
     d = _inputs(r)
@@ -180,6 +180,32 @@ def test_backward_generic_path_bf16(gpu, name):
     _, got = _gpu_backward(r, gpu, d, generic=True)
     _, ref = _oracle_backward(r, d)
     _compare(f"run {name} generic", got, ref, GRAD_RELL2)
+
+
+def test_generic_path_ignores_kept_preactivations(gpu):
+    """Off the matrix-core path (here: x not 16-byte aligned) moe_backward recomputes its
+    fp32 intermediates whether or not kept bf16 pre-activations are passed: the same
+    gradients bit for bit."""
+    import torch
+
+    r = recipes.SMALL["5"]
+    d = _inputs(r)
+    cfg = B.MoEConfig.from_run(r)
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    ws = B.alloc_workspace(cfg, gpu)
+    x = _unaligned(d["x"], gpu)
+    wg, w1, w3, w2 = (U.dev(d[n], gpu) for n in ("wg", "w1", "w3", "w2"))
+    B.route(cfg, x, wg, U.dev(d["bias"], gpu), plan, ws)
+    act = torch.zeros(B.saved_act_bytes(cfg), dtype=torch.uint8, device=gpu)  # deliberately not the forward's
+    bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=gpu)
+    outs = []
+    for a in (None, act):
+        grads = B.alloc_grads(cfg, gpu, bias=True, dg=True)
+        B.backward(cfg, x, wg, w1, w3, w2, plan, U.dev(d["dy"], gpu), grads, bws, act=a)
+        torch.cuda.synchronize()
+        outs.append({n: t.cpu() for n, t in grads.items()})
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
 
 
 @pytest.mark.parametrize("name", ["3a", "5"])
