@@ -182,6 +182,62 @@ def test_backward_generic_path_bf16(gpu, name):
     _compare(f"run {name} generic", got, ref, GRAD_RELL2)
 
 
+@pytest.mark.parametrize("name", ["2", "5"])
+def test_training_step_graph_replay(gpu, name):
+    """A training step of the layer (moe_forward_save, then moe_backward given the kept
+    pre-activations) captured in a HIP graph: every replay, with eager steps and
+    synchronisations in between, gives the eager y and gradients bit for bit."""
+    import torch
+
+    r = recipes.SMALL[name]
+    d = _inputs(r)
+    cfg = B.MoEConfig.from_run(r)
+    R_max = max(B.max_rows(cfg), 1)
+    x, wg, bias, dy = (U.dev(d[n], gpu) for n in ("x", "wg", "bias", "dy"))
+    w1, w3, w2 = U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu)
+    plan = B.alloc_plan(cfg, gpu, logits=True)
+    X = torch.empty((R_max, r.H), dtype=torch.bfloat16, device=gpu)
+    Y = torch.empty_like(X)
+    y = torch.empty((r.T, r.H), dtype=torch.bfloat16, device=gpu)
+    ws = B.alloc_workspace(cfg, gpu)
+    act = torch.empty(B.saved_act_bytes(cfg), dtype=torch.uint8, device=gpu)
+    grads = B.alloc_grads(cfg, gpu, bias=True, dg=True)
+    bws = torch.empty(max(B.backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=gpu)
+    s = torch.cuda.Stream()
+
+    def step():
+        B.forward_save(cfg, x, wg, bias, w1, w3, w2, x, y, plan, X, Y, act, ws, stream=s)
+        B.backward(cfg, x, wg, w1, w3, w2, plan, dy, grads, bws, stream=s, act=act)
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    g_eager = {n: t.clone() for n, t in grads.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.zero_()
+        for t in grads.values():
+            t.fill_(float("nan"))
+        with torch.cuda.stream(s):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i} y"
+        for n, t in grads.items():
+            assert torch.equal(t, g_eager[n]), f"replay {i} {n}"
+        with torch.cuda.stream(s):  # eager work between replays
+            step()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+    # and the eager step is the oracle's gradient within the matrix-core bound
+    _, ref = _oracle_backward(r, d)
+    _compare(f"graph run {name}", {n: t.cpu().numpy().astype(np.float64) for n, t in g_eager.items()}, ref,
+             GRAD_RELL2_MC)
+
+
 def test_generic_path_ignores_kept_preactivations(gpu):
     """Off the matrix-core path (here: x not 16-byte aligned) moe_backward recomputes its
     fp32 intermediates whether or not kept bf16 pre-activations are passed: the same
