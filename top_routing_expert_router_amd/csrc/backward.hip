@@ -472,6 +472,71 @@ __global__ void __launch_bounds__(256) col_sum_part_kernel(const float* __restri
   if (ph == 0 && e < E) part[(int64_t)c * E + e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
 }
 
+// dx[t][h] += sum over e ascending of dl[t][e] Wg[h][e]: fp32 fma from zero, then
+// one add into dx (the arithmetic of gemm_generic_kernel, so the same bits).
+// 128 x 128 tiles of (t, h), 256 threads of 8 x 8 outputs, 16-wide e stages
+// stored e-major in LDS so that a thread's 8 t and 8 h values of one e are two
+// 32-byte reads.  E % 4 == 0, H % 4 == 0, dl, Wg and dx 16-byte aligned.
+__global__ void __launch_bounds__(256) router_dx_kernel(const float* __restrict__ dl, const float* __restrict__ Wg,
+                                                        float* __restrict__ dx, int T, int H, int E) {
+  constexpr int BT = 128, BH = 128, BK = 16;
+  __shared__ __align__(16) float As[BK][BT + 4], Bs[BK][BH + 4];
+  const int t0 = blockIdx.y * BT, h0 = blockIdx.x * BH, tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;  // the thread's h block tx * 8 and t block ty * 8
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+  for (int e0 = 0; e0 < E; e0 += BK) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {  // 128 rows x 4 groups of 4 e, per operand
+      const int p = tid + 256 * q, row = p >> 2, c4 = (p & 3) * 4, e = e0 + c4;
+      const int t = t0 + row, h = h0 + row;
+      const bool ein = e < E;  // E % 4 == 0: a group is whole or past the end
+      const f32x4_t a = (t < T && ein) ? *reinterpret_cast<const f32x4_t*>(dl + (int64_t)t * E + e)
+                                       : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4_t b = (h < H && ein) ? *reinterpret_cast<const f32x4_t*>(Wg + (int64_t)h * E + e)
+                                       : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        As[c4 + j][row] = a[j];
+        Bs[c4 + j][row] = b[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&As[kk][ty * 8]);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&As[kk][ty * 8 + 4]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(&Bs[kk][tx * 8]);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(&Bs[kk][tx * 8 + 4]);
+      const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = t0 + ty * 8 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j4 = 0; j4 < 8; j4 += 4) {
+      const int h = h0 + tx * 8 + j4;
+      if (h >= H) continue;  // H % 4 == 0: a group of 4 is whole or past the end
+      f32x4_t* o = reinterpret_cast<f32x4_t*>(dx + (int64_t)t * H + h);
+      f32x4_t c = *o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = c[j] + acc[i][j4 + j];
+      *o = c;
+    }
+  }
+}
+
 // out[i] = sum over g < parts of part[g * n + i], in g order.
 __global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ part, int parts, int64_t n,
                                                        float* __restrict__ out) {
@@ -747,6 +812,11 @@ hipError_t router_backward(const BackwardArgs& a, const BwdLayout& L, const floa
     if ((err = hipGetLastError()) != hipSuccess) return err;
     col_sum_final_kernel<<<(E + 63) / 64, 256, 0, st>>>(part, a.dbias, chunks, E);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  const bool a16 = ((reinterpret_cast<uintptr_t>(a.Wg) | reinterpret_cast<uintptr_t>(a.dx)) & 15) == 0;
+  if (E % 4 == 0 && H % 4 == 0 && a16) {  // dl is 256-byte aligned in the workspace
+    router_dx_kernel<<<dim3((H + 127) / 128, (T + 127) / 128), 256, 0, st>>>(dl, a.Wg, a.dx, T, H, E);
+    return hipGetLastError();
   }
   GemmArgs x{};  // dx[t][h] += sum_e dl[t][e] Wg[h][e]
   x.A = dl, x.sam = E, x.sak = 1;
