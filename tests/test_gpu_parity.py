@@ -404,6 +404,42 @@ def test_expert_ffn_large_tiles(gpu, act, F, H):
     U.assert_close(U.host(Yd)[:oplan["R"]], Yref, True, f"expert FFN large tiles act={act}")
 
 
+# Row counts on both sides of every 32-row token-fragment boundary of the
+# 128- and 256-row tiles (a wave multiplies only its fragments that hold rows
+# of the tile), with empty experts between them.
+_FRAG_ROWS = [1, 31, 32, 33, 0, 63, 64, 65, 95, 96, 97, 127, 128, 0, 129, 159, 160, 161, 191, 192, 193, 223, 224,
+              225, 255, 256, 257, 300, 5, 0, 40, 90]
+
+
+@pytest.mark.parametrize("act,E", [(recipes.SWIGLU, 32), (recipes.GELU, 32), (recipes.SWIGLU, 16),
+                                   (recipes.RELU, 16)])
+def test_expert_ffn_fragment_boundaries(gpu, act, E):
+    """Expert FFN on experts of 0..300 rows placed around every 32-row fragment edge; E = 32 puts the
+    experts of at most 128 rows in 128-row tiles and the others in 256-row ones, E = 16 (the last 16
+    counts, more than 128 rows per expert on average) every expert in 256-row tiles.  Every output
+    element compared with the oracle."""
+    import torch
+
+    counts = np.array(_FRAG_ROWS[-E:], np.int32)
+    R = int(counts.sum())
+    r = recipes.SMALL["4"].scaled(name=f"frag-{act}-{E}", T=R, H=256, F=320, E=E, k=1, act=act, dropless=1,
+                                  gate_mode=recipes.SOFTMAX_TOPK, bias="n1")
+    d = recipes.gen_all(r)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    X = d["x"]  # R token rows, read as the expert-contiguous rows
+    Yref = oracle.expert_ffn(X, offsets, r.dtype, r.act, d["w1"], d["w3"], d["w2"])
+    cfg = B.MoEConfig.from_run(r)
+    gp = B.alloc_plan(cfg, gpu)
+    gp["offsets"].copy_(torch.from_numpy(offsets))
+    Xd = torch.zeros((B.max_rows(cfg), r.H), dtype=torch.bfloat16, device=gpu)
+    Xd[:R].copy_(U.dev(X, "cpu"))
+    Yd = torch.full_like(Xd, float("nan"))
+    ws = B.alloc_workspace(cfg, gpu)
+    B.expert_ffn(cfg, Xd, gp, U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), Yd, ws)
+    torch.cuda.synchronize()
+    U.assert_close(U.host(Yd)[:R], Yref, True, f"expert FFN fragment edges act={act} E={E}")
+
+
 # --------------------------------------------------------------------------- split-bf16 router
 
 

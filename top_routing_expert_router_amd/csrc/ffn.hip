@@ -13,6 +13,8 @@
 // The tile schedule is derived on the device from offsets[E+1]: workgroup id ->
 // (global m-tile, n-tile); a block-wide scan of ceil(kept_e / BM) maps the
 // m-tile to its expert.  No host synchronisation, no tile straddles experts.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -415,15 +417,8 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   constexpr int KS = BK / 16;                             // MFMA k-steps per stage
   static_assert(ROWS * CPR % (64 * NW) == 0 && BM % 64 == 0 && (CPR == 4 || CPR == 8 || CPR == 2), "tile");
   static_assert(MF >= 1 && NF >= 1 && (!kGated || NF % 2 == 0), "SwiGLU waves pair gate and up fragments");
-  static_assert(BT || MF * NF >= MF + NF, "enough MFMAs to interleave the next k-step's reads");
   static_assert(!BT || (EPI == EPI_NONE && WR % 128 == 0), "k-major weights: plain products, 16+ chunks per k-row");
   static_assert(!SAVE || EPI == EPI_RELU || EPI == EPI_GELU || EPI == EPI_SWIGLU, "pre-activations of the first GEMM");
-  constexpr int NRD = MF + (BT ? 2 : 1) * NF;              // LDS reads per k-step
-  constexpr int NIL = MF * NF < NRD ? MF * NF : NRD;        // of them interleaved one by one with MFMAs
-  // more reads than MFMAs per k-step (k-major 128-row tiles): the extra reads go
-  // first, and they are the token fragments, so that the first MFMAs of the next
-  // k-step wait only for reads issued early in this one
-  constexpr bool kXFirst = NRD > NIL;
   static_assert(S >= 2 && S - 2 <= 4 && (S - 1) * L < 64 && KS % 2 == 0, "stages");
   extern __shared__ __align__(16) uint16_t smem[];
   int* s_ts = reinterpret_cast<int*>(smem + S * STAGE);  // [E+1] first tile of each expert
@@ -566,12 +561,20 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   struct Frags {
     bf16x8_t w[NF], x[MF];
   };
-  auto read_frags = [&](int buf, int kk, Frags& fr) {
+  // V (0 .. MF): the wave's token fragments that hold rows of the tile; the
+  // others are neither read nor multiplied (their rows are never stored)
+  auto read_frags = [&](auto vc, int buf, int kk, Frags& fr) {
+    constexpr int V = decltype(vc)::value;
+    if constexpr (V == 0) return;
+    // more reads than MFMAs per k-step: the extra reads go first, and they are
+    // the token fragments, so that the first MFMAs of the next k-step wait
+    // only for reads issued early in this one
+    constexpr bool kXFirst = V + (BT ? 2 : 1) * NF > V * NF;
     const uint16_t* st = smem + buf * STAGE;
     const int c = kk * 2 + (lane >> 5);
     if constexpr (kXFirst) {
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
+      for (int i = 0; i < V; ++i) {
         const int r = wm * (MF * 32) + i * 32 + (lane & 31);
         fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
       }
@@ -592,17 +595,18 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
     }
     if constexpr (!kXFirst) {
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
+      for (int i = 0; i < V; ++i) {
         const int r = wm * (MF * 32) + i * 32 + (lane & 31);
         fr.x[i] = *reinterpret_cast<const bf16x8_t*>(st + lds_pos(r, c));
       }
     }
   };
-  auto mfma = [&](const Frags& fr) {
+  auto mfma = [&](auto vc, const Frags& fr) {
+    constexpr int V = decltype(vc)::value;
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
+      for (int i = 0; i < V; ++i)
         acc[f][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.w[f], fr.x[i], acc[f][i], 0, 0, 0);
   };
 
@@ -714,42 +718,57 @@ __global__ void __launch_bounds__(64 * NW, 2) grouped_gemm_pipe_kernel(const uin
   // MFMAs of stage j, reading k-step kk + 1 while k-step kk multiplies ->
   // wait for stage j + 1, barrier, read its first k-step while the last MFMAs
   // of stage j drain.  A buffer is overwritten only after the barrier that
-  // follows every wave's last read of it.
-  PipeTile ct = decode(0);  // tile being computed
-  zero();
+  // follows every wave's last read of it.  The nk steps of a tile run in the
+  // instance of `tile_steps` for the wave's count of valid token fragments;
+  // every instance issues the same loads and barriers.
   Frags fr[2];
-  wait_stages<L>(issued - 1);
-  lds_barrier();
-  read_frags(0, 0, fr[0]);
-  for (int j = 0; j < total_steps; ++j) {
-    if (issued < total_steps) issue_next();
-    const int buf = j % S;
+  auto tile_steps = [&](auto vc, int j0) {
+    constexpr int V = decltype(vc)::value;
+    constexpr int NRD = V == 0 ? 0 : V + (BT ? 2 : 1) * NF;  // LDS reads per k-step
+    constexpr int NMF = V * NF;                              // MFMAs per k-step
+    constexpr int NIL = NMF < NRD ? NMF : NRD;               // reads interleaved one by one with MFMAs
+    read_frags(vc, j0 % S, 0, fr[0]);
+    for (int j = j0; j < j0 + nk; ++j) {
+      if (issued < total_steps) issue_next();
+      const int buf = j % S;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      if (kk + 1 < KS) read_frags(buf, kk + 1, fr[(kk + 1) & 1]);
-      mfma(fr[kk & 1]);
-      if (kk + 1 < KS) {
-        // one fragment read of the next k-step between consecutive MFMAs, so
-        // the LDS latency hides behind the matrix pipe instead of a full drain
-        if constexpr (kXFirst) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) read_frags(vc, buf, kk + 1, fr[(kk + 1) & 1]);
+        mfma(vc, fr[kk & 1]);
+        if (NMF > 0 && kk + 1 < KS) {
+          // one fragment read of the next k-step between consecutive MFMAs, so
+          // the LDS latency hides behind the matrix pipe instead of a full drain
+          if constexpr (NRD > NIL) __builtin_amdgcn_sched_group_barrier(0x100, NRD - NIL, 0);
 #pragma unroll
-        for (int q = 0; q < NIL; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int q = 0; q < NIL; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (NMF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NIL, 0);
         }
-        if constexpr (!BT || MF * NF > NIL) __builtin_amdgcn_sched_group_barrier(0x008, MF * NF - NIL, 0);
+      }
+      if (j + 1 < total_steps) {
+        wait_stages<L>(issued - j - 2);  // stage j + 1 complete
+        lds_barrier();
+        if (j + 1 < j0 + nk) read_frags(vc, (j + 1) % S, 0, fr[0]);
       }
     }
-    if (j + 1 < total_steps) {
-      wait_stages<L>(issued - j - 2);  // stage j + 1 complete
-      lds_barrier();
-      read_frags((j + 1) % S, 0, fr[0]);
-    }
-    if ((j + 1) % nk == 0) {
-      store(ct);
-      zero();
-      if (j + 1 < total_steps) ct = decode((j + 1) / nk);
-    }
+  };
+  wait_stages<L>(issued - 1);
+  lds_barrier();
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const PipeTile ct = decode(ti);  // tile being computed
+    zero();
+    int nv = (ct.rows - wm * (MF * 32) + 31) / 32;
+    nv = nv < 0 ? 0 : (nv > MF ? MF : nv);
+    nv = __builtin_amdgcn_readfirstlane(nv);
+    const int j0 = ti * nk;
+    if (nv >= MF) tile_steps(std::integral_constant<int, MF>{}, j0);
+    else if (MF > 3 && nv == 3) tile_steps(std::integral_constant<int, (MF > 3 ? 3 : 0)>{}, j0);
+    else if (MF > 2 && nv == 2) tile_steps(std::integral_constant<int, (MF > 2 ? 2 : 0)>{}, j0);
+    else if (nv == 1) tile_steps(std::integral_constant<int, 1>{}, j0);
+    else tile_steps(std::integral_constant<int, 0>{}, j0);
+    store(ct);
   }
   if constexpr (EPI == EPI_COMBINE1) combine1_dropped(cmb, C, N, rmax, slot, G, tid, 64 * NW);
 }
