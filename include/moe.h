@@ -202,9 +202,9 @@ moe_status moe_route(const moe_config *cfg, const void *x, const float *Wg, cons
 /* moe_route without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  Same arguments, kernels and results as moe_route; the route
- * scratch is a static device array of the library (48 MiB, one per device, held
+ * scratch is a static device array of the library (96 MiB, one per device, held
  * until the process ends), so the call allocates nothing.  Configurations whose
- * route scratch (the routing part of moe_workspace_bytes) exceeds 48 MiB return
+ * route scratch (the routing part of moe_workspace_bytes) exceeds 96 MiB return
  * MOE_ERR_WORKSPACE with the sizes in moe_last_error().  Every call on a device
  * shares that device's array, which keeps the last call's contents (the kernels
  * initialise everything they read): calls that overlap on one device race and

@@ -47,13 +47,15 @@ struct SplitScratch {
   void* wp;       // [3][Ep][H] bf16 weight pieces
   double* wsq;    // [H/64][Ep] partial sums of w^2
   double* wn;     // [Ep] ||w_e||
-  float* xsq;     // [T] sum_h x^2
+  double* lpart;  // [HS][T][Ep] binary64 partial logit sums (E > 64; HS = split_router_hsplit)
+  float* xsq;     // [HS][T] partial sums of x^2 (HS = 1 for E <= 64)
   int2* pairs;    // [T*E] candidate (token, expert)
   int4* utok;     // [T] queued tokens (token, first pair, pair count)
   int* count;     // [2] pairs, queued tokens
 };
 int split_router_ep(int E);
 int split_router_hs(int H);
+int split_router_hsplit(int T, int E, int H);
 // Work the router's last kernel may take over (null pointers: not wanted):
 // the ranks and block histogram of launch_router_rank, and the per-block
 // partials of launch_router_losses.  *fused reports what was done (1: ranks,

@@ -64,7 +64,8 @@ int64_t expert_rows_cap(const moe_config* c, int64_t R_max) {
 struct Layout {
   int nb, Q;
   bool split;  // split-bf16 router buffers present
-  size_t hist, logits, wp, wsq, wn, xsq, pairs, utok, count, lp, lz, lc, lkey, lq, nslot, route_end, h, ffn_end, total;
+  size_t hist, logits, wp, wsq, wn, lpart, xsq, pairs, utok, count, lp, lz, lc, lkey, lq, nslot, route_end, h, ffn_end,
+      total;
   size_t hs, ys, soff, shared_end;  // shared expert: hidden [T][Fs], output [T][H], offsets {0, T}
 };
 
@@ -81,14 +82,16 @@ Layout layout_of(const moe_config* c) {
   L.logits = align_up(sizeof(int32_t) * (size_t)c->E * (size_t)L.Q);
   size_t end = L.logits + align_up(sizeof(float) * (size_t)c->T * (size_t)c->E);
   L.split = split_router_shape(c);
-  L.wp = L.wsq = L.wn = L.xsq = L.pairs = L.utok = L.count = end;
+  L.wp = L.wsq = L.wn = L.lpart = L.xsq = L.pairs = L.utok = L.count = end;
   if (L.split) {
     const size_t Ep = (size_t)moe::split_router_ep(c->E), HS = (size_t)moe::split_router_hs(c->H);
+    const size_t hsplit = (size_t)moe::split_router_hsplit(c->T, c->E, c->H);
     L.wp = end;
     L.wsq = L.wp + align_up(sizeof(uint16_t) * 3 * Ep * (size_t)c->H);
     L.wn = L.wsq + align_up(sizeof(double) * HS * Ep);
-    L.xsq = L.wn + align_up(sizeof(double) * Ep);
-    L.pairs = L.xsq + align_up(sizeof(float) * (size_t)c->T);
+    L.lpart = L.wn + align_up(sizeof(double) * Ep);
+    L.xsq = L.lpart + (c->E > 64 ? align_up(sizeof(double) * hsplit * (size_t)c->T * Ep) : 0);
+    L.pairs = L.xsq + align_up(sizeof(float) * hsplit * (size_t)c->T);
     L.utok = L.pairs + align_up(sizeof(int2) * (size_t)c->T * (size_t)c->E);
     L.count = L.utok + align_up(sizeof(int4) * (size_t)c->T);
     end = L.count + kAlign;
@@ -137,7 +140,7 @@ moe_status route_body(const moe_config* c, const void* x, const float* Wg, const
 // the library holds its own copy until the process ends), shared by every call
 // on that device.  Host code uses only the device address taken from the symbol
 // (per device, once), never the array's name.
-constexpr size_t kStaticScratchBytes = (size_t)48 << 20;
+constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
 __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 std::mutex g_scratch_mu;
@@ -281,6 +284,7 @@ moe_status route_body(const moe_config* c, const void* x, const float* Wg, const
     sc.wp = w + L.wp;
     sc.wsq = reinterpret_cast<double*>(w + L.wsq);
     sc.wn = reinterpret_cast<double*>(w + L.wn);
+    sc.lpart = reinterpret_cast<double*>(w + L.lpart);
     sc.xsq = reinterpret_cast<float*>(w + L.xsq);
     sc.pairs = reinterpret_cast<int2*>(w + L.pairs);
     sc.utok = reinterpret_cast<int4*>(w + L.utok);

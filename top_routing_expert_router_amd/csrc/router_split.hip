@@ -383,8 +383,9 @@ template <int TG, int EG, int KS, int MF, int WN, int S, bool FUSE, int KMAX, bo
 __global__ void __launch_bounds__(512) router_split_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wp, const float* __restrict__ Wg,
     const float* __restrict__ bias,
-    const double* __restrict__ wsq, float* __restrict__ logits, float* __restrict__ xsq, double* __restrict__ wn,
-    int T, int H, int E, int Ep, int k, int gate_mode, double c1, int32_t* __restrict__ topk_idx,
+    const double* __restrict__ wsq, float* __restrict__ logits, double* __restrict__ lpart, float* __restrict__ xsq,
+    double* __restrict__ wn, int T, int H, int E, int Ep, int k, int gate_mode, double c1,
+    int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_gate, int2* __restrict__ pairs, int4* __restrict__ utok, int* __restrict__ count,
     SplitTail tail) {
   static_assert(TG * EG * KS == 8, "8 waves");
@@ -404,7 +405,12 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   const int tg = w % TG, eg = (w / TG) % EG, ks = w / (TG * EG);
   const int t0 = blockIdx.x * BM, e0 = blockIdx.y * BN;
   const int nk = H / kChunk;
-  const int nks = nk / KS;  // stages (chunks per slice)
+  // Unfused (the experts span several workgroups): the h chunks are also
+  // split over gridDim.z workgroups, each writing the binary64 sums of its
+  // own chunks; they are added in z order when the logits are certified.
+  const int nkw = FUSE ? nk : nk / (int)gridDim.z;   // chunks of this workgroup
+  const int kc0 = FUSE ? 0 : (int)blockIdx.z * nkw;  // its first chunk
+  const int nks = nkw / KS;                          // stages (chunks per slice)
 
   auto lds_pos = [](int r, int c) { return (r * 8 + (c ^ ((r >> 1) & 7))) * 8; };
 
@@ -446,7 +452,7 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
       const int r = p >> 3;
       const int c = (p & 7) ^ ((r >> 1) & 7);
       const int sl = r / SR, rr = r % SR;
-      const int h = (sl * nks + j) * kChunk + c * 8;
+      const int h = (kc0 + sl * nks + j) * kChunk + c * 8;
       const uint16_t* src;
       if (rr < BM) {
         const int t = t0 + rr < T ? t0 + rr : T - 1;
@@ -631,7 +637,7 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
   }
 
   if (!FUSE) {
-    if (blockIdx.x == 0 && tid < BN && e0 + tid < E) {
+    if (blockIdx.x == 0 && blockIdx.z == 0 && tid < BN && e0 + tid < E) {
       double s = 0.0;
       for (int hb = 0; hb < nk; ++hb) s += wsq[(size_t)hb * Ep + e0 + tid];
       wn[e0 + tid] = sqrt(s * (1.0 + 0x1p-40));
@@ -654,22 +660,25 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
       const int el = (eg * WN + n) * 16 + (lane & 15);
       const int e = e0 + el;
       if (e >= E) continue;
-      const double b = FUSE ? (double)s_bias[el] : (bias ? (double)bias[e] : 0.0);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int tl = (tg * MF + i) * 16 + 4 * (lane >> 4) + jj;
-          const float v = (float)(acc64[i][n][jj] + b);
-          if (t0 + tl < T) logits[(size_t)(t0 + tl) * E + e] = v;
-          if (FUSE) s_v[tl * SV + el] = v;
+          if constexpr (FUSE) {
+            const float v = (float)(acc64[i][n][jj] + (double)s_bias[el]);
+            if (t0 + tl < T) logits[(size_t)(t0 + tl) * E + e] = v;
+            s_v[tl * SV + el] = v;
+          } else if (t0 + tl < T) {
+            lpart[((size_t)blockIdx.z * T + t0 + tl) * Ep + e] = acc64[i][n][jj];
+          }
         }
     }
     if (eg == 0 && lane < 16) {
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
         const int tl = (tg * MF + i) * 16 + lane;
-        if (!FUSE && t0 + tl < T) xsq[t0 + tl] = sq[i];
+        if (!FUSE && t0 + tl < T) xsq[(size_t)blockIdx.z * T + t0 + tl] = sq[i];
         if (FUSE) s_x[tl] = sq[i];
       }
     }
@@ -892,28 +901,40 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
 
 // ---------------------------------------------------------------------------
 // Certify + select (experts beyond one workgroup's tile): one wave per token.
+// The approximate logit is the binary64 sum of the HS partial sums (in their
+// order) plus the bias, rounded once to fp32; sum_h x^2 the fp32 sum of its
+// HS parts.
 // ---------------------------------------------------------------------------
 template <int JE, int KMAX>
-__global__ void __launch_bounds__(256) router_certify_kernel(const float* __restrict__ logits,
+__global__ void __launch_bounds__(256) router_certify_kernel(const double* __restrict__ lpart, int HS,
+                                                             float* __restrict__ logits,
                                                              const float* __restrict__ xsq,
                                                              const double* __restrict__ wn,
                                                              const float* __restrict__ bias, int T, int H, int E,
-                                                             int k, int gate_mode, double c1,
+                                                             int Ep, int k, int gate_mode, double c1,
                                                              int32_t* __restrict__ topk_idx,
                                                              float* __restrict__ topk_gate, int2* __restrict__ pairs,
                                                              int4* __restrict__ utok, int* __restrict__ count) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  const float xn = xnorm_bound(xsq[t], H);
+  float* row = logits + (size_t)t * E;
+  float sq = 0.0f;
+  for (int z = 0; z < HS; ++z) sq += xsq[(size_t)z * T + t];
+  const float xn = xnorm_bound(sq, H);
   float v[JE], be[JE], wne[JE];
 #pragma unroll
   for (int j = 0; j < JE; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : -__builtin_inff();
     wne[j] = e < E ? (float)wn[e] * (1.0f + 0x1p-20f) : 0.0f;
     be[j] = (bias && e < E) ? bias[e] : 0.0f;
+    v[j] = -__builtin_inff();
+    if (e < E) {
+      double s = 0.0;
+      for (int z = 0; z < HS; ++z) s += lpart[((size_t)z * T + t) * Ep + e];
+      v[j] = (float)(s + (double)be[j]);
+      row[e] = v[j];
+    }
   }
   certify_token<64, JE, KMAX>(v, wne, be, E, H, k, gate_mode, (float)c1 * (1.0f + 0x1p-20f), true, t, xn, topk_idx,
                               topk_gate, pairs, utok,
@@ -978,6 +999,18 @@ int split_router_ep(int E) {
 
 int split_router_hs(int H) { return H / kChunk; }
 
+// Workgroups the unfused logits split h over (a divisor of the chunk count):
+// the largest power of two up to 8 that keeps the grid of 256-token x
+// 64-expert tiles within 256 workgroups.
+int split_router_hsplit(int T, int E, int H) {
+  if (E <= 64) return 1;
+  const int64_t tiles = (int64_t)((T + 255) / 256) * (split_router_ep(E) / 64);
+  const int nk = H / kChunk;
+  int hs = 1;
+  while (hs < 8 && tiles * hs * 2 <= 256 && nk % (hs * 2) == 0) hs *= 2;
+  return hs;
+}
+
 struct SplitArgs {
   const uint16_t* x;
   const uint16_t* wp;
@@ -988,6 +1021,7 @@ struct SplitArgs {
   float* topk_gate;
   const SplitScratch* sc;
   int T, H, E, Ep, k, gate_mode;
+  int hs;  // h split over workgroups (unfused form)
   double c1;
   SplitTail tail;  // requested epilogue work (null pointers: none)
   int* fused;      // out: 1 ranks done, 2 loss partials done
@@ -1016,8 +1050,9 @@ static hipError_t launch_split_logits(const SplitArgs& a, hipStream_t st) {
   auto kern = router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX, RAW>;
   hipError_t err = lds_limit_once<router_split_logits_kernel<TG, EG, KS, MF, WN, S, FUSE, KMAX, RAW>>((int)shm);
   if (err != hipSuccess) return err;
-  dim3 grid((a.T + BM - 1) / BM, a.Ep / BN);
-  kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.Wg, a.bias, a.sc->wsq, a.logits, a.sc->xsq, a.sc->wn, a.T, a.H, a.E, a.Ep,
+  dim3 grid((a.T + BM - 1) / BM, a.Ep / BN, FUSE ? 1 : a.hs);
+  kern<<<grid, dim3(512), shm, st>>>(a.x, a.wp, a.Wg, a.bias, a.sc->wsq, a.logits, a.sc->lpart, a.sc->xsq, a.sc->wn,
+                                     a.T, a.H, a.E, a.Ep,
                                      a.k, a.gate_mode, a.c1, a.topk_idx, a.topk_gate, a.sc->pairs, a.sc->utok,
                                      a.sc->count, tail);
   return hipGetLastError();
@@ -1061,7 +1096,8 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;  // expert ids 0 .. E-1
   const SplitTail tail{ep.dst_rank, ep.hist, nbits, (T + 63) / 64, ep.Ppart, ep.Zpart, ep.Cpart, ep.score_fn};
-  SplitArgs a{xb, wp, Wg, bias, logits, topk_idx, topk_gate, &sc, T, H, E, Ep, k, gate_mode, c1, tail, fused};
+  SplitArgs a{xb,  wp, Wg, bias,      logits, topk_idx, topk_gate, &sc, T,    H,
+              E,   Ep, k,  gate_mode, split_router_hsplit(T, E, H),   c1,        tail, fused};
 
   if (E <= 16) {
     // 16 experts per wave; split h across waves when there are few tokens
@@ -1073,8 +1109,8 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
   } else if (E <= 64) {
     err = raw ? launch_split_fused<2, 4, 1, 2, 1, 4, true>(a, st) : launch_split_fused<2, 4, 1, 2, 1, 4>(a, st);
   } else {
-    err = (nk % 2) ? launch_split_logits<2, 4, 1, 2, 2, 2, false, 1>(a, st)
-                   : launch_split_logits<2, 2, 2, 2, 2, 2, false, 1>(a, st);
+    // 256 tokens x 64 experts per workgroup, h split over a.hs workgroups
+    err = launch_split_logits<4, 2, 1, 4, 2, 2, false, 1>(a, st);
   }
   if (err != hipSuccess) return err;
 
@@ -1086,9 +1122,9 @@ hipError_t launch_router_split(const void* x, const float* Wg, const float* bias
 #define MOE_CR(J, K)                                                                                               \
   do {                                                                                                             \
     if (!fused_tile) {                                                                                             \
-      router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(logits, sc.xsq, sc.wn, bias, T, H, E, k, gate_mode, \
-                                                               c1, topk_idx, topk_gate, sc.pairs, sc.utok,        \
-                                                               sc.count);                                          \
+      router_certify_kernel<J, K><<<cgrid, dim3(256), 0, st>>>(sc.lpart, a.hs, logits, sc.xsq, sc.wn, bias, T, H, \
+                                                               E, Ep, k, gate_mode, c1, topk_idx, topk_gate,      \
+                                                               sc.pairs, sc.utok, sc.count);                       \
       if ((err = hipGetLastError()) != hipSuccess) return err;                                                     \
       router_refine_kernel<J, K><<<rgrid, dim3(256), 0, st>>>(xb, wp, bias, sc.pairs, sc.utok, sc.count, logits,  \
                                                               H, E, Ep, k, gate_mode, topk_idx, topk_gate);        \
