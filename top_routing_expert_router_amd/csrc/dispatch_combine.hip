@@ -102,6 +102,63 @@ __global__ void __launch_bounds__(256) combine_kernel(const void* __restrict__ Y
   }
 }
 
+// K5 for bf16 rows in 16-byte groups and k <= KU: the same sum in the same
+// order, with the token's choices and all of its expert rows loaded before the
+// first multiply-add (KU rows in flight per thread instead of one at a time).
+template <int KU>
+__global__ void __launch_bounds__(256) combine_bf16_kernel(const uint16_t* __restrict__ Y,
+                                                           const int32_t* __restrict__ dst_row,
+                                                           const float* __restrict__ gate,
+                                                           const uint16_t* __restrict__ residual,
+                                                           uint16_t* __restrict__ y, int64_t total, int nch, int H,
+                                                           int k, int rmax, const uint16_t* __restrict__ shared) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / nch;
+    const int64_t c = (i - t * nch) * 8;
+    int d[KU];
+    float g[KU];
+#pragma unroll
+    for (int r = 0; r < KU; ++r) {
+      d[r] = r < k ? dst_row[t * k + r] : -1;
+      g[r] = r < k ? gate[t * k + r] : 0.0f;
+    }
+    u32x4_t q[KU];
+#pragma unroll
+    for (int r = 0; r < KU; ++r)
+      q[r] = (d[r] >= 0 && d[r] < rmax) ? *reinterpret_cast<const u32x4_t*>(Y + (size_t)d[r] * H + c)
+                                        : u32x4_t{0, 0, 0, 0};
+    const u32x4_t rq = residual ? *reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c)
+                                : u32x4_t{0, 0, 0, 0};
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = __uint_as_float(rq[j] << 16);
+      acc[2 * j + 1] = __uint_as_float(rq[j] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < KU; ++r) {
+      if (d[r] < 0 || d[r] >= rmax) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = __builtin_fmaf(g[r], __uint_as_float(q[r][j] << 16), acc[2 * j]);
+        acc[2 * j + 1] = __builtin_fmaf(g[r], __uint_as_float(q[r][j] & 0xFFFF0000u), acc[2 * j + 1]);
+      }
+    }
+    if (shared) {  // the shared expert's output, added last
+      const u32x4_t sq = *reinterpret_cast<const u32x4_t*>(shared + (size_t)t * H + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(sq[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(sq[j] & 0xFFFF0000u);
+      }
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_bits(acc[2 * j]) | (f32_to_bf16_bits(acc[2 * j + 1]) << 16);
+    *reinterpret_cast<u32x4_t*>(y + (size_t)t * H + c) = o;
+  }
+}
+
 static int grid_for(int64_t total, int block) {
   int64_t g = (total + block - 1) / block;
   const int64_t cap = 256 * 64;  // enough resident waves for 256 CUs; the loop strides the rest
@@ -147,6 +204,18 @@ hipError_t launch_combine(const void* Y, const int32_t* dst_row, const float* ga
   if (T == 0) return hipSuccess;
   const int nch = (H + 7) / 8;
   const int64_t total = (int64_t)T * nch;
+  if (bf16 && vec_ok && H % 8 == 0 && k <= 16) {
+    const uint16_t *Yb = static_cast<const uint16_t*>(Y), *rb = static_cast<const uint16_t*>(residual),
+                   *sb = static_cast<const uint16_t*>(shared);
+    uint16_t* yb = static_cast<uint16_t*>(y);
+    const int g = grid_for(total, 256);
+    if (k <= 1) combine_bf16_kernel<1><<<g, 256, 0, st>>>(Yb, dst_row, gate, rb, yb, total, nch, H, k, rmax, sb);
+    else if (k <= 2) combine_bf16_kernel<2><<<g, 256, 0, st>>>(Yb, dst_row, gate, rb, yb, total, nch, H, k, rmax, sb);
+    else if (k <= 4) combine_bf16_kernel<4><<<g, 256, 0, st>>>(Yb, dst_row, gate, rb, yb, total, nch, H, k, rmax, sb);
+    else if (k <= 8) combine_bf16_kernel<8><<<g, 256, 0, st>>>(Yb, dst_row, gate, rb, yb, total, nch, H, k, rmax, sb);
+    else combine_bf16_kernel<16><<<g, 256, 0, st>>>(Yb, dst_row, gate, rb, yb, total, nch, H, k, rmax, sb);
+    return hipGetLastError();
+  }
   if (bf16)
     combine_kernel<true><<<grid_for(total, 256), 256, 0, st>>>(Y, dst_row, gate, residual, y, total, nch, H, k,
                                                                 rmax, vec_ok, shared);
