@@ -76,6 +76,30 @@ def test_route_full_size(gpu, name):
     _check_route(r, gplan, _oracle_route(r, x, wg, bias))
 
 
+# Split router with more than 64 experts: the h chunks are split over 1, 2, 4 or 8
+# workgroups per 256-token x 64-expert tile (as many as keep the grid within 256
+# workgroups and divide the chunk count), their binary64 parts added at
+# certification.  One shape per split count, and one with an odd chunk count.
+_HSPLIT_SHAPES = {
+    "hs8": dict(T=700, E=256, H=512),     # 12 tiles, 8 chunks
+    "hs4": dict(T=333, E=256, H=256),     # 8 tiles, 4 chunks
+    "hs2": dict(T=8192, E=256, H=256),    # 128 tiles
+    "hs1": dict(T=16384, E=256, H=128),   # 256 tiles
+    "odd": dict(T=700, E=96, H=192),      # 3 chunks
+}
+
+
+@pytest.mark.parametrize("name", list(_HSPLIT_SHAPES))
+def test_split_router_h_split(gpu, name):
+    """Routing through the split-h logits kernel, every token compared with the oracle (plan
+    bit-exact, logits and gates within tolerance)."""
+    r = recipes.SMALL["5"].scaled(name=f"5-{name}", **_HSPLIT_SHAPES[name])
+    x = recipes.gen_x(r)
+    wg, bias = recipes.gen_router(r)
+    _, gplan = _gpu_route(r, gpu, x, wg, bias)
+    _check_route(r, gplan, _oracle_route(r, x, wg, bias))
+
+
 @pytest.mark.parametrize("name", ["2", "3b", "5"])
 def test_dispatch_bit_exact(gpu, name):
     import torch
