@@ -464,6 +464,37 @@ def test_expert_ffn_fragment_boundaries(gpu, act, E):
     U.assert_close(U.host(Yd)[:R], Yref, True, f"expert FFN fragment edges act={act} E={E}")
 
 
+
+@pytest.mark.parametrize("act,H,F,counts", [
+    (recipes.SWIGLU, 250, 500, [1, 63, 64, 65, 0, 700, 7, 1300]),
+    (recipes.RELU, 128, 200, [64, 0, 1290, 31, 1292, 5]),
+    (recipes.GELU, 100, 140, [3, 2500, 0, 2400]),
+    (recipes.SWIGLU, 37, 45, [1, 63, 64, 65, 0, 130, 7]),  # below the tiles' size threshold
+])
+def test_expert_ffn_f32_tiles(gpu, act, H, F, counts):
+    """fp32 expert FFN with row counts around the 64-row tile edge and k and output widths that
+    are not multiples of the tile: the LDS-tiled kernel (at least 2^26 multiply-adds per GEMM) and
+    the one-thread-per-output kernel below that, every output element against the oracle."""
+    import torch
+
+    counts = np.array(counts, np.int32)
+    R = int(counts.sum())
+    r = recipes.RUNS["1"].scaled(name=f"f32tiles-{act}-{H}", T=R, H=H, F=F, E=len(counts), k=1, act=act,
+                                 dropless=1)
+    d = recipes.gen_all(r)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    Yref = oracle.expert_ffn(d["x"], offsets, r.dtype, r.act, d["w1"], d["w3"], d["w2"])
+    cfg = B.MoEConfig.from_run(r)
+    gp = B.alloc_plan(cfg, gpu)
+    gp["offsets"].copy_(torch.from_numpy(offsets))
+    Xd = torch.zeros((B.max_rows(cfg), r.H), dtype=torch.float32, device=gpu)
+    Xd[:R].copy_(torch.from_numpy(d["x"]))
+    Yd = torch.full_like(Xd, float("nan"))
+    ws = B.alloc_workspace(cfg, gpu)
+    B.expert_ffn(cfg, Xd, gp, U.dev(d["w1"], gpu), U.dev(d["w3"], gpu), U.dev(d["w2"], gpu), Yd, ws)
+    torch.cuda.synchronize()
+    U.assert_close(U.host(Yd)[:R], Yref, False, f"fp32 expert FFN act={act} H={H} F={F}")
+
 # --------------------------------------------------------------------------- split-bf16 router
 
 

@@ -278,6 +278,82 @@ __global__ void __launch_bounds__(64) grouped_gemm_scalar_kernel(const void* __r
 }
 
 // ---------------------------------------------------------------------------
+// fp32 grouped GEMM, LDS-tiled: a 256-thread block computes 64 rows x 64
+// columns of one expert (each thread 4 x 4), staging 16 k of the A rows and
+// of the weight rows (both of them for SwiGLU) in LDS, k-major so that a
+// thread's four rows and four columns are two 16-byte LDS reads (fp32
+// layers, which the bf16 tiles do not take).  Every
+// output is one fp32 fma chain in k order, as in the scalar kernel, so the
+// two give the same bits.  Block (mt, nt): m-tile mt of the expert list
+// (ceil(kept_e / 64) per expert), n-tile nt.
+// ---------------------------------------------------------------------------
+constexpr int F32_T = 64, F32_BK = 16;
+
+template <int EPI>
+__global__ void __launch_bounds__(256) grouped_gemm_f32_kernel(const float* __restrict__ A,
+                                                               const float* __restrict__ B,
+                                                               const float* __restrict__ B2, float* __restrict__ C,
+                                                               const int32_t* __restrict__ offsets, int E, int N,
+                                                               int K) {
+  constexpr bool kGated = EPI == EPI_SWIGLU;
+  // rows of 68: the 16 k of one row land in distinct banks when stored
+  __shared__ __align__(16) float sa[F32_BK][F32_T + 4];
+  __shared__ __align__(16) float sb[kGated ? 2 : 1][F32_BK][F32_T + 4];
+  __shared__ int s_scan[5];
+  __shared__ int s_info[2];
+  if (!find_tile<F32_T>(offsets, E, blockIdx.x, s_scan, s_info)) return;
+  const int e = s_info[0];
+  const int row0 = offsets[e] + s_info[1];
+  const int rows = min(F32_T, offsets[e + 1] - row0);
+  const int n0 = blockIdx.y * F32_T;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  // loads: thread tid brings k = tid % 16 of row tid / 16 + 16 i (i < 4)
+  const int lk = tid & 15, lr = tid >> 4;
+  float acc[2][4][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[g][i][j] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += F32_BK) {
+    const int k = k0 + lk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lr + 16 * i;
+      sa[lk][r] = (r < rows && k < K) ? A[(size_t)(row0 + r) * K + k] : 0.0f;
+      const int n = n0 + r;
+      sb[0][lk][r] = (n < N && k < K) ? B[((size_t)e * N + n) * K + k] : 0.0f;
+      if constexpr (kGated) sb[1][lk][r] = (n < N && k < K) ? B2[((size_t)e * N + n) * K + k] : 0.0f;
+    }
+    __syncthreads();
+    const int kn = K - k0 < F32_BK ? K - k0 : F32_BK;
+    for (int kk = 0; kk < kn; ++kk) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sa[kk][4 * ty]);
+#pragma unroll
+      for (int g = 0; g < (kGated ? 2 : 1); ++g) {
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(&sb[g][kk][4 * tx]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[g][i][j] = __builtin_fmaf(a[i], b[j], acc[g][i][j]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * ty + i;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 4 * tx + j;
+      if (n < N) C[(size_t)(row0 + r) * N + n] = epilogue<EPI, false>(acc[0][i][j], acc[1][i][j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pipelined persistent grouped GEMM (the bf16 path when K % 32 == 0).
 //
 // Roles: the MFMA's first operand is a weight fragment (rows n), the second a
@@ -1153,6 +1229,21 @@ static hipError_t launch_scalar(const void* A, const void* B, const void* B2, vo
   return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_f32(const void* A, const void* B, const void* B2, void* C, const int32_t* offsets, int E,
+                             int N, int K, int64_t R_max, hipStream_t st) {
+  // m-tiles: at most ceil(R_max / 64) + one partial tile per expert
+  const int64_t mtiles = (R_max + F32_T - 1) / F32_T + (R_max < E ? R_max : E);
+  const int ntn = (N + F32_T - 1) / F32_T;
+  if (mtiles <= 0 || ntn <= 0) return hipSuccess;
+  if (mtiles > INT32_MAX || ntn > 65535) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_COMBINE1) return hipErrorInvalidValue;
+  grouped_gemm_f32_kernel<EPI><<<dim3((unsigned)mtiles, (unsigned)ntn), dim3(256), 0, st>>>(
+      static_cast<const float*>(A), static_cast<const float*>(B), static_cast<const float*>(B2),
+      static_cast<float*>(C), offsets, E, N, K);
+  return hipGetLastError();
+}
+
 template <int EPI, bool SAVE = false>
 static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, const void* B2, void* C,
                              const int32_t* offsets, int E, int N, int K, int64_t R_max, int64_t rows_cap,
@@ -1213,6 +1304,9 @@ static hipError_t launch_one(bool vec, bool bf16, const void* A, const void* B, 
   if (gather || EPI == EPI_COMBINE1 || SAVE) return hipErrorInvalidValue;
   if (vec && bf16) return launch_bf16<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   if (bf16) return launch_scalar<true, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
+  // fp32: the LDS tiles once there is work to fill them (below about 2^26
+  // multiply-adds the one-thread-per-output kernel has less fixed latency)
+  if (R_max * (int64_t)N * K >= ((int64_t)1 << 26)) return launch_f32<EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
   return launch_scalar<false, EPI>(A, B, B2, C, offsets, E, N, K, R_max, st);
 }
 
