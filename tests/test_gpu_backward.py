@@ -1,6 +1,6 @@
 """GPU parity of moe_backward with the backward oracle (oracle/backward.py).
 
-For each workload's reduced shape (the routing structure of runs 1-5: dtype,
+For each workload's reduced shape (the routing structure of every workload: dtype,
 activation, gate mode, capacity and drops) the GPU routes (bit-exact with the
 oracle, asserted here again), then moe_backward takes dy and the plan; the oracle
 takes the same inputs and its own plan.  Every gradient is compared element by

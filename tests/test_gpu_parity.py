@@ -234,7 +234,7 @@ def test_forward_full_size_sampled(gpu, name):
 @pytest.mark.parametrize("name", ["2", "3a", "5"])
 def test_route_full_size_deterministic(gpu, name):
     """Two routings of the same full-size batch give the same bits (logits, choices, gates,
-    plan), also where undecided tokens go through the global refinement queue (run 5)."""
+    plan), also where undecided tokens go through the global refinement queue (256 experts, top-8)."""
     r = recipes.RUNS[name]
     x = recipes.gen_x(r)
     wg, bias = recipes.gen_router(r)
