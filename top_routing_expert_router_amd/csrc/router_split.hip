@@ -432,36 +432,49 @@ __global__ void __launch_bounds__(512) router_split_logits_kernel(
     }
   }
 
+  // Each load instruction's address at the first stage, computed once: a stage
+  // adds 128 bytes (the next 64 h of a bf16 row) or, for the fp32 weight block,
+  // 64 rows of E floats.
+  uintptr_t lbase[L];
+  bool lraw[L];
+#pragma unroll
+  for (int q = 0; q < L; ++q) {
+    int g = q * 8 + w;
+    if (g >= NI) g = NI - 1;  // waves without a group of their own repeat the last one
+    lraw[q] = RAW && g >= NIX;
+    if (RAW && g >= NIX) {
+      // weight block: 16-byte slot s of row h holds experts 4 (s ^ 4((h >> 3) & 3)) .. +3,
+      // so the four 8-h groups a fragment read spans fall on different banks
+      const int q2 = (g - NIX) * 64 + lane;
+      const int hr = q2 >> 4;
+      int c4 = ((q2 & 15) ^ (((hr >> 3) & 3) << 2)) * 4;
+      if (e0 + c4 >= E) c4 = 0;  // columns past E: any valid address (never used)
+      lbase[q] = reinterpret_cast<uintptr_t>(Wg + (size_t)hr * E + e0 + c4);
+      continue;
+    }
+    const int p = g * 64 + lane;
+    const int r = p >> 3;
+    const int c = (p & 7) ^ ((r >> 1) & 7);
+    const int sl = r / SR, rr = r % SR;
+    const int h = (kc0 + sl * nks) * kChunk + c * 8;
+    const uint16_t* src;
+    if (rr < BM) {
+      const int t = t0 + rr < T ? t0 + rr : T - 1;
+      src = x + (size_t)t * H + h;
+    } else {
+      const int q2 = rr - BM;
+      src = wp + ((size_t)(q2 / BN) * Ep + e0 + q2 % BN) * H + h;
+    }
+    lbase[q] = reinterpret_cast<uintptr_t>(src);
+  }
+  const size_t wstep = (size_t)kChunk * E * sizeof(float);
   auto issue = [&](int buf, int j) {
     uint16_t* st = smem + buf * STAGE;
 #pragma unroll
     for (int q = 0; q < L; ++q) {
-      int g = q * 8 + w;
-      if (g >= NI) g = NI - 1;  // waves without a group of their own repeat the last one
-      if (RAW && g >= NIX) {
-        // weight block: 16-byte slot s of row h holds experts 4 (s ^ 4((h >> 3) & 3)) .. +3,
-        // so the four 8-h groups a fragment read spans fall on different banks
-        const int q2 = (g - NIX) * 64 + lane;
-        const int hr = q2 >> 4;
-        int c4 = ((q2 & 15) ^ (((hr >> 3) & 3) << 2)) * 4;
-        if (e0 + c4 >= E) c4 = 0;  // columns past E: any valid address (never used)
-        __builtin_amdgcn_global_load_lds(Wg + (size_t)(j * kChunk + hr) * E + e0 + c4, st + g * 512, 16, 0, 0);
-        continue;
-      }
-      const int p = g * 64 + lane;
-      const int r = p >> 3;
-      const int c = (p & 7) ^ ((r >> 1) & 7);
-      const int sl = r / SR, rr = r % SR;
-      const int h = (kc0 + sl * nks + j) * kChunk + c * 8;
-      const uint16_t* src;
-      if (rr < BM) {
-        const int t = t0 + rr < T ? t0 + rr : T - 1;
-        src = x + (size_t)t * H + h;
-      } else {
-        const int q2 = rr - BM;
-        src = wp + ((size_t)(q2 / BN) * Ep + e0 + q2 % BN) * H + h;
-      }
-      __builtin_amdgcn_global_load_lds(src, st + g * 512, 16, 0, 0);
+      const int g = q * 8 + w < NI ? q * 8 + w : NI - 1;
+      const uintptr_t a = lbase[q] + (size_t)j * (lraw[q] ? wstep : (size_t)kChunk * sizeof(uint16_t));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(a), st + g * 512, 16, 0, 0);
     }
   };
 
